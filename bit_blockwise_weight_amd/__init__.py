@@ -1,0 +1,292 @@
+"""Python binding of libqk — blockwise 4-bit (NF4 / FP4) weight quantization on
+AMD MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libqk.so
+(built in-tree by ``bit_blockwise_weight_amd.build``); PyTorch provides device
+memory and the current stream.  Each function has the name of the C call it
+wraps (see include/qk.h) and raises ``QKError`` on a non-zero status.  If the
+library is missing or fails to load, the error is raised at the first call,
+not at import.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "QKError", "QuantState", "QuantizedWeight", "NF4", "FP4", "CUSTOM", "lib",
+    "qk_make_codebook", "qk_quantize_blockwise", "qk_double_quant_workspace_size", "qk_double_quant",
+    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemm_nf4", "qk_last_error", "qk_version",
+    "qk_backend_info", "quantize",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqk.so")
+
+QK_OK, QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED, QK_ERR_BAD_STATE, QK_ERR_HIP, QK_ERR_NO_DEVICE, QK_ERR_WORKSPACE = \
+    0, -1, -2, -3, -4, -5, -6
+STATUS_NAMES = {0: "QK_OK", -1: "QK_ERR_INVALID_ARG", -2: "QK_ERR_UNSUPPORTED", -3: "QK_ERR_BAD_STATE",
+                -4: "QK_ERR_HIP", -5: "QK_ERR_NO_DEVICE", -6: "QK_ERR_WORKSPACE"}
+QK_F32, QK_BF16, QK_F16 = 0, 1, 2
+NF4, FP4, CUSTOM = 0, 1, 2
+QK_STATE_MAGIC = 0x314B5451
+QK_STATE_VERSION = 1
+QK_DQ_BLOCK = 256
+
+_DTYPE_CODE = {torch.float32: QK_F32, torch.bfloat16: QK_BF16, torch.float16: QK_F16}
+
+
+class QKError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class QuantState(ctypes.Structure):
+    """Mirror of qk_quant_state (include/qk.h)."""
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("version", ctypes.c_uint32),
+        ("struct_bytes", ctypes.c_uint32),
+        ("codebook_kind", ctypes.c_int32),
+        ("n", ctypes.c_int64),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("blocksize", ctypes.c_int32),
+        ("nested", ctypes.c_int32),
+        ("dq_blocksize", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("levels", ctypes.c_float * 16),
+        ("codes", ctypes.c_void_p),
+        ("absmax", ctypes.c_void_p),
+        ("q8", ctypes.c_void_p),
+        ("dq_scale", ctypes.c_void_p),
+        ("dq_mean", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_load_error = None
+
+
+def lib():
+    """The loaded libqk (ctypes), with argument types declared.  Raises QKError
+    if the library is missing or cannot be loaded."""
+    global _lib, _load_error
+    if _lib is not None:
+        return _lib
+    if _load_error is not None:
+        raise QKError(QK_ERR_NO_DEVICE, _load_error)
+    if not os.path.exists(LIB_PATH):
+        _load_error = f"{LIB_PATH} is not built (run: python -m bit_blockwise_weight_amd.build)"
+        raise QKError(QK_ERR_NO_DEVICE, _load_error)
+    try:
+        L = ctypes.CDLL(LIB_PATH)
+    except OSError as e:
+        _load_error = f"cannot load {LIB_PATH}: {e}"
+        raise QKError(QK_ERR_NO_DEVICE, _load_error) from e
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    st_p = ctypes.POINTER(QuantState)
+    sigs = {
+        "qk_make_codebook": [i32, ctypes.POINTER(ctypes.c_float)],
+        "qk_quantize_blockwise": [vp, i32, i64, i32, ctypes.POINTER(ctypes.c_float), vp, vp, vp],
+        "qk_double_quant_workspace_size": [i64, ctypes.POINTER(ctypes.c_size_t)],
+        "qk_double_quant": [vp, i64, i32, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "qk_state_init": [st_p, i32, ctypes.POINTER(ctypes.c_float), i64, i64, i32, vp, vp, vp, vp, vp],
+        "qk_dequantize": [st_p, vp, i32, vp],
+        "qk_gemv_nf4": [vp, i32, st_p, vp, vp],
+        "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp],
+    }
+    for name, args in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int32
+    for name in ("qk_last_error", "qk_version", "qk_backend_info"):
+        fn = getattr(L, name)
+        fn.argtypes = []
+        fn.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != QK_OK:
+        raise QKError(status, lib().qk_last_error().decode("utf-8", "replace"))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors passed to libqk must be on a HIP device")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to libqk must be contiguous")
+
+
+def _levels_arg(levels):
+    lv = torch.as_tensor(levels, dtype=torch.float32).detach().cpu().contiguous()
+    if lv.numel() != 16:
+        raise ValueError("a level table has 16 entries")
+    return (ctypes.c_float * 16)(*lv.tolist()), lv
+
+
+def qk_last_error() -> str:
+    return lib().qk_last_error().decode("utf-8", "replace")
+
+
+def qk_version() -> str:
+    return lib().qk_version().decode()
+
+
+def qk_backend_info() -> str:
+    return lib().qk_backend_info().decode()
+
+
+def qk_make_codebook(kind: int = NF4) -> torch.Tensor:
+    buf = (ctypes.c_float * 16)()
+    _check(lib().qk_make_codebook(int(kind), buf))
+    return torch.tensor(list(buf), dtype=torch.float32)
+
+
+def qk_quantize_blockwise(x: torch.Tensor, blocksize: int = 64, levels=None, codes=None, absmax=None):
+    """Returns (codes uint8[ceil(n/2)], absmax fp32[ceil(n/B)]) on x's device."""
+    _require_cuda(x)
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported input dtype {x.dtype}")
+    n = x.numel()
+    if levels is None:
+        levels = qk_make_codebook(NF4)
+    lv, _ = _levels_arg(levels)
+    if codes is None:
+        codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=x.device)
+    if absmax is None:
+        absmax = torch.empty((n + blocksize - 1) // blocksize, dtype=torch.float32, device=x.device)
+    _require_cuda(codes, absmax)
+    with torch.cuda.device(x.device):
+        _check(lib().qk_quantize_blockwise(_ptr(x), _DTYPE_CODE[x.dtype], n, int(blocksize), lv, _ptr(codes),
+                                           _ptr(absmax), ctypes.c_void_p(_stream(x))))
+    return codes, absmax
+
+
+def qk_double_quant_workspace_size(nblocks: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().qk_double_quant_workspace_size(int(nblocks), ctypes.byref(out)))
+    return int(out.value)
+
+
+def qk_double_quant(absmax: torch.Tensor, dq_blocksize: int = QK_DQ_BLOCK, q8=None, scale=None, mean=None,
+                    workspace=None):
+    """Returns (q8 int8[nb], scale fp32[ceil(nb/256)], mean fp32[1])."""
+    _require_cuda(absmax)
+    nb = absmax.numel()
+    dev = absmax.device
+    if q8 is None:
+        q8 = torch.empty(nb, dtype=torch.int8, device=dev)
+    if scale is None:
+        scale = torch.empty((nb + dq_blocksize - 1) // max(1, dq_blocksize), dtype=torch.float32, device=dev)
+    if mean is None:
+        mean = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = qk_double_quant_workspace_size(nb)
+    if workspace is None:
+        workspace = torch.empty(max(8, wsb), dtype=torch.uint8, device=dev)
+    _require_cuda(q8, scale, mean, workspace)
+    with torch.cuda.device(dev):
+        _check(lib().qk_double_quant(_ptr(absmax), nb, int(dq_blocksize), _ptr(q8), _ptr(scale), _ptr(mean),
+                                     _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(absmax))))
+    return q8, scale, mean
+
+
+def qk_state_init(codebook_kind: int, levels, rows: int, cols: int, blocksize: int, codes: torch.Tensor,
+                  absmax=None, q8=None, dq_scale=None, dq_mean=None) -> QuantState:
+    st = QuantState()
+    lv, lv_t = _levels_arg(levels)
+    _check(lib().qk_state_init(ctypes.byref(st), int(codebook_kind), lv, int(rows), int(cols), int(blocksize),
+                               _ptr(codes), _ptr(absmax), _ptr(q8), _ptr(dq_scale), _ptr(dq_mean)))
+    # keep the device buffers alive as long as the descriptor
+    st._keep = (codes, absmax, q8, dq_scale, dq_mean, lv_t)
+    return st
+
+
+def qk_dequantize(state: QuantState, out_dtype=torch.bfloat16, out=None, device=None) -> torch.Tensor:
+    dev = device if device is not None else state._keep[0].device
+    if out is None:
+        out = torch.empty(state.n, dtype=out_dtype, device=dev)
+    _require_cuda(out)
+    with torch.cuda.device(out.device):
+        _check(lib().qk_dequantize(ctypes.byref(state), _ptr(out), _DTYPE_CODE[out.dtype],
+                                   ctypes.c_void_p(_stream(out))))
+    return out
+
+
+def qk_gemv_nf4(x: torch.Tensor, state: QuantState, y=None) -> torch.Tensor:
+    _require_cuda(x)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("qk_gemv_nf4 takes bf16 activations")
+    x2 = x.reshape(-1, state.cols)
+    M = x2.shape[0]
+    if y is None:
+        y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=x.device)
+    _require_cuda(y)
+    with torch.cuda.device(x.device):
+        _check(lib().qk_gemv_nf4(_ptr(x2), M, ctypes.byref(state), _ptr(y), ctypes.c_void_p(_stream(x))))
+    return y
+
+
+def qk_gemm_nf4(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: float = 0.0, Y=None) -> torch.Tensor:
+    _require_cuda(X, A, B)
+    X2 = X.reshape(-1, state.cols)
+    M = X2.shape[0]
+    r = 0 if A is None else A.shape[1]
+    if Y is None:
+        Y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=X.device)
+    _require_cuda(Y)
+    with torch.cuda.device(X.device):
+        _check(lib().qk_gemm_nf4(_ptr(X2), M, ctypes.byref(state), _ptr(A), _ptr(B), int(r), float(lora_scale),
+                                 _ptr(Y), ctypes.c_void_p(_stream(X))))
+    return Y
+
+
+class QuantizedWeight:
+    """A weight W[N, K] quantized on the device: its buffers and its descriptor."""
+
+    def __init__(self, state: QuantState, codes, absmax=None, q8=None, scale=None, mean=None):
+        self.state = state
+        self.codes, self.absmax, self.q8, self.scale, self.mean = codes, absmax, q8, scale, mean
+
+    @property
+    def shape(self):
+        return (self.state.rows, self.state.cols)
+
+    def dequantize(self, out_dtype=torch.bfloat16, out=None):
+        return qk_dequantize(self.state, out_dtype, out, device=self.codes.device)
+
+    def gemv(self, x, y=None):
+        return qk_gemv_nf4(x, self.state, y)
+
+    def gemm(self, X, A=None, B=None, lora_scale=0.0, Y=None):
+        return qk_gemm_nf4(X, self.state, A, B, lora_scale, Y)
+
+
+def quantize(w: torch.Tensor, blocksize: int = 64, kind: int = NF4, double_quant: bool = True,
+             levels=None) -> QuantizedWeight:
+    """qk_quantize_blockwise (+ qk_double_quant) of a 2-D weight and the descriptor."""
+    if w.dim() != 2:
+        raise ValueError("quantize expects a 2-D weight [N, K]")
+    if levels is None:
+        levels = qk_make_codebook(kind)
+    codes, absmax = qk_quantize_blockwise(w, blocksize, levels)
+    if double_quant:
+        q8, scale, mean = qk_double_quant(absmax)
+        st = qk_state_init(kind, levels, w.shape[0], w.shape[1], blocksize, codes, None, q8, scale, mean)
+        return QuantizedWeight(st, codes, None, q8, scale, mean)
+    st = qk_state_init(kind, levels, w.shape[0], w.shape[1], blocksize, codes, absmax)
+    return QuantizedWeight(st, codes, absmax)

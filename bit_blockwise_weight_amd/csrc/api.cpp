@@ -1,0 +1,266 @@
+// C ABI of libqk: argument and descriptor validation, error reporting, kernel
+// launch.  Every check runs on the host before anything is launched and no
+// device pointer is dereferenced here; a rejected call launches nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "qk_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qk_status ok() {
+    g_last_error.clear();
+    return QK_OK;
+}
+
+qk_status fail(qk_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_blocksize(int32_t b) { return b == 64 || b == 128 || b == 256; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The current device must be a gfx950 (checked once per device id).
+qk_status ensure_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) return fail(QK_ERR_NO_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    static int checked[64] = {0};   // 0 unknown, 1 ok, 2 wrong arch
+    if (dev < 64 && checked[dev] == 1) return QK_OK;
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(QK_ERR_NO_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) checked[dev] = good ? 1 : 2;
+    if (!good) return fail(QK_ERR_NO_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+    return QK_OK;
+}
+
+qk_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(QK_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+qk_status validate_state(const qk_quant_state* st) {
+    if (!st) return fail(QK_ERR_INVALID_ARG, "quant state pointer is NULL");
+    if (st->magic != QK_STATE_MAGIC)
+        return fail(QK_ERR_BAD_STATE, "quant state: bad magic 0x%08x (not a qk_quant_state or corrupted)", st->magic);
+    if (st->version != QK_STATE_VERSION)
+        return fail(QK_ERR_BAD_STATE, "quant state: unknown version %u (this library reads %u)", st->version,
+                    QK_STATE_VERSION);
+    if (st->struct_bytes != sizeof(qk_quant_state))
+        return fail(QK_ERR_BAD_STATE, "quant state: struct_bytes %u != %zu", st->struct_bytes, sizeof(qk_quant_state));
+    if (st->rows < 1 || st->cols < 1 || st->n < 1)
+        return fail(QK_ERR_BAD_STATE, "quant state: rows, cols and n must be >= 1");
+    if (st->rows > (int64_t)1 << 40 || st->cols > (int64_t)1 << 40 || st->n != st->rows * st->cols)
+        return fail(QK_ERR_BAD_STATE, "quant state: n (%lld) != rows (%lld) * cols (%lld)", (long long)st->n,
+                    (long long)st->rows, (long long)st->cols);
+    if (!valid_blocksize(st->blocksize))
+        return fail(QK_ERR_BAD_STATE, "quant state: block size %d (expected 64, 128 or 256)", st->blocksize);
+    if (st->codebook_kind < QK_NF4 || st->codebook_kind > QK_CUSTOM)
+        return fail(QK_ERR_BAD_STATE, "quant state: unknown codebook kind %d", st->codebook_kind);
+    if (st->reserved != 0) return fail(QK_ERR_BAD_STATE, "quant state: reserved field is not 0");
+    for (int i = 0; i < 16; ++i)
+        if (!std::isfinite(st->levels[i])) return fail(QK_ERR_BAD_STATE, "quant state: level %d is not finite", i);
+    if (!st->codes) return fail(QK_ERR_BAD_STATE, "quant state: codes pointer is NULL");
+    if (!aligned(st->codes, 4)) return fail(QK_ERR_BAD_STATE, "quant state: codes must be 4-byte aligned");
+    if (st->nested == 1) {
+        if (st->dq_blocksize != QK_DQ_BLOCK)
+            return fail(QK_ERR_BAD_STATE, "quant state: nested with dq_blocksize %d (expected 256)", st->dq_blocksize);
+        if (!st->q8 || !st->dq_scale || !st->dq_mean)
+            return fail(QK_ERR_BAD_STATE, "quant state: nested needs q8, dq_scale and dq_mean");
+        if (st->absmax) return fail(QK_ERR_BAD_STATE, "quant state: nested state also carries plain absmax");
+        if (!aligned(st->dq_scale, 4) || !aligned(st->dq_mean, 4))
+            return fail(QK_ERR_BAD_STATE, "quant state: dq_scale and dq_mean must be 4-byte aligned");
+    } else if (st->nested == 0) {
+        if (!st->absmax) return fail(QK_ERR_BAD_STATE, "quant state: plain state needs absmax");
+        if (st->q8 || st->dq_scale || st->dq_mean || st->dq_blocksize != 0)
+            return fail(QK_ERR_BAD_STATE, "quant state: plain state carries double-quant fields");
+        if (!aligned(st->absmax, 4)) return fail(QK_ERR_BAD_STATE, "quant state: absmax must be 4-byte aligned");
+    } else {
+        return fail(QK_ERR_BAD_STATE, "quant state: nested flag %d (expected 0 or 1)", st->nested);
+    }
+    return QK_OK;
+}
+
+qk::DeqArgs deq_args(const qk_quant_state* st) {
+    qk::DeqArgs a;
+    a.codes = st->codes;
+    a.absmax = st->absmax;
+    a.q8 = st->q8;
+    a.dq_scale = st->dq_scale;
+    a.dq_mean = st->dq_mean;
+    a.n = st->n;
+    a.blocksize = st->blocksize;
+    a.nested = st->nested;
+    std::memcpy(a.levels, st->levels, sizeof(a.levels));
+    return a;
+}
+
+thread_local const char* g_gemv_variant = "none";
+thread_local const char* g_gemm_variant = "none";
+
+}  // namespace
+
+extern "C" {
+
+qk_status qk_make_codebook(int32_t kind, float* levels_out) {
+    if (!levels_out) return fail(QK_ERR_INVALID_ARG, "qk_make_codebook: levels_out is NULL");
+    if (kind == QK_NF4) return qk::make_nf4(levels_out) == QK_OK ? ok() : QK_ERR_INVALID_ARG;
+    if (kind == QK_FP4) return qk::make_fp4(levels_out) == QK_OK ? ok() : QK_ERR_INVALID_ARG;
+    return fail(QK_ERR_INVALID_ARG, "qk_make_codebook: unknown kind %d (QK_NF4=0, QK_FP4=1)", kind);
+}
+
+qk_status qk_quantize_blockwise(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize, const float* levels,
+                                uint8_t* codes, float* absmax, void* stream) {
+    if (!x || !levels || !codes || !absmax)
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: NULL pointer argument");
+    if (n < 1) return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: n must be >= 1 (got %lld)", (long long)n);
+    if (x_dtype != QK_BF16 && x_dtype != QK_F16 && x_dtype != QK_F32)
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: unknown x dtype %d", x_dtype);
+    if (!valid_blocksize(blocksize))
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: block size %d (expected 64, 128 or 256)", blocksize);
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(absmax, 4))
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: x must be 16-byte aligned, codes and absmax 4-byte");
+    qk::QuantLut lut;
+    const char* why = "";
+    const qk_status lst = qk::build_quant_lut(levels, &lut, &why);
+    if (lst != QK_OK) return fail(lst, "qk_quantize_blockwise: %s", why);
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_quantize(x, x_dtype, n, blocksize, lut, codes, absmax,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                    "qk_quantize_blockwise");
+}
+
+qk_status qk_double_quant_workspace_size(int64_t nblocks, size_t* bytes) {
+    if (!bytes) return fail(QK_ERR_INVALID_ARG, "qk_double_quant_workspace_size: bytes is NULL");
+    if (nblocks < 1) return fail(QK_ERR_INVALID_ARG, "qk_double_quant_workspace_size: nblocks must be >= 1");
+    *bytes = qk::dq_workspace_bytes(nblocks);
+    return ok();
+}
+
+qk_status qk_double_quant(const float* absmax, int64_t nblocks, int32_t dq_blocksize, int8_t* q8, float* scale,
+                          float* mean, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!absmax || !q8 || !scale || !mean) return fail(QK_ERR_INVALID_ARG, "qk_double_quant: NULL pointer argument");
+    if (nblocks < 1) return fail(QK_ERR_INVALID_ARG, "qk_double_quant: nblocks must be >= 1");
+    if (dq_blocksize != QK_DQ_BLOCK)
+        return fail(QK_ERR_UNSUPPORTED, "qk_double_quant: dq_blocksize %d (only 256 is implemented)", dq_blocksize);
+    if (!aligned(absmax, 4) || !aligned(q8, 4) || !aligned(scale, 4) || !aligned(mean, 4))
+        return fail(QK_ERR_INVALID_ARG, "qk_double_quant: absmax, q8, scale and mean must be 4-byte aligned");
+    const size_t need = qk::dq_workspace_bytes(nblocks);
+    if (!workspace || workspace_bytes < need)
+        return fail(QK_ERR_WORKSPACE, "qk_double_quant: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 8)) return fail(QK_ERR_INVALID_ARG, "qk_double_quant: workspace must be 8-byte aligned");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_double_quant(absmax, nblocks, q8, scale, mean, workspace,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                    "qk_double_quant");
+}
+
+qk_status qk_state_init(qk_quant_state* st, int32_t codebook_kind, const float* levels, int64_t rows, int64_t cols,
+                        int32_t blocksize, const uint8_t* codes, const float* absmax, const int8_t* q8,
+                        const float* dq_scale, const float* dq_mean) {
+    if (!st || !levels || !codes) return fail(QK_ERR_INVALID_ARG, "qk_state_init: NULL state, levels or codes");
+    if (rows < 1 || cols < 1) return fail(QK_ERR_INVALID_ARG, "qk_state_init: rows and cols must be >= 1");
+    if (!valid_blocksize(blocksize))
+        return fail(QK_ERR_INVALID_ARG, "qk_state_init: block size %d (expected 64, 128 or 256)", blocksize);
+    const bool nested = q8 || dq_scale || dq_mean;
+    if (nested && absmax) return fail(QK_ERR_INVALID_ARG, "qk_state_init: give either absmax or q8/dq_scale/dq_mean");
+    if (nested && !(q8 && dq_scale && dq_mean))
+        return fail(QK_ERR_INVALID_ARG, "qk_state_init: a nested state needs q8, dq_scale and dq_mean");
+    if (!nested && !absmax) return fail(QK_ERR_INVALID_ARG, "qk_state_init: absmax is NULL");
+    std::memset(st, 0, sizeof(*st));
+    st->magic = QK_STATE_MAGIC;
+    st->version = QK_STATE_VERSION;
+    st->struct_bytes = sizeof(qk_quant_state);
+    st->codebook_kind = codebook_kind;
+    st->rows = rows;
+    st->cols = cols;
+    st->n = rows * cols;
+    st->blocksize = blocksize;
+    st->nested = nested ? 1 : 0;
+    st->dq_blocksize = nested ? QK_DQ_BLOCK : 0;
+    std::memcpy(st->levels, levels, sizeof(st->levels));
+    st->codes = codes;
+    st->absmax = absmax;
+    st->q8 = q8;
+    st->dq_scale = dq_scale;
+    st->dq_mean = dq_mean;
+    return ok();
+}
+
+qk_status qk_dequantize(const qk_quant_state* st, void* out, int32_t out_dtype, void* stream) {
+    const qk_status v = validate_state(st);
+    if (v != QK_OK) return v;
+    if (!out) return fail(QK_ERR_INVALID_ARG, "qk_dequantize: out is NULL");
+    if (out_dtype != QK_BF16 && out_dtype != QK_F32)
+        return fail(QK_ERR_INVALID_ARG, "qk_dequantize: out dtype %d (expected QK_F32 or QK_BF16)", out_dtype);
+    if (!aligned(out, 16)) return fail(QK_ERR_INVALID_ARG, "qk_dequantize: out must be 16-byte aligned");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_dequantize(deq_args(st), out, out_dtype, reinterpret_cast<hipStream_t>(stream)),
+                    "qk_dequantize");
+}
+
+qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* y, void* stream) {
+    const qk_status v = validate_state(st);
+    if (v != QK_OK) return v;
+    if (!x || !y) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4: NULL x or y");
+    if (M < 1 || M > 16) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4: M must be in 1..16 (got %d)", M);
+    if (!aligned(x, 16) || !aligned(y, 4)) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4: x must be 16-byte aligned, y 4-byte");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    qk::MatArgs w{deq_args(st), st->rows, st->cols};
+    return launched(qk::launch_gemv(x, M, w, y, reinterpret_cast<hipStream_t>(stream), &g_gemv_variant),
+                    "qk_gemv_nf4");
+}
+
+qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const void* A, const void* B, int32_t r,
+                      float lora_scale, void* Y, void* stream) {
+    const qk_status v = validate_state(st);
+    if (v != QK_OK) return v;
+    if (!X || !Y) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: NULL X or Y");
+    if (M < 1 || M > ((int64_t)1 << 31)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: M must be in 1..2^31");
+    if ((A == nullptr) != (B == nullptr)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: give both LoRA A and B, or neither");
+    if (A && (r < 1 || r > 64)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: LoRA rank must be in 1..64 (got %d)", r);
+    if (A && !std::isfinite(lora_scale)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: lora_scale is not finite");
+    if (!aligned(X, 2) || !aligned(Y, 2) || (A && (!aligned(A, 2) || !aligned(B, 2))))
+        return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: bf16 buffers must be 2-byte aligned");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    qk::MatArgs w{deq_args(st), st->rows, st->cols};
+    return launched(qk::launch_gemm(X, M, w, A, B, A ? r : 0, lora_scale, Y, reinterpret_cast<hipStream_t>(stream),
+                                    &g_gemm_variant),
+                    "qk_gemm_nf4");
+}
+
+const char* qk_last_error(void) { return g_last_error.c_str(); }
+
+const char* qk_version(void) { return "qk 0.1.0 gfx950"; }
+
+const char* qk_backend_info(void) {
+    static thread_local std::string s;
+    s = std::string("quantize: wave per 512 elements, DPP block absmax, reciprocal+Markstein division, LDS bin table; ") +
+        "double_quant: fp64 tree partials + int8 per 256; dequantize: LDS levels; gemv: " + g_gemv_variant +
+        "; gemm: " + g_gemm_variant;
+    return s.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal declarations shared by the host API and the HIP kernels of libqk.
+// Not installed; the public ABI is include/qk.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qk.h"
+
+namespace qk {
+
+// ---------------------------------------------------------------------------
+// Exact nearest-level lookup used by the quantize kernel.
+//
+// The normalised value t lies in [-1, 1].  It is binned by
+//     bin(t) = RN(t * S + S)   (an integer in [0, 2S], computed as the low 24
+//                                bits of fmaf(t, S, S + 2^23))
+// which is monotone in t.  The host evaluates the same fmaf, finds in which bin
+// every decision threshold falls, and checks that no bin holds two.  Each bin
+// then stores the code below its threshold, the code above it, and the
+// threshold itself (a binary32 value T such that "t >= T" is exactly the
+// nearest-level decision, tie rule included).  A bin without a threshold
+// stores T = 2 (never reached).
+// ---------------------------------------------------------------------------
+constexpr int kLutMaxS = 64;
+constexpr int kLutMaxBins = 2 * kLutMaxS + 1;
+
+struct QuantLut {
+    float S;                 // bins per unit of t
+    float C;                 // S + 2^23
+    int32_t nbins;           // 2S + 1
+    int32_t sorted;          // 1: code order is value order (codes are c_lo + [t >= T])
+    float T[kLutMaxBins];    // threshold of each bin
+    uint32_t c[kLutMaxBins]; // sorted: c_lo; otherwise c_lo | (c_hi << 16)
+};
+
+// Build the lookup for a level table (code order).  Returns QK_OK,
+// QK_ERR_INVALID_ARG (non-finite or out of [-1, 1]) or QK_ERR_UNSUPPORTED (a
+// midpoint that is not exact in binary64, or thresholds too close for S <= 64).
+qk_status build_quant_lut(const float levels[16], QuantLut* lut, const char** why);
+
+// Level tables.
+qk_status make_nf4(float out[16]);
+qk_status make_fp4(float out[16]);
+
+// Standard normal quantile, Wichura's algorithm AS 241 (PPND16), fp64.
+double normal_quantile(double p);
+
+// Compute units of the current device (cached; 256 if the query fails).
+int device_cu_count();
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (return hipError_t of the launch).
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize,
+                           const QuantLut& lut, uint8_t* codes, float* absmax, hipStream_t s);
+
+size_t dq_workspace_bytes(int64_t nblocks);
+hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int8_t* q8, float* scale,
+                               float* mean, void* workspace, hipStream_t s);
+
+struct DeqArgs {
+    const uint8_t* codes;
+    const float* absmax;
+    const int8_t* q8;
+    const float* dq_scale;
+    const float* dq_mean;
+    int64_t n;
+    int32_t blocksize;
+    int32_t nested;
+    float levels[16];
+};
+hipError_t launch_dequantize(const DeqArgs& a, void* out, int32_t out_dtype, hipStream_t s);
+
+struct MatArgs {
+    DeqArgs w;       // the weight [N, K]
+    int64_t N;
+    int64_t K;
+};
+hipError_t launch_gemv(const void* x, int32_t M, const MatArgs& w, void* y, hipStream_t s,
+                       const char** variant);
+hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B,
+                       int32_t r, float lora_scale, void* Y, hipStream_t s, const char** variant);
+
+}  // namespace qk

@@ -1,0 +1,259 @@
+/*
+ * qk.h — C ABI of a blockwise 4-bit weight quantization library for AMD MI355X
+ * (gfx950): NF4 / FP4 quantize and dequantize with one fp32 absmax per block,
+ * double quantization of the absmax array, and the dequantize-fused decode GEMV
+ * and prefill / training GEMM of a frozen QLoRA base layer.
+ *
+ * Sources of the definitions (cited by page title and section):
+ *  [NF4]   "篇2-bitsandbytes-具体观-算法与实现剖析" (xyzblog), §2.2 QLoRA / NF4,
+ *          【原理】① (NF4 levels: 16 equal-probability slabs of N(0,1), each
+ *          represented by its midpoint, normalised to [-1, 1]), 【原理】② (double
+ *          quantization of the absmax), 【代码】 (quantize_4bit with blocksize 64,
+ *          quant_type nf4 / fp4, compress_statistics; the quant_state fields
+ *          absmax / code / state2 / offset / nested_absmax; FP4 built as the
+ *          2-exponent-bit, 1-mantissa-bit signed case of a generic float-format
+ *          table; the 4-bit linear forward = dequantize + matmul), 【例子】 and
+ *          figure 2-2 (the pipeline: split into blocks of 64, absmax per block,
+ *          divide, table lookup, pack two codes per byte, quantize the absmax
+ *          again into state2).
+ *  [DEQ]   "LLM 相關知識" (technicalnotes, tag qlora), section 5 動態反量化:
+ *          the 4-bit base is restored to BF16 layer by layer right before its
+ *          matmul; section 2-2 LoRA and section 8 (merge / no-merge): the
+ *          layer output is the base output plus the LoRA output X·A·B.
+ *  [YOLO]  "Tim Dettmers 如何用 bitsandbytes 與 QLoRA 降低 LLM 訓練門檻？"
+ *          (yololab), sections on NF4, double quantization and QLoRA: the
+ *          quantizer, loader and kernel must share exactly one definition of
+ *          codebook, block size, scale and packing.
+ *
+ * Conventions for every call
+ *  - Memory: the caller owns every buffer.  Pointers documented "device" must
+ *    point to device memory of the current HIP device; "host" pointers to
+ *    ordinary host memory.  The library allocates no device memory and frees
+ *    nothing; the one call that needs scratch space takes a caller workspace.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Every device call is asynchronous on that stream and never
+ *    synchronizes.
+ *  - Errors: every call returns a qk_status.  Arguments are validated on the
+ *    host before anything is launched, and no device pointer is dereferenced on
+ *    the host; a rejected call launches nothing.  A message for the last
+ *    failure of the calling thread is available from qk_last_error().
+ *  - Numerics: inputs must be finite (not checked in the kernels).  All sizes
+ *    are element counts unless stated otherwise.
+ *  - Layout of a quantized tensor of n elements, block size B (the weight
+ *    W[N, K] is row-major, so n = N*K and blocks run over the flattened
+ *    tensor; a block may straddle two rows when K % B != 0):
+ *      codes     uint8  [ceil(n/2)]  element 2t in the high nibble of byte t,
+ *                                    element 2t+1 in the low nibble; the low
+ *                                    nibble of the last byte is 0 when n is odd
+ *      absmax    fp32   [nb]         nb = ceil(n/B), block j = [jB, min(jB+B, n))
+ *      or, double-quantized (nested):
+ *      q8        int8   [nb]
+ *      dq_scale  fp32   [nd]         nd = ceil(nb/256)
+ *      dq_mean   fp32   [1]
+ */
+#ifndef QK_H
+#define QK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qk_status;
+enum {
+    QK_OK = 0,
+    QK_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad enum, misaligned buffer */
+    QK_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement */
+    QK_ERR_BAD_STATE = -3,     /* qk_quant_state with a wrong magic, version, size or
+                                  inconsistent fields (unknown or corrupted metadata) */
+    QK_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed */
+    QK_ERR_NO_DEVICE = -5,     /* no usable gfx950 device */
+    QK_ERR_WORKSPACE = -6      /* workspace missing or smaller than required */
+};
+
+/* element types */
+enum { QK_F32 = 0, QK_BF16 = 1, QK_F16 = 2 };
+
+/* level tables */
+enum { QK_NF4 = 0, QK_FP4 = 1, QK_CUSTOM = 2 };
+
+#define QK_STATE_MAGIC 0x314B5451u   /* "QTK1" little-endian */
+#define QK_STATE_VERSION 1u
+#define QK_DQ_BLOCK 256
+
+/*
+ * Descriptor of one quantized tensor (the [NF4] quant_state).  Plain data: the
+ * pointers are device pointers owned by the caller.  Build it with
+ * qk_state_init(); a descriptor whose magic, version or struct_bytes do not
+ * match, or whose fields disagree (n != rows*cols, bad block size, missing
+ * pointers), is rejected with QK_ERR_BAD_STATE by every call that takes one.
+ */
+typedef struct qk_quant_state {
+    uint32_t magic;          /* QK_STATE_MAGIC */
+    uint32_t version;        /* QK_STATE_VERSION */
+    uint32_t struct_bytes;   /* sizeof(qk_quant_state) */
+    int32_t codebook_kind;   /* QK_NF4, QK_FP4 or QK_CUSTOM (informative) */
+    int64_t n;               /* number of elements = rows * cols */
+    int64_t rows;            /* N: output features of the weight */
+    int64_t cols;            /* K: input features of the weight */
+    int32_t blocksize;       /* B: 64, 128 or 256 */
+    int32_t nested;          /* 1: absmax is double-quantized (q8, dq_scale, dq_mean) */
+    int32_t dq_blocksize;    /* 256 when nested, else 0 */
+    int32_t reserved;        /* 0 */
+    float levels[16];        /* level of each 4-bit code, in code order */
+    const uint8_t* codes;    /* device, [ceil(n/2)], 4-byte aligned */
+    const float* absmax;     /* device, [nb], when !nested (else NULL) */
+    const int8_t* q8;        /* device, [nb], when nested (else NULL) */
+    const float* dq_scale;   /* device, [ceil(nb/256)], when nested (else NULL) */
+    const float* dq_mean;    /* device, [1], when nested (else NULL) */
+} qk_quant_state;
+
+/*
+ * qk_make_codebook — host.  [NF4] 【原理】① and 【代码】.
+ *   kind QK_NF4: levels[i] = RN_fp32( Phi^-1((2i+1)/32) / Phi^-1(31/32) ),
+ *       i = 0..15, with Phi^-1 the standard normal quantile evaluated in fp64
+ *       (Wichura's algorithm AS 241); symmetric, strictly increasing, no zero.
+ *   kind QK_FP4: the signed E2M1 minifloat with subnormals in code order
+ *       (code = sign<<3 | exponent<<1 | mantissa), normalised by its largest
+ *       magnitude: {0, 1/12, 1/6, 1/4, 1/3, 1/2, 2/3, 1, -0, -1/12, ..., -1}.
+ *   levels_out: host, float[16], written.
+ *   Errors: QK_ERR_INVALID_ARG for a null pointer or an unknown kind.
+ */
+qk_status qk_make_codebook(int32_t kind, float* levels_out);
+
+/*
+ * qk_quantize_blockwise — device.  [NF4] 【例子】, figure 2-2; [YOLO] sections
+ * on 8-bit optimizers (a scale per block) and NF4.
+ *   For each block j of the flattened input:
+ *     absmax[j] = max |x_k| over the block (fp32, exact);
+ *     t_k  = RN_fp32(x_k / absmax[j])   (IEEE division; t = +0 if absmax is 0);
+ *     code = index of the level nearest to t_k, exactly; on a tie the smaller
+ *            index wins;
+ *   and the codes are packed two per byte, high nibble first.
+ *   x:         device, [n] elements of x_dtype (QK_BF16, QK_F16 or QK_F32),
+ *              16-byte aligned.
+ *   n:         number of elements, >= 1.
+ *   blocksize: 64, 128 or 256.
+ *   levels:    host, float[16] in code order (any finite table in [-1, 1]
+ *              whose distinct values have binary64-exact midpoints; both
+ *              qk_make_codebook tables qualify).  Copied at the call.
+ *   codes:     device, [ceil(n/2)] bytes, 4-byte aligned, written.
+ *   absmax:    device, [ceil(n/blocksize)] fp32, 4-byte aligned, written.
+ *   Errors: QK_ERR_INVALID_ARG (null / misaligned pointer, n < 1, bad block
+ *   size or dtype, levels outside [-1, 1] or not finite); QK_ERR_UNSUPPORTED
+ *   for a table whose lookup cannot be built exactly; QK_ERR_HIP on launch
+ *   failure.
+ */
+qk_status qk_quantize_blockwise(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize,
+                                const float* levels, uint8_t* codes, float* absmax, void* stream);
+
+/*
+ * qk_double_quant_workspace_size — host.  Bytes of device workspace that
+ * qk_double_quant needs for `nblocks` absmax values (a few bytes per 4096).
+ */
+qk_status qk_double_quant_workspace_size(int64_t nblocks, size_t* bytes);
+
+/*
+ * qk_double_quant — device.  [NF4] 【原理】② and 【代码】 (state2, offset);
+ * [YOLO] section "Double quantization 連 scale 本身也壓縮".
+ *     mean  = RN_fp32( T / nblocks ), T = the fp64 sum of absmax along a
+ *             perfect binary tree (absmax zero-padded to the next power of two,
+ *             neighbours added level by level), divided in fp64;
+ *     c_j   = RN_fp32(absmax_j - mean);
+ *     for each block d of dq_blocksize values (the last may be partial):
+ *       s_d = max |c_j|,  scale[d] = RN_fp32(s_d / 127),
+ *       q8_j = 0 if s_d == 0, else round-half-even( RN_fp32(RN_fp32(c_j / s_d) * 127) ).
+ *   absmax:    device, [nblocks] fp32 (nblocks >= 1), 4-byte aligned.
+ *   dq_blocksize: 256.
+ *   q8:        device, [nblocks] int8, written.
+ *   scale:     device, [ceil(nblocks/256)] fp32, written.
+ *   mean:      device, [1] fp32, written.
+ *   workspace: device, at least qk_double_quant_workspace_size() bytes,
+ *              8-byte aligned; contents on entry are ignored.
+ *   Errors: QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED (dq_blocksize != 256),
+ *   QK_ERR_WORKSPACE, QK_ERR_HIP.
+ */
+qk_status qk_double_quant(const float* absmax, int64_t nblocks, int32_t dq_blocksize, int8_t* q8,
+                          float* scale, float* mean, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * qk_state_init — host.  Fills a descriptor.  Pass absmax for a plain state,
+ * or q8 / dq_scale / dq_mean (and absmax == NULL) for a nested one.
+ *   levels: host float[16] in code order, copied.
+ *   Errors: QK_ERR_INVALID_ARG (null state / codes / levels, rows or cols < 1,
+ *   bad block size, neither or both absmax forms given).
+ */
+qk_status qk_state_init(qk_quant_state* st, int32_t codebook_kind, const float* levels,
+                        int64_t rows, int64_t cols, int32_t blocksize, const uint8_t* codes,
+                        const float* absmax, const int8_t* q8, const float* dq_scale,
+                        const float* dq_mean);
+
+/*
+ * qk_dequantize — device.  [DEQ] section 5; [NF4] 【代码】.
+ *     a'_j = absmax[j]                                   (plain), or
+ *     a'_j = RN_fp32( RN_fp32(q8_j * dq_scale[d]) + dq_mean )   (nested);
+ *     y_k  = RN_fp32( levels[code_k] * a'_{block(k)} )  (separate roundings, no FMA)
+ *   written as fp32 or as bf16 (round to nearest even).  Signed zeros kept.
+ *   st:  host pointer to a valid descriptor.
+ *   out: device, [n] elements of out_dtype (QK_F32 or QK_BF16), 16-byte aligned.
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_HIP.
+ */
+qk_status qk_dequantize(const qk_quant_state* st, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * qk_gemv_nf4 — device.  Decode-time product with the dequantized weight:
+ *     y[m, :] = x[m, :] · deq(W)^T,  m < M,
+ *   [NF4] 【代码】 (4-bit linear forward: dequantize + matmul), [DEQ] section 5.
+ *   The weight is dequantized inside the kernel and never written out.  The
+ *   products use bf16 copies of the 16 levels, scaled by the block's absmax in
+ *   fp32, with fp32 accumulation: the result agrees with the fp64 product on
+ *   the bf16-dequantized weight to rel. Frobenius error <= 5e-3 and max error
+ *   <= 2e-2 * max|ref|.
+ *   x:  device, [M, K] bf16 row-major (K = st->cols), 16-byte aligned.
+ *   M:  1..16.
+ *   st: host pointer to a valid descriptor of W [N, K] (N = st->rows).
+ *   y:  device, [M, N] bf16 row-major, written.
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG (M outside 1..16, null or
+ *   misaligned pointers), QK_ERR_HIP.
+ */
+qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* y, void* stream);
+
+/*
+ * qk_gemm_nf4 — device.  Prefill / training forward of a frozen 4-bit base
+ * layer with an unmerged LoRA adapter ([DEQ] sections 2-2 and 8; [NF4] §2.2):
+ *     Y = X · deq(W)^T + lora_scale · (X · A) · B
+ *   The weight is dequantized tile by tile to bf16 exactly as qk_dequantize
+ *   would write it, multiplied on bf16 matrix cores with fp32 accumulation;
+ *   the rank-r LoRA product is accumulated in the same pass and added in the
+ *   epilogue.  Agreement with the fp64 reference: rel. Frobenius <= 5e-3,
+ *   max error <= 2e-2 * max|ref|.
+ *   X: device, [M, K] bf16 row-major, K = st->cols.
+ *   M: >= 1.
+ *   A: device, [K, r] bf16 row-major, or NULL (no LoRA term).
+ *   B: device, [r, N] bf16 row-major, or NULL (no LoRA term).
+ *   r: LoRA rank, 1..64 when A and B are given (ignored otherwise).
+ *   lora_scale: alpha / r.
+ *   Y: device, [M, N] bf16 row-major, written.
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_HIP.
+ */
+qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const void* A,
+                      const void* B, int32_t r, float lora_scale, void* Y, void* stream);
+
+/* Message for the calling thread's last failed call ("" if none).  The
+ * string stays valid until the thread's next qk_* call. */
+const char* qk_last_error(void);
+
+/* Library version string, e.g. "qk 0.1.0 gfx950". */
+const char* qk_version(void);
+
+/* Which kernel variant each call uses, for logs and benchmarks. */
+const char* qk_backend_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK_H */

@@ -1,0 +1,177 @@
+"""C-ABI tests that need no GPU: the library loads, exports every call that
+include/qk.h declares, builds the level tables on the host exactly as the
+oracle defines them, and rejects bad arguments and corrupted descriptors with
+the documented status before touching any device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_blockwise_weight_amd as qk
+from oracle import codebook
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: every case fails validation first
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "qk.h"), encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qk_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qk.LIB_PATH):
+        pytest.fail("libqk.so is not built; run python -m bit_blockwise_weight_amd.build")
+    return qk.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_symbols()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_version_and_backend_strings(L):
+    assert "gfx950" in qk.qk_version()
+    assert "quantize" in qk.qk_backend_info()
+
+
+def test_nf4_table_matches_oracle_bitwise(L):
+    got = qk.qk_make_codebook(qk.NF4).numpy()
+    np.testing.assert_array_equal(got.view(np.uint32), codebook.nf4_levels().view(np.uint32))
+
+
+def test_fp4_table_matches_oracle_bitwise(L):
+    got = qk.qk_make_codebook(qk.FP4).numpy()
+    np.testing.assert_array_equal(got.view(np.uint32), codebook.fp4_levels().view(np.uint32))
+
+
+def test_make_codebook_errors(L):
+    buf = (ctypes.c_float * 16)()
+    assert L.qk_make_codebook(7, buf) == qk.QK_ERR_INVALID_ARG
+    assert "unknown kind" in qk.qk_last_error()
+    assert L.qk_make_codebook(0, None) == qk.QK_ERR_INVALID_ARG
+
+
+def _levels(kind=qk.NF4):
+    lv = qk.qk_make_codebook(kind).tolist()
+    return (ctypes.c_float * 16)(*lv)
+
+
+def test_quantize_argument_errors(L):
+    lv = _levels()
+    s = None
+    assert L.qk_quantize_blockwise(None, qk.QK_BF16, 64, 64, lv, FAKE, FAKE, s) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_quantize_blockwise(FAKE, qk.QK_BF16, 0, 64, lv, FAKE, FAKE, s) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_quantize_blockwise(FAKE, qk.QK_BF16, 64, 32, lv, FAKE, FAKE, s) == qk.QK_ERR_INVALID_ARG
+    assert "block size" in qk.qk_last_error()
+    assert L.qk_quantize_blockwise(FAKE, 9, 64, 64, lv, FAKE, FAKE, s) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_quantize_blockwise(ctypes.c_void_p(0x10002), qk.QK_BF16, 64, 64, lv, FAKE, FAKE, s) \
+        == qk.QK_ERR_INVALID_ARG
+    assert "aligned" in qk.qk_last_error()
+    bad = (ctypes.c_float * 16)(*([2.0] + [0.0] * 15))
+    assert L.qk_quantize_blockwise(FAKE, qk.QK_BF16, 64, 64, bad, FAKE, FAKE, s) == qk.QK_ERR_INVALID_ARG
+    nan = (ctypes.c_float * 16)(*([float("nan")] + [0.0] * 15))
+    assert L.qk_quantize_blockwise(FAKE, qk.QK_BF16, 64, 64, nan, FAKE, FAKE, s) == qk.QK_ERR_INVALID_ARG
+
+
+def test_quantize_rejects_table_whose_lookup_is_not_exact(L):
+    # three levels one ulp apart: two thresholds one ulp apart cannot sit in different bins
+    lv = qk.qk_make_codebook(qk.NF4).numpy().copy()
+    lv[13] = np.nextafter(lv[12], np.float32(1.0))
+    lv[14] = np.nextafter(lv[13], np.float32(1.0))
+    arr = (ctypes.c_float * 16)(*lv.tolist())
+    assert L.qk_quantize_blockwise(FAKE, qk.QK_BF16, 64, 64, arr, FAKE, FAKE, None) == qk.QK_ERR_UNSUPPORTED
+
+
+def test_double_quant_errors_and_workspace(L):
+    assert qk.qk_double_quant_workspace_size(1) >= 8
+    assert qk.qk_double_quant_workspace_size(4096 * 4096 + 1) >= 8 * 4097
+    out = ctypes.c_size_t()
+    assert L.qk_double_quant_workspace_size(0, ctypes.byref(out)) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_double_quant(FAKE, 1000, 128, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == qk.QK_ERR_UNSUPPORTED
+    assert L.qk_double_quant(FAKE, 1000, 256, FAKE, FAKE, FAKE, None, 0, None) == qk.QK_ERR_WORKSPACE
+    assert L.qk_double_quant(FAKE, 1000, 256, FAKE, FAKE, FAKE, FAKE, 0, None) == qk.QK_ERR_WORKSPACE
+    assert "workspace" in qk.qk_last_error()
+    assert L.qk_double_quant(FAKE, 0, 256, FAKE, FAKE, FAKE, FAKE, 64, None) == qk.QK_ERR_INVALID_ARG
+
+
+def _state(nested=True):
+    st = qk.QuantState()
+    lv = _levels()
+    if nested:
+        rc = L_().qk_state_init(ctypes.byref(st), qk.NF4, lv, 4, 64, 64, FAKE, None, FAKE, FAKE, FAKE)
+    else:
+        rc = L_().qk_state_init(ctypes.byref(st), qk.NF4, lv, 4, 64, 64, FAKE, FAKE, None, None, None)
+    assert rc == qk.QK_OK
+    return st
+
+
+def L_():
+    return qk.lib()
+
+
+def test_state_init_fills_descriptor(L):
+    st = _state()
+    assert st.magic == qk.QK_STATE_MAGIC and st.version == qk.QK_STATE_VERSION
+    assert st.struct_bytes == ctypes.sizeof(qk.QuantState) == 160
+    assert st.n == 256 and st.nested == 1 and st.dq_blocksize == 256
+    lv = _levels()
+    bad = qk.QuantState()
+    assert L.qk_state_init(ctypes.byref(bad), qk.NF4, lv, 4, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE) \
+        == qk.QK_ERR_INVALID_ARG
+    assert L.qk_state_init(ctypes.byref(bad), qk.NF4, lv, 0, 64, 64, FAKE, FAKE, None, None, None) \
+        == qk.QK_ERR_INVALID_ARG
+    assert L.qk_state_init(ctypes.byref(bad), qk.NF4, lv, 4, 64, 48, FAKE, FAKE, None, None, None) \
+        == qk.QK_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value", [
+    ("magic", 0xDEADBEEF), ("version", 99), ("struct_bytes", 100), ("blocksize", 32), ("n", 255),
+    ("nested", 2), ("dq_blocksize", 128), ("q8", None), ("codes", None), ("reserved", 1),
+    ("codebook_kind", 17), ("codes", 0x10001),
+])
+def test_corrupted_descriptor_is_rejected_by_every_consumer(L, field, value):
+    st = _state()
+    setattr(st, field, value)
+    y = FAKE
+    assert L.qk_dequantize(ctypes.byref(st), y, qk.QK_BF16, None) == qk.QK_ERR_BAD_STATE
+    assert L.qk_gemv_nf4(FAKE, 1, ctypes.byref(st), y, None) == qk.QK_ERR_BAD_STATE
+    assert L.qk_gemm_nf4(FAKE, 4, ctypes.byref(st), None, None, 0, 0.0, y, None) == qk.QK_ERR_BAD_STATE
+    assert "quant state" in qk.qk_last_error()
+
+
+def test_nonfinite_level_in_descriptor(L):
+    st = _state()
+    st.levels[3] = float("inf")
+    assert L.qk_dequantize(ctypes.byref(st), FAKE, qk.QK_BF16, None) == qk.QK_ERR_BAD_STATE
+
+
+def test_consumer_argument_errors(L):
+    st = _state()
+    assert L.qk_dequantize(ctypes.byref(st), None, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_dequantize(ctypes.byref(st), FAKE, qk.QK_F16, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_dequantize(None, FAKE, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemv_nf4(FAKE, 0, ctypes.byref(st), FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemv_nf4(FAKE, 17, ctypes.byref(st), FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemm_nf4(FAKE, 0, ctypes.byref(st), None, None, 0, 0.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, None, 16, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 65, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 16, float("inf"), FAKE, None) \
+        == qk.QK_ERR_INVALID_ARG
+
+
+def test_missing_library_error_is_deferred(tmp_path, monkeypatch):
+    """A missing .so does not break import; the first call raises QKError."""
+    monkeypatch.setattr(qk, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(qk, "_lib", None)
+    monkeypatch.setattr(qk, "_load_error", None)
+    with pytest.raises(qk.QKError) as ei:
+        qk.qk_make_codebook(qk.NF4)
+    assert "not built" in str(ei.value)
