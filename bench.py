@@ -1,0 +1,432 @@
+"""Benchmark of the blockwise 4-bit weight hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+One step = every stage of the path over one Llama-7B-shaped layer set (q, k,
+v, o [4096, 4096]; gate, up [11008, 4096]; down [4096, 11008]; bf16 weights
+~ N(0, 0.02), synthetic):
+  for each of the 7 weights:
+    qk_quantize_blockwise (NF4, block 64) + qk_double_quant   (steps a2-a5)
+    qk_dequantize to bf16                                     (a6)
+    qk_gemv_nf4 at M = 1 and M = 16                           (a7)
+    qk_gemm_nf4 at M = 4096 tokens with LoRA r = 16, alpha/r = 2   (a8)
+Inputs are resident in HBM before timing starts.
+
+Output: one JSON line.  `value` is the step's time at the MI355X roofline
+(sum over launches of max(algorithmic bytes / 8 TB/s, flops / 2.5 PFLOP/s))
+divided by the measured step time, in percent.  `breakdown` gives each
+stage's absolute rate; `roofline` the dominant kernel (the GEMM) measured with
+HIP events on the stream the kernels run on; `cpu_baseline` the CPU oracle on
+a bounded sample of the same work.
+
+Other modes:
+  --copy-calibration          run a plain 1 GiB device copy (for HBM counter scaling)
+  --summarize-pmc DIR KERNEL  summarize rocprofv3 --pmc output of FETCH_SIZE / WRITE_SIZE
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_BPS = 8.0e12          # MI355X HBM3E
+MFMA_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA
+METRIC = "NF4 GEMV/quantize HBM GB/s and fused GEMM TFLOP/s, as % of MI355X roofline"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ----------------------------------------------------------------- algorithmic work
+
+def nblk(n, b):
+    return (n + b - 1) // b
+
+
+def bytes_quantize(n, B=64):
+    # read bf16 x, write codes and fp32 absmax
+    return 2 * n + (n + 1) // 2 + 4 * nblk(n, B)
+
+
+def bytes_double_quant(nb):
+    # read fp32 absmax, write int8 q, fp32 scale per 256, fp32 mean
+    return 4 * nb + nb + 4 * nblk(nb, 256) + 4
+
+
+def bytes_state(n, B=64):
+    nb = nblk(n, B)
+    return (n + 1) // 2 + nb + 4 * nblk(nb, 256) + 4
+
+
+def bytes_dequantize(n, B=64):
+    return bytes_state(n, B) + 2 * n
+
+
+def bytes_gemv(M, N, K, B=64):
+    return bytes_state(N * K, B) + 2 * M * K + 2 * M * N
+
+
+def flops_gemm(M, N, K, r):
+    return 2 * M * N * K + 2 * M * K * r + 2 * M * r * N
+
+
+def bytes_gemm(M, N, K, r, B=64):
+    return 2 * M * K + bytes_state(N * K, B) + 2 * K * r + 2 * r * N + 2 * M * N
+
+
+def roofline_s(nbytes, flops=0.0):
+    return max(nbytes / HBM_BPS, flops / MFMA_BF16_FLOPS)
+
+
+def source_sha(name):
+    p = os.path.join(ROOT, "bit_blockwise_weight_amd", "csrc", name)
+    with open(p, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+# ----------------------------------------------------------------- GPU benchmark
+
+def build_workload(torch, qk, workloads):
+    dev = torch.device("cuda:0")
+    M_TOK, R = 4096, 16
+    mats = []
+    lv = qk.qk_make_codebook(qk.NF4)
+    for i, (name, N, K) in enumerate(workloads.LLAMA7B_SHAPES):
+        wbits = workloads.llama7b_weight(i)
+        w = torch.from_numpy(wbits.view("int16")).view(torch.bfloat16).to(dev).reshape(N, K)
+        n = N * K
+        nb = nblk(n, 64)
+        m = {
+            "name": name, "N": N, "K": K, "w": w,
+            "codes": torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev),
+            "absmax": torch.empty(nb, dtype=torch.float32, device=dev),
+            "q8": torch.empty(nb, dtype=torch.int8, device=dev),
+            "scale": torch.empty(nblk(nb, 256), dtype=torch.float32, device=dev),
+            "mean": torch.empty(1, dtype=torch.float32, device=dev),
+            "ws": torch.empty(max(8, qk.qk_double_quant_workspace_size(nb)), dtype=torch.uint8, device=dev),
+            "deq": torch.empty(n, dtype=torch.bfloat16, device=dev),
+            "y1": torch.empty((1, N), dtype=torch.bfloat16, device=dev),
+            "y16": torch.empty((16, N), dtype=torch.bfloat16, device=dev),
+            "Y": torch.empty((M_TOK, N), dtype=torch.bfloat16, device=dev),
+        }
+        m["state"] = qk.qk_state_init(qk.NF4, lv, N, K, 64, m["codes"], None, m["q8"], m["scale"], m["mean"])
+        mats.append(m)
+    acts = {}
+    for K in sorted(set(m["K"] for m in mats)):
+        acts[K] = {
+            "x1": torch.from_numpy(workloads.activations("llama7b_layer", 1, K, tag=100 + K).view("int16"))
+            .view(torch.bfloat16).to(dev),
+            "x16": torch.from_numpy(workloads.activations("llama7b_layer", 16, K, tag=200 + K).view("int16"))
+            .view(torch.bfloat16).to(dev),
+            "X": torch.from_numpy(workloads.activations("qlora_prefill", M_TOK, K, tag=K).view("int16"))
+            .view(torch.bfloat16).to(dev),
+        }
+    lora = {}
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    for m in mats:
+        A = (torch.randn((m["K"], R), generator=g) * 0.01).to(torch.bfloat16).to(dev)
+        Bm = (torch.randn((R, m["N"]), generator=g) * 0.01).to(torch.bfloat16).to(dev)
+        lora[m["name"]] = (A, Bm)
+    gemm_ws = torch.empty(max(16, qk.qk_gemm_nf4_workspace_size(M_TOK, R)), dtype=torch.uint8, device=dev)
+    return {"mats": mats, "acts": acts, "lora": lora, "M": M_TOK, "r": R, "levels": lv, "gemm_ws": gemm_ws}
+
+
+OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lora"]
+
+
+def run_step(torch, qk, wl, events=None):
+    """One pass of the hot path over the layer set.  With `events`, every launch
+    is bracketed by HIP events recorded on the current stream."""
+    lv = wl["levels"]
+    M, r = wl["M"], wl["r"]
+    for m in wl["mats"]:
+        a = wl["acts"][m["K"]]
+        A, Bm = wl["lora"][m["name"]]
+        calls = [
+            ("quantize", lambda: qk.qk_quantize_blockwise(m["w"], 64, lv, m["codes"], m["absmax"])),
+            ("double_quant", lambda: qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])),
+            ("dequantize", lambda: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])),
+            ("gemv_m1", lambda: qk.qk_gemv_nf4(a["x1"], m["state"], m["y1"])),
+            ("gemv_m16", lambda: qk.qk_gemv_nf4(a["x16"], m["state"], m["y16"])),
+            ("gemm_lora", lambda: qk.qk_gemm_nf4(a["X"], m["state"], A, Bm, 2.0, m["Y"], wl["gemm_ws"])),
+        ]
+        for op, fn in calls:
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                events.append((op, m, e0, e1))
+            else:
+                fn()
+
+
+def work_of(op, m, wl):
+    N, K = m["N"], m["K"]
+    n = N * K
+    if op == "quantize":
+        return bytes_quantize(n), 0
+    if op == "double_quant":
+        return bytes_double_quant(nblk(n, 64)), 0
+    if op == "dequantize":
+        return bytes_dequantize(n), 0
+    if op == "gemv_m1":
+        return bytes_gemv(1, N, K), 2 * N * K
+    if op == "gemv_m16":
+        return bytes_gemv(16, N, K), 2 * 16 * N * K
+    if op == "gemm_lora":
+        return bytes_gemm(wl["M"], N, K, wl["r"]), flops_gemm(wl["M"], N, K, wl["r"])
+    raise KeyError(op)
+
+
+def gemv_isolated(torch, qk, workloads, reps=6, iters=20):
+    """GEMV M=1 over `reps` copies of the layer set (607 MB of NF4 state at 6),
+    cycled so the 256 MB last-level cache cannot hold them; HBM rate."""
+    dev = torch.device("cuda:0")
+    lv = qk.qk_make_codebook(qk.NF4)
+    states, xs, ys = [], {}, []
+    total_bytes = 0
+    for rep in range(reps):
+        for i, (name, N, K) in enumerate(workloads.LLAMA7B_SHAPES):
+            w = torch.randn((N, K), device=dev, dtype=torch.float32).mul_(0.02).to(torch.bfloat16)
+            qw = qk.quantize(w, 64, qk.NF4, True)
+            del w
+            states.append((qw, K, N))
+            ys.append(torch.empty((1, N), dtype=torch.bfloat16, device=dev))
+            total_bytes += bytes_gemv(1, N, K)
+    for K in (4096, 11008):
+        xs[K] = torch.randn((1, K), device=dev).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    for (qw, K, N), y in zip(states, ys):
+        qk.qk_gemv_nf4(xs[K], qw.state, y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        for (qw, K, N), y in zip(states, ys):
+            qk.qk_gemv_nf4(xs[K], qw.state, y)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3
+    launches = iters * len(states)
+    return {"gb_per_s": total_bytes * iters / sec / 1e9, "us_per_layer": sec / (iters * reps) * 1e6,
+            "launches": launches, "working_set_mb": round(total_bytes / 1e6, 1)}
+
+
+def cpu_baseline(workloads):
+    """The CPU oracle, as it stands, on a bounded sample of the step's work:
+    quantize + double-quant + dequantize of the 4096 x 4096 q weight, the fp64
+    GEMV at M = 1 and M = 16 on it, and the fp64 GEMM + LoRA for 256 of the 4096
+    token rows.  Reported in the same unit as `value`."""
+    import numpy as np
+    from oracle import blockwise as obw, codebook as ocb, dequant as odq, double_quant as odd, matmul as omm
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    N, K = 4096, 4096
+    wbits = workloads.llama7b_weight(0)
+    wf = (wbits.astype(np.uint32) << 16).view(np.float32).reshape(-1)
+    lv = ocb.nf4_levels()
+    t0 = time.perf_counter()
+    packed, amax = obw.quantize_blockwise(wf, 64, lv)
+    q, sig, mu = odd.double_quant(amax)
+    t1 = time.perf_counter()
+    yb = odq.dequantize_bf16_bits(packed, wf.size, 64, lv, odd.reconstruct_absmax(q, sig, mu))
+    wd = ((yb.astype(np.uint32) << 16).view(np.float32)).reshape(N, K)
+    t2 = time.perf_counter()
+    x16 = workloads.activations("llama7b_layer", 16, K, tag=200 + K)
+    xf = (x16.astype(np.uint32) << 16).view(np.float32).reshape(16, K)
+    omm.qlora_forward_f64(xf[:1], wd)
+    omm.qlora_forward_f64(xf, wd)
+    t3 = time.perf_counter()
+    rows = 256
+    X = workloads.activations("qlora_prefill", rows, K, tag=9)
+    Xf = (X.astype(np.uint32) << 16).view(np.float32).reshape(rows, K)
+    g = np.random.default_rng(1)
+    A = g.standard_normal((K, 16)) * 0.01
+    Bm = g.standard_normal((16, N)) * 0.01
+    omm.qlora_forward_f64(Xf, wd, A, Bm, 2.0)
+    t4 = time.perf_counter()
+    n = N * K
+    roof = (roofline_s(bytes_quantize(n)) + roofline_s(bytes_double_quant(nblk(n, 64))) +
+            roofline_s(bytes_dequantize(n)) + roofline_s(bytes_gemv(1, N, K)) + roofline_s(bytes_gemv(16, N, K)) +
+            roofline_s(bytes_gemm(rows, N, K, 16), flops_gemm(rows, N, K, 16)))
+    total = t4 - t0
+    return {
+        "value": round(100.0 * roof / total, 6), "unit": "% of MI355X roofline", "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"q weight 4096x4096: oracle quantize+double-quant {t1 - t0:.2f} s and dequantize {t2 - t1:.2f} s "
+                   f"on 1 core, fp64 GEMV M=1,16 {t3 - t2:.2f} s and fp64 GEMM+LoRA on 256 of 4096 rows "
+                   f"{t4 - t3:.2f} s on {blas_threads} BLAS threads; total {total:.2f} s"),
+        "oracle_quantize_melem_per_s": round(n / (t1 - t0) / 1e6, 2),
+        "oracle_gemm_gflop_per_s": round(flops_gemm(rows, N, K, 16) / (t4 - t3) / 1e9, 2),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def load_traffic(kernel_key):
+    p = os.path.join(PROFILES, f"traffic_{kernel_key}.json")
+    if not os.path.exists(p):
+        return None, None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("source_sha") != source_sha(t.get("source", "gemm.hip")):
+        return None, t
+    return t.get("bytes_per_dispatch"), t
+
+
+def bench(args):
+    import torch
+    import bit_blockwise_weight_amd as qk
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 2
+    qk.lib()   # the HIP library must load; no fallback exists
+    wl = build_workload(torch, qk, workloads)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        run_step(torch, qk, wl)
+    torch.cuda.synchronize()
+
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(torch, qk, wl, events)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+
+    per_op = {op: {"s": 0.0, "bytes": 0, "flops": 0, "roof_s": 0.0, "launches": 0} for op in OPS}
+    roof_total = 0.0
+    for op, m, e0, e1 in events:
+        d = e0.elapsed_time(e1) / 1e3
+        b, f = work_of(op, m, wl)
+        rs = roofline_s(b, f if op == "gemm_lora" else 0.0)
+        po = per_op[op]
+        po["s"] += d
+        po["bytes"] += b
+        po["flops"] += f
+        po["roof_s"] += rs
+        po["launches"] += 1
+        roof_total += rs
+    roof_per_step = roof_total / args.steps
+    value = 100.0 * roof_per_step / step_s
+
+    breakdown = {}
+    for op, po in per_op.items():
+        ent = {"us_per_launch": round(po["s"] / po["launches"] * 1e6, 2), "launches_per_step": po["launches"] // args.steps,
+               "frac_of_roofline": round(po["roof_s"] / po["s"], 4)}
+        if op == "gemm_lora":
+            ent["tflop_per_s"] = round(po["flops"] / po["s"] / 1e12, 1)
+        else:
+            ent["gb_per_s"] = round(po["bytes"] / po["s"] / 1e9, 1)
+        breakdown[op] = ent
+
+    g = per_op["gemm_lora"]
+    achieved = g["flops"] / g["s"] / 1e12
+    traffic, tinfo = load_traffic("gemm")
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+            "frac": round(achieved * 1e12 / MFMA_BF16_FLOPS, 4), "traffic": traffic,
+            "kernel": "qk gemm_kernel (fused dequant + LoRA)", "us_per_launch": round(g["s"] / g["launches"] * 1e6, 2),
+            "flops_per_launch": g["flops"] // g["launches"]}
+
+    extra = {}
+    if not args.skip_isolated:
+        extra["gemv_m1_isolated_607MB"] = gemv_isolated(torch, qk, workloads)
+
+    cpu = None
+    if not args.skip_cpu:
+        cpu = cpu_baseline(workloads)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "% of MI355X roofline", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16/nf4",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) activations)",
+        "config": {"workload": "llama7b-layer-set: q,k,v,o [4096,4096], gate,up [11008,4096], down [4096,11008]; "
+                               "NF4 block 64 + double quant; GEMV M=1,16; GEMM M=4096 + LoRA r=16",
+                   "global_batch": wl["M"], "seq_len": 1024, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown, "extra": extra,
+        "roofline_ms_per_step": round(roof_per_step * 1e3, 3), "backend": qk.qk_backend_info(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "iters": 3}), flush=True)
+    return 0
+
+
+def summarize_pmc(directory, kernel_substr, out_path, source="gemm.hip"):
+    """Reads rocprofv3 --pmc counter CSVs (FETCH_SIZE pass and WRITE_SIZE pass,
+    plus a copy-calibration pass) and writes the per-dispatch HBM traffic of the
+    kernel whose name contains `kernel_substr`, scaled by the copy kernel."""
+    import csv
+
+    def rows_of(pattern):
+        out = []
+        for p in glob.glob(os.path.join(directory, "**", pattern), recursive=True):
+            with open(p) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    recs = rows_of("*counter_collection.csv")
+    vals = {}
+    for r in recs:
+        name = r.get("Kernel_Name", "")
+        cn = r.get("Counter_Name", "")
+        try:
+            v = float(r.get("Counter_Value", "nan"))
+        except ValueError:
+            continue
+        key = "copy" if ("copy" in name.lower() or "elementwise" in name.lower()) else (
+            "target" if kernel_substr in name else None)
+        if key is None:
+            continue
+        vals.setdefault((key, cn), []).append(v)
+    summary = {k[0] + ":" + k[1]: sum(v) / len(v) for k, v in vals.items()}
+    print(json.dumps(summary, indent=1))
+    return summary
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--skip-isolated", action="store_true", help="skip the isolated GEMV HBM measurement")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the hot path here runs on a single "
+              "device and this build has no multi-GPU path", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        return copy_calibration()
+    return bench(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

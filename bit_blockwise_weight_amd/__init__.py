@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "QKError", "QuantState", "QuantizedWeight", "NF4", "FP4", "CUSTOM", "lib",
     "qk_make_codebook", "qk_quantize_blockwise", "qk_double_quant_workspace_size", "qk_double_quant",
-    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemm_nf4", "qk_last_error", "qk_version",
+    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_last_error", "qk_version",
     "qk_backend_info", "quantize",
 ]
 
@@ -97,7 +97,8 @@ def lib():
         "qk_state_init": [st_p, i32, ctypes.POINTER(ctypes.c_float), i64, i64, i32, vp, vp, vp, vp, vp],
         "qk_dequantize": [st_p, vp, i32, vp],
         "qk_gemv_nf4": [vp, i32, st_p, vp, vp],
-        "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp],
+        "qk_gemm_nf4_workspace_size": [i64, i32, ctypes.POINTER(ctypes.c_size_t)],
+        "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp, ctypes.c_size_t, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -241,17 +242,28 @@ def qk_gemv_nf4(x: torch.Tensor, state: QuantState, y=None) -> torch.Tensor:
     return y
 
 
-def qk_gemm_nf4(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: float = 0.0, Y=None) -> torch.Tensor:
+def qk_gemm_nf4_workspace_size(M: int, r: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().qk_gemm_nf4_workspace_size(int(M), int(r), ctypes.byref(out)))
+    return int(out.value)
+
+
+def qk_gemm_nf4(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: float = 0.0, Y=None,
+                workspace=None) -> torch.Tensor:
     _require_cuda(X, A, B)
     X2 = X.reshape(-1, state.cols)
     M = X2.shape[0]
     r = 0 if A is None else A.shape[1]
     if Y is None:
         Y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=X.device)
-    _require_cuda(Y)
+    wsb = qk_gemm_nf4_workspace_size(M, r)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=X.device)
+    _require_cuda(Y, workspace)
     with torch.cuda.device(X.device):
         _check(lib().qk_gemm_nf4(_ptr(X2), M, ctypes.byref(state), _ptr(A), _ptr(B), int(r), float(lora_scale),
-                                 _ptr(Y), ctypes.c_void_p(_stream(X))))
+                                 _ptr(Y), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                 ctypes.c_void_p(_stream(X))))
     return Y
 
 
@@ -272,8 +284,8 @@ class QuantizedWeight:
     def gemv(self, x, y=None):
         return qk_gemv_nf4(x, self.state, y)
 
-    def gemm(self, X, A=None, B=None, lora_scale=0.0, Y=None):
-        return qk_gemm_nf4(X, self.state, A, B, lora_scale, Y)
+    def gemm(self, X, A=None, B=None, lora_scale=0.0, Y=None, workspace=None):
+        return qk_gemm_nf4(X, self.state, A, B, lora_scale, Y, workspace)
 
 
 def quantize(w: torch.Tensor, blocksize: int = 64, kind: int = NF4, double_quant: bool = True,

@@ -106,6 +106,7 @@ qk::DeqArgs deq_args(const qk_quant_state* st) {
     a.dq_mean = st->dq_mean;
     a.n = st->n;
     a.blocksize = st->blocksize;
+    a.blocksize_log2 = st->blocksize == 64 ? 6 : st->blocksize == 128 ? 7 : 8;
     a.nested = st->nested;
     std::memcpy(a.levels, st->levels, sizeof(a.levels));
     return a;
@@ -232,8 +233,15 @@ qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* 
                     "qk_gemv_nf4");
 }
 
+qk_status qk_gemm_nf4_workspace_size(int64_t M, int32_t r, size_t* bytes) {
+    if (!bytes) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4_workspace_size: bytes is NULL");
+    if (M < 1 || r < 0 || r > 64) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4_workspace_size: M >= 1, r in 0..64");
+    *bytes = qk::gemm_workspace_bytes(M, r);
+    return ok();
+}
+
 qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const void* A, const void* B, int32_t r,
-                      float lora_scale, void* Y, void* stream) {
+                      float lora_scale, void* Y, void* workspace, size_t workspace_bytes, void* stream) {
     const qk_status v = validate_state(st);
     if (v != QK_OK) return v;
     if (!X || !Y) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: NULL X or Y");
@@ -243,11 +251,16 @@ qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const 
     if (A && !std::isfinite(lora_scale)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: lora_scale is not finite");
     if (!aligned(X, 2) || !aligned(Y, 2) || (A && (!aligned(A, 2) || !aligned(B, 2))))
         return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: bf16 buffers must be 2-byte aligned");
+    const size_t need = qk::gemm_workspace_bytes(M, A ? r : 0);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(QK_ERR_WORKSPACE, "qk_gemm_nf4: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 16)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: workspace must be 16-byte aligned");
     const qk_status dev = ensure_device();
     if (dev != QK_OK) return dev;
     qk::MatArgs w{deq_args(st), st->rows, st->cols};
-    return launched(qk::launch_gemm(X, M, w, A, B, A ? r : 0, lora_scale, Y, reinterpret_cast<hipStream_t>(stream),
-                                    &g_gemm_variant),
+    return launched(qk::launch_gemm(X, M, w, A, B, A ? r : 0, lora_scale, Y, workspace,
+                                    reinterpret_cast<hipStream_t>(stream), &g_gemm_variant),
                     "qk_gemm_nf4");
 }
 

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DeqArgs a, void* _
                     for (int j = 0; j < 4; ++j)
                         if (base / 2 + j < nbytes) w[k] |= (uint32_t)a.codes[base / 2 + j] << (8 * j);
                 }
-                sc[k] = block_scale(a, base / a.blocksize);
+                sc[k] = block_scale(a, base >> a.blocksize_log2);
             }
         }
 #pragma unroll

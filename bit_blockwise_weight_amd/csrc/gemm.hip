@@ -64,7 +64,7 @@ __device__ __forceinline__ uint32_t deq_pair(const float* lev, uint32_t byte, fl
 }
 
 template <bool kGeneric, bool kLora>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
     __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN * kLdsStride];
     __shared__ float lev[16];
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
             const int64_t e0 = wn_row * K + k0 + whalf * 32;
             if (wrow_ok) {
                 cr = *reinterpret_cast<const uint4*>(a.w.codes + e0 / 2);
-                csc = wscale(a.w, e0 / a.w.blocksize);
+                csc = wscale(a.w, e0 >> a.w.blocksize_log2);
             } else {
                 cr = make_uint4(0, 0, 0, 0);
                 csc = 0.0f;
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
                     const int64_t e = wn_row * K + k;
                     const uint32_t byte = a.w.codes[e >> 1];
                     code = (e & 1) ? (byte & 0xFu) : (byte >> 4);
-                    sc = wscale(a.w, e / a.w.blocksize);
+                    sc = wscale(a.w, e >> a.w.blocksize_log2);
                 }
                 cg[i >> 1] |= code << ((i & 1) ? 0 : 4);
                 scg[i] = sc;
@@ -340,16 +340,478 @@ template <bool kGeneric>
 hipError_t launch_typed(const GemmArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
     if (a.A)
-        hipLaunchKernelGGL((gemm_kernel<kGeneric, true>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((gemm_tile128_kernel<kGeneric, true>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<kGeneric, false>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((gemm_tile128_kernel<kGeneric, false>), grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fast path: 256 x 256 output tile, K step 64, 4 waves.  Wave w owns weight
+// rows [64w, 64w + 64) of the tile (two 32-column MFMA tiles) and all 256 token
+// rows (eight 32-row MFMA tiles), so each weight of the tile is dequantized by
+// exactly one lane of one wave, straight into MFMA B-fragment registers:
+//   lane l = (j = l % 32, g = l / 32) holds the 16 code bytes of weights
+//   [64s + 32g, 64s + 32g + 32) of its row (one absmax block); a byte is looked
+//   up in an LDS table of fp32 level pairs (32 interleaved copies, address built
+//   by one v_perm), multiplied by the block's a' and rounded to bf16 — the same
+//   bf16(RN(level * a')) that qk_dequantize writes.  Quarter q of the step (8
+//   weights) is the B operand of the q-th 16-deep MFMA; the A operand is
+//   X[row][64s + 32g + 8q .. +8] from LDS, the same k order.
+// Pipeline (one barrier per step):
+//   * at the start of step s the X tile of step s + 1 is loaded straight into the
+//     other LDS buffer (global_load_lds_dwordx4, no staging registers) and the
+//     codes of step s + 2 into registers;
+//   * the B fragments of the next quarter are dequantized while the 16 MFMAs of
+//     the current quarter run.
+// X rows are 128 bytes in LDS with the 16-byte chunks XOR-swizzled by the row
+// (chunk c of row r sits in slot c ^ (r & 7)), so the fragment reads of 8
+// consecutive rows hit 8 different bank groups.
+// ---------------------------------------------------------------------------
+namespace v4 {
+
+constexpr int TM = 256;
+constexpr int TN = 256;
+constexpr int TK = 64;
+constexpr int kCopies = 32;
+constexpr int kSplits = 8;                // K splits of the LoRA X*A pre-pass
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ uint32_t xoff(int row, int chunk) {   // byte offset in an X tile
+    return (uint32_t)(row * 8 + (chunk ^ (row & 7))) * 16u;
+}
+
+template <int R16, bool kNested>
+__global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const float* __restrict__ T) {
+    constexpr int kRp = 16 * R16;
+    constexpr int kTs = kRp + 8;                       // LoRA T rows in LDS (bf16 elements)
+    // r <= 16: s X A is staged as bf16 hi/lo next to the K-loop buffers in the prologue;
+    // larger ranks stage it in the K-loop buffers after the loop
+    constexpr bool kTEarly = R16 == 1;
+    constexpr int kXBytes = 2 * TM * 128;              // two X tiles
+    constexpr int kTabBytes = 256 * kCopies * 8;       // fp32 level-pair table
+    constexpr int kTBytes = kTEarly ? 2 * TM * kTs * 2 : 0;
+    __shared__ __attribute__((aligned(1024))) uint4 lds[(kXBytes + kTabBytes + kTBytes) / 16];
+    char* ldsb = reinterpret_cast<char*>(lds);
+    uint4* xs0 = lds;                                               // X tile buffer 0
+    uint4* xs1 = lds + TM * 8;                                      // X tile buffer 1
+    uint2* tab = reinterpret_cast<uint2*>(ldsb + kXBytes);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane & 31;
+    const int g = lane >> 5;
+    const int64_t m0 = (int64_t)blockIdx.y * TM;
+    const int64_t n0 = (int64_t)blockIdx.x * TN;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t nk = K / TK, nk1 = nk - 1;
+    const int r = a.r;
+
+    for (int i = tid; i < 256 * kCopies; i += 256) {
+        const int b = i / kCopies;
+        tab[i] = make_uint2(as_uint(a.w.levels[b >> 4]), as_uint(a.w.levels[b & 15]));
+    }
+
+    int64_t wrow[2], wrow_c[2];
+    bool wok[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        wrow[ct] = n0 + 64 * wave + 32 * ct + j;
+        wok[ct] = wrow[ct] < N;
+        wrow_c[ct] = wok[ct] ? wrow[ct] : N - 1;
+    }
+    const uint32_t lane_sel = (uint32_t)(lane & (kCopies - 1)) * 8u;
+    const char* tabb = reinterpret_cast<const char*>(tab);
+    const float mean = kNested ? *a.w.dq_mean : 0.0f;
+
+    // LoRA operands read in the prologue (r <= 16): B fragments and s X A as bf16 hi/lo in LDS
+    uint16_t* thi = reinterpret_cast<uint16_t*>(ldsb + (kTEarly ? kXBytes + kTabBytes : 0));
+    uint16_t* tlo = thi + TM * kTs;
+    auto load_lora_b = [&](int kk, bf16x8_t (&bl)[2]) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            // unconditional loads (clamped indices); ranks >= r are zeroed afterwards
+            uint32_t e[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int jj = kk + 8 * g + t;
+                e[t] = (uint32_t)a.B[(int64_t)(jj < r ? jj : r - 1) * N + wrow_c[ct]];
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) e[t] = (kk + 8 * g + t < r) ? e[t] : 0u;
+            bl[ct] = __builtin_bit_cast(bf16x8_t, make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16),
+                                                             e[4] | (e[5] << 16), e[6] | (e[7] << 16)));
+        }
+    };
+    auto stage_t = [&]() {
+        // thread t: row t of the tile; s X A already summed over the K splits
+        const int64_t gm = m0 + tid < M ? m0 + tid : M - 1;
+#pragma unroll
+        for (int c4 = 0; c4 < kRp / 4; ++c4) {
+            const float4 sum = *reinterpret_cast<const float4*>(T + gm * kRp + 4 * c4);
+            const uint32_t h01 = pack_bf16x2(sum.x, sum.y), h23 = pack_bf16x2(sum.z, sum.w);
+            const uint32_t l01 = pack_bf16x2(sum.x - as_float(h01 << 16), sum.y - as_float(h01 & 0xFFFF0000u));
+            const uint32_t l23 = pack_bf16x2(sum.z - as_float(h23 << 16), sum.w - as_float(h23 & 0xFFFF0000u));
+            *reinterpret_cast<uint2*>(&thi[tid * kTs + 4 * c4]) = make_uint2(h01, h23);
+            *reinterpret_cast<uint2*>(&tlo[tid * kTs + 4 * c4]) = make_uint2(l01, l23);
+        }
+    };
+    bf16x8_t bl_early[2];
+    if constexpr (kTEarly) {
+        load_lora_b(0, bl_early);
+        stage_t();
+    }
+
+    // X tile rows loaded by this lane (clamped to the last valid row: rows past M
+    // only feed output rows that are never stored)
+    const uint16_t* xsrc[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const int p = (v * 4 + wave) * 64 + lane;          // LDS 16-byte slot written by this lane
+        const int row = p >> 3, slot = p & 7;
+        const int chunk = slot ^ (row & 7);
+        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
+        xsrc[v] = a.X + gm * K + chunk * 8;
+    }
+    auto load_x = [&](int64_t s, int buf) {
+        const int64_t k0 = (s < nk1 ? s : nk1) * TK;
+        char* base = reinterpret_cast<char*>(buf ? xs1 : xs0);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            lptr_t dst = (lptr_t)((__attribute__((address_space(3))) char*)base + (v * 4 + wave) * 1024);
+            __builtin_amdgcn_global_load_lds((gptr_t)(xsrc[v] + k0), dst, 16, 0, 0);
+        }
+    };
+
+    // codes + raw scale words of a step (c[ct] = 16 bytes; q = q8 or absmax bits; d = dq scale)
+    struct Codes {
+        uint4 c[2];
+        int32_t q[2];
+        float d[2];
+    };
+    auto load_codes = [&](int64_t s, Codes& cs) {
+        const int64_t k0 = (s < nk1 ? s : nk1) * TK;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int64_t e0 = wrow_c[ct] * K + k0 + 32 * g;
+            const int64_t blk = e0 >> a.w.blocksize_log2;
+            cs.c[ct] = *reinterpret_cast<const uint4*>(a.w.codes + e0 / 2);
+            if constexpr (kNested) {
+                cs.q[ct] = (int32_t)a.w.q8[blk];
+                cs.d[ct] = a.w.dq_scale[blk / QK_DQ_BLOCK];
+            } else {
+                cs.q[ct] = (int32_t)as_uint(a.w.absmax[blk]);
+                cs.d[ct] = 1.0f;
+            }
+        }
+    };
+    auto scale_of = [&](const Codes& cs, int ct) {
+        float sc;
+        if constexpr (kNested) sc = __fadd_rn(__fmul_rn((float)cs.q[ct], cs.d[ct]), mean);
+        else sc = as_float((uint32_t)cs.q[ct]);
+        return sc;
+    };
+    // B fragments of quarter q of a step: for each column tile, dword q of its codes
+    auto dequant_q = [&](const Codes& cs, int q, bf16x8_t (&dst)[2]) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const float sc = scale_of(cs, ct);
+            const uint32_t cw = q == 0 ? cs.c[ct].x : q == 1 ? cs.c[ct].y : q == 2 ? cs.c[ct].z : cs.c[ct].w;
+            uint32_t d[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t addr = __builtin_amdgcn_perm(cw, lane_sel, 0x0C0C0400u | ((uint32_t)(4 + b) << 8));
+                const uint2 lv = *reinterpret_cast<const uint2*>(tabb + addr);
+                d[b] = pack_bf16x2(__fmul_rn(as_float(lv.x), sc), __fmul_rn(as_float(lv.y), sc));
+            }
+            dst[ct] = __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+        }
+    };
+
+    floatx16_t acc[8][2];
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[rt][ct][e] = 0.0f;
+
+    Codes c0, c1, c2;              // steps s, s + 1, s + 2
+    load_codes(0, c0);
+    load_codes(1, c1);
+    load_x(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();               // table and X(0) in LDS
+    bf16x8_t bq[2];
+    dequant_q(c0, 0, bq);
+    __syncthreads();
+
+    for (int64_t s = 0; s < nk; ++s) {
+        const int buf = (int)(s & 1);
+        // loads for later steps, issued first so they have the whole step
+        load_codes(s + 2, c2);
+        load_x(s + 1, buf ^ 1);
+        const char* xbb = reinterpret_cast<const char*>(buf ? xs1 : xs0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bf16x8_t bn[2];
+            if (q < 3) dequant_q(c0, q + 1, bn);
+            else dequant_q(c1, 0, bn);
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt) {
+                const int row = 32 * rt + j;
+                const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(xbb + xoff(row, 4 * g + q));
+                acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bq[0], acc[rt][0], 0, 0, 0);
+                acc[rt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bq[1], acc[rt][1], 0, 0, 0);
+            }
+            bq[0] = bn[0];
+            bq[1] = bn[1];
+        }
+        c0 = c1;
+        c1 = c2;
+        __builtin_amdgcn_s_waitcnt(0);     // X(s + 1) has landed in LDS
+        __syncthreads();
+    }
+
+    if constexpr (R16 > 0) {
+        // LoRA: acc += (s X A) B, s X A as bf16 hi + lo (about 16 significant bits together)
+        if constexpr (!kTEarly) {
+            thi = reinterpret_cast<uint16_t*>(ldsb);    // the K-loop buffers are free now
+            tlo = thi + TM * kTs;
+            stage_t();
+            __syncthreads();
+        }
+#pragma unroll
+        for (int kk = 0; kk < kRp; kk += 16) {
+            bf16x8_t bl[2];
+            if constexpr (kTEarly) {
+                bl[0] = bl_early[0];
+                bl[1] = bl_early[1];
+            } else {
+                load_lora_b(kk, bl);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt) {
+                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&thi[(32 * rt + j) * kTs + kk + 8 * g]);
+                const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&tlo[(32 * rt + j) * kTs + kk + 8 * g]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[ct], acc[rt][ct], 0, 0, 0);
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bl[ct], acc[rt][ct], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // epilogue: stage the bf16 tile in LDS (256 rows x 512 bytes = the K-loop buffers and the
+    // table), then write Y with 16-byte row-contiguous stores.  Register e of MFMA tile (rt, ct)
+    // holds C[32 rt + 8(e/4) + 4g + e%4][64 wave + 32 ct + j].
+    uint16_t* cs = reinterpret_cast<uint16_t*>(ldsb);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int col = 64 * wave + 32 * ct + j;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * rt + 8 * (e / 4) + 4 * g + (e % 4);
+                cs[row * TN + col] = (uint16_t)(pack_bf16x2(acc[rt][ct][e], 0.0f) & 0xFFFFu);
+            }
+        }
+    }
+    __syncthreads();
+    const bool vec_ok = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
+    for (int c = tid; c < TM * (TN / 8); c += 256) {
+        const int row = c / (TN / 8), ch = c % (TN / 8);
+        const int64_t gm = m0 + row, gn = n0 + 8 * ch;
+        if (gm >= M || gn >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(&cs[row * TN + 8 * ch]);
+        uint16_t* dst = a.Y + gm * N + gn;
+        if (vec_ok && gn + 8 <= N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            for (int t = 0; t < 8 && gn + t < N; ++t) dst[t] = (uint16_t)(w4[t >> 1] >> ((t & 1) ? 16 : 0));
+        }
+    }
+}
+
+// Partial LoRA products, T_p[m][j] = s * sum_{k in split p} X[m][k] A[k][j], in
+// fp32, j < 16*R16 (columns >= r are 0).  Grid: (64-row groups, kSplits K
+// splits); a workgroup's 4 waves take 16 rows each and share the A tile of each
+// 64-deep step, transposed into LDS; the next step's X fragments are loaded
+// while the current step's MFMAs run.  lora_sum_kernel then adds the kSplits
+// partials in split order (deterministic).
+template <int R16>
+__global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restrict__ T) {
+    constexpr int kRp = 16 * R16;
+    constexpr int kS = TK + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t at[2][kRp * kS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int64_t M = a.M, K = a.K;
+    const int r = a.r;
+    const int64_t nk = K / TK;
+    const int split = blockIdx.y;
+    const int64_t s0 = nk * split / kSplits, s1 = nk * (split + 1) / kSplits;
+    const int64_t mrow = (int64_t)blockIdx.x * 64 + 16 * wave + l16;
+    const int64_t mrow_c = mrow < M ? mrow : M - 1;
+    const uint16_t* xrow = a.X + mrow_c * K + 8 * q4;
+    const bool a_vec = (r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.A) % 16) == 0;
+    constexpr int cpr = kRp / 8;                       // 16-byte chunks per A row (padded)
+    constexpr int kAPer = (TK * cpr + 255) / 256;
+
+    floatx4_t acc[R16];
+#pragma unroll
+    for (int jt = 0; jt < R16; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[jt][e] = 0.0f;
+
+    uint4 ar[kAPer];
+    auto load_a = [&](int64_t s) {
+#pragma unroll
+        for (int v = 0; v < kAPer; ++v) {
+            const int c = tid + 256 * v;
+            const int row = (c / cpr) < TK ? (c / cpr) : TK - 1, cc = c % cpr;
+            const uint16_t* src = a.A + (s * TK + row) * r;
+            if (a_vec) {
+                ar[v] = *reinterpret_cast<const uint4*>(src + (cc * 8 < r ? cc * 8 : r - 8));
+            } else {
+                uint32_t e[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) e[t] = (uint32_t)src[cc * 8 + t < r ? cc * 8 + t : r - 1];
+                ar[v] = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+            }
+        }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int v = 0; v < kAPer; ++v) {
+            const int c = tid + 256 * v;
+            const int row = c / cpr, cc = c % cpr;
+            if (row < TK) {
+                const uint32_t w4[4] = {ar[v].x, ar[v].y, ar[v].z, ar[v].w};
+                const int shift = (a_vec && cc * 8 + 8 > r) ? (cc * 8 - (r - 8)) : 0;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int st = t + shift;
+                    at[buf][(cc * 8 + t) * kS + row] =
+                        (cc * 8 + t < r && st < 8) ? (uint16_t)(w4[st >> 1] >> ((st & 1) ? 16 : 0)) : (uint16_t)0;
+                }
+            }
+        }
+    };
+
+    uint4 xv[2];
+    if (s0 < s1) {
+        load_a(s0);
+        xv[0] = *reinterpret_cast<const uint4*>(xrow + s0 * TK);
+        xv[1] = *reinterpret_cast<const uint4*>(xrow + s0 * TK + 32);
+        store_a(0);
+    }
+    __syncthreads();
+    for (int64_t s = s0; s < s1; ++s) {
+        const int buf = (int)((s - s0) & 1);
+        const bool more = s + 1 < s1;
+        uint4 xn[2];
+        if (more) {
+            load_a(s + 1);
+            xn[0] = *reinterpret_cast<const uint4*>(xrow + (s + 1) * TK);
+            xn[1] = *reinterpret_cast<const uint4*>(xrow + (s + 1) * TK + 32);
+        }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xv[kh]);
+#pragma unroll
+            for (int jt = 0; jt < R16; ++jt) {
+                const bf16x8_t ab = *reinterpret_cast<const bf16x8_t*>(&at[buf][(16 * jt + l16) * kS + 32 * kh + 8 * q4]);
+                acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ab, acc[jt], 0, 0, 0);
+            }
+        }
+        if (more) {
+            store_a(buf ^ 1);
+            xv[0] = xn[0];
+            xv[1] = xn[1];
+        }
+        __syncthreads();
+    }
+    // 16x16 output: lane holds C[4 q4 + e][l16]
+    float* Tp = T + (int64_t)split * M * kRp;
+#pragma unroll
+    for (int jt = 0; jt < R16; ++jt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t m = (int64_t)blockIdx.x * 64 + 16 * wave + 4 * q4 + e;
+            if (m < M) Tp[m * kRp + 16 * jt + l16] = acc[jt][e] * a.lora_scale;
+        }
+    }
+}
+
+// T[0] += T[1] + ... + T[kSplits - 1], element by element in split order.
+__global__ __launch_bounds__(256) void lora_sum_kernel(float4* __restrict__ T, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    float4 acc = T[i];
+#pragma unroll
+    for (int p = 1; p < kSplits; ++p) {
+        const float4 t = T[(int64_t)p * n4 + i];
+        acc.x += t.x; acc.y += t.y; acc.z += t.z; acc.w += t.w;
+    }
+    T[i] = acc;
+}
+
+}  // namespace v4
+
+template <bool kNested>
+void launch_fast_r(const GemmArgs& a, const float* T, hipStream_t s, dim3 grid, int r16) {
+    switch (r16) {
+        case 0: hipLaunchKernelGGL((v4::gemm_fast_kernel<0, kNested>), grid, dim3(256), 0, s, a, T); break;
+        case 1: hipLaunchKernelGGL((v4::gemm_fast_kernel<1, kNested>), grid, dim3(256), 0, s, a, T); break;
+        case 2: hipLaunchKernelGGL((v4::gemm_fast_kernel<2, kNested>), grid, dim3(256), 0, s, a, T); break;
+        case 3: hipLaunchKernelGGL((v4::gemm_fast_kernel<3, kNested>), grid, dim3(256), 0, s, a, T); break;
+        default: hipLaunchKernelGGL((v4::gemm_fast_kernel<4, kNested>), grid, dim3(256), 0, s, a, T); break;
+    }
+}
+
+void launch_lora_xa(const GemmArgs& a, float* T, hipStream_t s, int r16) {
+    const dim3 grid((unsigned)((a.M + 63) / 64), v4::kSplits);
+    switch (r16) {
+        case 1: hipLaunchKernelGGL((v4::lora_xa_kernel<1>), grid, dim3(256), 0, s, a, T); break;
+        case 2: hipLaunchKernelGGL((v4::lora_xa_kernel<2>), grid, dim3(256), 0, s, a, T); break;
+        case 3: hipLaunchKernelGGL((v4::lora_xa_kernel<3>), grid, dim3(256), 0, s, a, T); break;
+        default: hipLaunchKernelGGL((v4::lora_xa_kernel<4>), grid, dim3(256), 0, s, a, T); break;
+    }
+}
+
+hipError_t launch_fast(const GemmArgs& a, void* workspace, hipStream_t s) {
+    const dim3 grid((unsigned)((a.N + v4::TN - 1) / v4::TN), (unsigned)((a.M + v4::TM - 1) / v4::TM));
+    const int r16 = a.A ? (a.r + 15) / 16 : 0;
+    float* T = reinterpret_cast<float*>(workspace);
+    if (r16 > 0) {
+        launch_lora_xa(a, T, s, r16);
+        const int64_t n4 = a.M * 16 * r16 / 4;
+        hipLaunchKernelGGL(v4::lora_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                           reinterpret_cast<float4*>(T), n4);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.w.nested) launch_fast_r<true>(a, T, s, grid, r16);
+    else launch_fast_r<false>(a, T, s, grid, r16);
     return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gemm_workspace_bytes(int64_t M, int32_t r) {
+    return r > 0 ? (size_t)v4::kSplits * (size_t)M * (size_t)(((r + 15) / 16) * 16) * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B, int32_t r,
-                       float lora_scale, void* Y, hipStream_t s, const char** variant) {
+                       float lora_scale, void* Y, void* workspace, hipStream_t s, const char** variant) {
     GemmArgs a;
     a.X = reinterpret_cast<const uint16_t*>(X);
     a.A = reinterpret_cast<const uint16_t*>(A);
@@ -365,8 +827,8 @@ hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A
     const bool fast = (w.K % BK) == 0 && (w.K % w.w.blocksize) == 0 && (reinterpret_cast<uintptr_t>(X) % 16) == 0 &&
                       (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0;
     if (fast) {
-        *variant = "mfma 32x32x16 bf16, 128x128x64 tiles, W dequantized into LDS, LoRA in the K loop";
-        return launch_typed<false>(a, s);
+        *variant = "mfma 32x32x16 bf16, 256x256x64 tiles, W dequantized into B fragments, LoRA X*A pre-pass + epilogue";
+        return launch_fast(a, workspace, s);
     }
     *variant = "generic (element loads, flat-index dequantization), 128x128x64 tiles";
     return launch_typed<true>(a, s);

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(S * 64) void gemv_mfma_kernel(GemvArgs a) {
         for (int q = 0; q < 4; ++q) {
             xv[q] = x_ok ? *reinterpret_cast<const uint4*>(xrow + k0 + 8 * q) : make_uint4(0, 0, 0, 0);
         }
-        const float sc = row_ok ? row_scale(a.w, (row_elem0 + s * kStep) / a.w.blocksize) : 0.0f;
+        const float sc = row_ok ? row_scale(a.w, (row_elem0 + s * kStep) >> a.w.blocksize_log2) : 0.0f;
 
         floatx16_t part;
 #pragma unroll
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
         const int64_t e = n * K + k;
         const uint32_t byte = a.w.codes[e >> 1];
         const uint32_t code = (e & 1) ? (byte & 0xFu) : (byte >> 4);
-        const float wq = __fmul_rn(lev[code], row_scale(a.w, e / a.w.blocksize));
+        const float wq = __fmul_rn(lev[code], row_scale(a.w, e >> a.w.blocksize_log2));
         const float wd = as_float(pack_bf16x2(wq, 0.0f) << 16);   // bf16 dequantized weight
 #pragma unroll
         for (int m = 0; m < 16; ++m) {

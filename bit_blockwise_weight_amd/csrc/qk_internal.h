@@ -68,6 +68,7 @@ struct DeqArgs {
     const float* dq_mean;
     int64_t n;
     int32_t blocksize;
+    int32_t blocksize_log2;  // blocksize is a power of two: block of element e = e >> blocksize_log2
     int32_t nested;
     float levels[16];
 };
@@ -80,7 +81,9 @@ struct MatArgs {
 };
 hipError_t launch_gemv(const void* x, int32_t M, const MatArgs& w, void* y, hipStream_t s,
                        const char** variant);
+size_t gemm_workspace_bytes(int64_t M, int32_t r);
 hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B,
-                       int32_t r, float lora_scale, void* Y, hipStream_t s, const char** variant);
+                       int32_t r, float lora_scale, void* Y, void* workspace, hipStream_t s,
+                       const char** variant);
 
 }  // namespace qk

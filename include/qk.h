@@ -29,7 +29,8 @@
  *  - Memory: the caller owns every buffer.  Pointers documented "device" must
  *    point to device memory of the current HIP device; "host" pointers to
  *    ordinary host memory.  The library allocates no device memory and frees
- *    nothing; the one call that needs scratch space takes a caller workspace.
+ *    nothing; calls that need scratch space take a caller workspace whose size
+ *    a *_workspace_size query returns.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *    stream).  Every device call is asynchronous on that stream and never
  *    synchronizes.
@@ -222,13 +223,20 @@ qk_status qk_dequantize(const qk_quant_state* st, void* out, int32_t out_dtype, 
 qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* y, void* stream);
 
 /*
+ * qk_gemm_nf4_workspace_size — host.  Bytes of device workspace qk_gemm_nf4
+ * needs for M token rows and LoRA rank r (0 when r == 0: no workspace).
+ */
+qk_status qk_gemm_nf4_workspace_size(int64_t M, int32_t r, size_t* bytes);
+
+/*
  * qk_gemm_nf4 — device.  Prefill / training forward of a frozen 4-bit base
  * layer with an unmerged LoRA adapter ([DEQ] sections 2-2 and 8; [NF4] §2.2):
  *     Y = X · deq(W)^T + lora_scale · (X · A) · B
  *   The weight is dequantized tile by tile to bf16 exactly as qk_dequantize
- *   would write it, multiplied on bf16 matrix cores with fp32 accumulation;
- *   the rank-r LoRA product is accumulated in the same pass and added in the
- *   epilogue.  Agreement with the fp64 reference: rel. Frobenius <= 5e-3,
+ *   would write it and multiplied on bf16 matrix cores with fp32 accumulation.
+ *   The rank-r LoRA term: lora_scale · X · A is formed once per call (fp32, in
+ *   the workspace), and its product with B is added to the accumulators in the
+ *   GEMM epilogue.  Agreement with the fp64 reference: rel. Frobenius <= 5e-3,
  *   max error <= 2e-2 * max|ref|.
  *   X: device, [M, K] bf16 row-major, K = st->cols.
  *   M: >= 1.
@@ -237,10 +245,13 @@ qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* 
  *   r: LoRA rank, 1..64 when A and B are given (ignored otherwise).
  *   lora_scale: alpha / r.
  *   Y: device, [M, N] bf16 row-major, written.
- *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_HIP.
+ *   workspace: device, >= qk_gemm_nf4_workspace_size(M, r) bytes, 16-byte
+ *     aligned (may be NULL when A and B are NULL); contents on entry ignored.
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_WORKSPACE, QK_ERR_HIP.
  */
 qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const void* A,
-                      const void* B, int32_t r, float lora_scale, void* Y, void* stream);
+                      const void* B, int32_t r, float lora_scale, void* Y, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Message for the calling thread's last failed call ("" if none).  The
  * string stays valid until the thread's next qk_* call. */

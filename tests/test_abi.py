@@ -143,7 +143,7 @@ def test_corrupted_descriptor_is_rejected_by_every_consumer(L, field, value):
     y = FAKE
     assert L.qk_dequantize(ctypes.byref(st), y, qk.QK_BF16, None) == qk.QK_ERR_BAD_STATE
     assert L.qk_gemv_nf4(FAKE, 1, ctypes.byref(st), y, None) == qk.QK_ERR_BAD_STATE
-    assert L.qk_gemm_nf4(FAKE, 4, ctypes.byref(st), None, None, 0, 0.0, y, None) == qk.QK_ERR_BAD_STATE
+    assert L.qk_gemm_nf4(FAKE, 4, ctypes.byref(st), None, None, 0, 0.0, y, None, 0, None) == qk.QK_ERR_BAD_STATE
     assert "quant state" in qk.qk_last_error()
 
 
@@ -160,11 +160,23 @@ def test_consumer_argument_errors(L):
     assert L.qk_dequantize(None, FAKE, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
     assert L.qk_gemv_nf4(FAKE, 0, ctypes.byref(st), FAKE, None) == qk.QK_ERR_INVALID_ARG
     assert L.qk_gemv_nf4(FAKE, 17, ctypes.byref(st), FAKE, None) == qk.QK_ERR_INVALID_ARG
-    assert L.qk_gemm_nf4(FAKE, 0, ctypes.byref(st), None, None, 0, 0.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
-    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, None, 16, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
-    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 65, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
-    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 16, float("inf"), FAKE, None) \
+    assert L.qk_gemm_nf4(FAKE, 0, ctypes.byref(st), None, None, 0, 0.0, FAKE, None, 0, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, None, 16, 2.0, FAKE, FAKE, 1 << 20, None) \
         == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 65, 2.0, FAKE, FAKE, 1 << 20, None) \
+        == qk.QK_ERR_INVALID_ARG
+    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 16, float("inf"), FAKE, FAKE, 1 << 20, None) \
+        == qk.QK_ERR_INVALID_ARG
+    # LoRA needs a workspace of the queried size
+    need = qk.qk_gemm_nf4_workspace_size(8, 16)
+    assert need >= 8 * 16 * 4
+    assert qk.qk_gemm_nf4_workspace_size(8, 0) == 0
+    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 16, 2.0, FAKE, None, 0, None) == qk.QK_ERR_WORKSPACE
+    assert L.qk_gemm_nf4(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 16, 2.0, FAKE, FAKE, need - 1, None) \
+        == qk.QK_ERR_WORKSPACE
+    assert "workspace" in qk.qk_last_error()
+    out = ctypes.c_size_t()
+    assert L.qk_gemm_nf4_workspace_size(8, 65, ctypes.byref(out)) == qk.QK_ERR_INVALID_ARG
 
 
 def test_missing_library_error_is_deferred(tmp_path, monkeypatch):
