@@ -25,6 +25,7 @@ Other modes:
 """
 
 import argparse
+import ctypes
 import glob
 import hashlib
 import json
@@ -133,38 +134,46 @@ def build_workload(torch, qk, workloads):
         Bm = (torch.randn((R, m["N"]), generator=g) * 0.01).to(torch.bfloat16).to(dev)
         lora[m["name"]] = (A, Bm)
     gemm_ws = torch.empty(max(16, qk.qk_gemm_nf4_workspace_size(M_TOK, R)), dtype=torch.uint8, device=dev)
-    return {"mats": mats, "acts": acts, "lora": lora, "M": M_TOK, "r": R, "levels": lv, "gemm_ws": gemm_ws}
+    levels_c = (ctypes.c_float * 16)(*lv.tolist())
+    return {"mats": mats, "acts": acts, "lora": lora, "M": M_TOK, "r": R, "levels": lv, "levels_c": levels_c,
+            "gemm_ws": gemm_ws}
 
 
 OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lora"]
 
 
-def run_step(torch, qk, wl, events=None):
-    """One pass of the hot path over the layer set.  With `events`, every launch
-    is bracketed by HIP events recorded on the current stream."""
-    lv = wl["levels"]
-    M, r = wl["M"], wl["r"]
+def step_calls(torch, qk, wl):
+    """The launches of one pass of the hot path over the layer set, in order, as
+    (op, matrix, callable)."""
+    lv = wl["levels_c"]
+    calls = []
     for m in wl["mats"]:
         a = wl["acts"][m["K"]]
         A, Bm = wl["lora"][m["name"]]
-        calls = [
-            ("quantize", lambda: qk.qk_quantize_blockwise(m["w"], 64, lv, m["codes"], m["absmax"])),
-            ("double_quant", lambda: qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])),
-            ("dequantize", lambda: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])),
-            ("gemv_m1", lambda: qk.qk_gemv_nf4(a["x1"], m["state"], m["y1"])),
-            ("gemv_m16", lambda: qk.qk_gemv_nf4(a["x16"], m["state"], m["y16"])),
-            ("gemm_lora", lambda: qk.qk_gemm_nf4(a["X"], m["state"], A, Bm, 2.0, m["Y"], wl["gemm_ws"])),
+        calls += [
+            ("quantize", m, lambda m=m: qk.qk_quantize_blockwise(m["w"], 64, lv, m["codes"], m["absmax"])),
+            ("double_quant", m, lambda m=m: qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])),
+            ("dequantize", m, lambda m=m: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])),
+            ("gemv_m1", m, lambda m=m, a=a: qk.qk_gemv_nf4(a["x1"], m["state"], m["y1"])),
+            ("gemv_m16", m, lambda m=m, a=a: qk.qk_gemv_nf4(a["x16"], m["state"], m["y16"])),
+            ("gemm_lora", m, lambda m=m, a=a, A=A, Bm=Bm: qk.qk_gemm_nf4(a["X"], m["state"], A, Bm, 2.0, m["Y"],
+                                                                         wl["gemm_ws"])),
         ]
-        for op, fn in calls:
-            if events is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                events.append((op, m, e0, e1))
-            else:
-                fn()
+    return calls
+
+
+def run_step(calls, events=None):
+    """One pass of the hot path.  With `events` (len(calls) + 1 pre-created HIP
+    events), an event is recorded on the current stream before the first launch
+    and after every launch, so launch i took events[i] -> events[i + 1]."""
+    if events is None:
+        for _, _, fn in calls:
+            fn()
+        return
+    events[0].record()
+    for i, (_, _, fn) in enumerate(calls):
+        fn()
+        events[i + 1].record()
 
 
 def work_of(op, m, wl):
@@ -293,19 +302,27 @@ def bench(args):
         return 2
     qk.lib()   # the HIP library must load; no fallback exists
     wl = build_workload(torch, qk, workloads)
+    calls = step_calls(torch, qk, wl)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
-        run_step(torch, qk, wl)
-    torch.cuda.synchronize()
-
-    events = []
+        run_step(calls)
+    # events are created before timing: creating one can stall the host
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run_step(torch, qk, wl, events)
+    for k in range(args.steps):
+        run_step(calls, evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
+    events = [(op, m, ev[i], ev[i + 1]) for ev in evs for i, (op, m, _) in enumerate(calls)]
+    # the same steps without the per-launch events, for the cost of recording them
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for k in range(args.steps):
+        run_step(calls)
+    torch.cuda.synchronize()
+    step_noev_s = (time.perf_counter() - t2) / args.steps
 
     per_op = {op: {"s": 0.0, "bytes": 0, "flops": 0, "roof_s": 0.0, "launches": 0} for op in OPS}
     roof_total = 0.0
@@ -341,7 +358,7 @@ def bench(args):
             "kernel": "qk gemm_kernel (fused dequant + LoRA)", "us_per_launch": round(g["s"] / g["launches"] * 1e6, 2),
             "flops_per_launch": g["flops"] // g["launches"]}
 
-    extra = {}
+    extra = {"ms_per_step_without_events": round(step_noev_s * 1e3, 3)}
     if not args.skip_isolated:
         extra["gemv_m1_isolated_607MB"] = gemv_isolated(torch, qk, workloads)
 

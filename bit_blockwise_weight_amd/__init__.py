@@ -9,6 +9,7 @@ library is missing or fails to load, the error is raised at the first call,
 not at import.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -121,6 +122,13 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _on(dev: torch.device):
+    """Makes `dev` current for the call (a no-op when it already is)."""
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -134,6 +142,10 @@ def _require_cuda(*ts):
 
 
 def _levels_arg(levels):
+    if isinstance(levels, ctypes.Array):      # already a float[16]
+        if len(levels) != 16:
+            raise ValueError("a level table has 16 entries")
+        return levels, torch.tensor(list(levels), dtype=torch.float32)
     lv = torch.as_tensor(levels, dtype=torch.float32).detach().cpu().contiguous()
     if lv.numel() != 16:
         raise ValueError("a level table has 16 entries")
@@ -172,7 +184,7 @@ def qk_quantize_blockwise(x: torch.Tensor, blocksize: int = 64, levels=None, cod
     if absmax is None:
         absmax = torch.empty((n + blocksize - 1) // blocksize, dtype=torch.float32, device=x.device)
     _require_cuda(codes, absmax)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         _check(lib().qk_quantize_blockwise(_ptr(x), _DTYPE_CODE[x.dtype], n, int(blocksize), lv, _ptr(codes),
                                            _ptr(absmax), ctypes.c_void_p(_stream(x))))
     return codes, absmax
@@ -200,7 +212,7 @@ def qk_double_quant(absmax: torch.Tensor, dq_blocksize: int = QK_DQ_BLOCK, q8=No
     if workspace is None:
         workspace = torch.empty(max(8, wsb), dtype=torch.uint8, device=dev)
     _require_cuda(q8, scale, mean, workspace)
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(lib().qk_double_quant(_ptr(absmax), nb, int(dq_blocksize), _ptr(q8), _ptr(scale), _ptr(mean),
                                      _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(absmax))))
     return q8, scale, mean
@@ -222,7 +234,7 @@ def qk_dequantize(state: QuantState, out_dtype=torch.bfloat16, out=None, device=
     if out is None:
         out = torch.empty(state.n, dtype=out_dtype, device=dev)
     _require_cuda(out)
-    with torch.cuda.device(out.device):
+    with _on(out.device):
         _check(lib().qk_dequantize(ctypes.byref(state), _ptr(out), _DTYPE_CODE[out.dtype],
                                    ctypes.c_void_p(_stream(out))))
     return out
@@ -237,7 +249,7 @@ def qk_gemv_nf4(x: torch.Tensor, state: QuantState, y=None) -> torch.Tensor:
     if y is None:
         y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=x.device)
     _require_cuda(y)
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         _check(lib().qk_gemv_nf4(_ptr(x2), M, ctypes.byref(state), _ptr(y), ctypes.c_void_p(_stream(x))))
     return y
 
@@ -260,7 +272,7 @@ def qk_gemm_nf4(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: 
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=X.device)
     _require_cuda(Y, workspace)
-    with torch.cuda.device(X.device):
+    with _on(X.device):
         _check(lib().qk_gemm_nf4(_ptr(X2), M, ctypes.byref(state), _ptr(A), _ptr(B), int(r), float(lora_scale),
                                  _ptr(Y), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                  ctypes.c_void_p(_stream(X))))

@@ -380,7 +380,7 @@ typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 __device__ __forceinline__ uint32_t xoff(int row, int chunk) {   // byte offset in an X tile
-    return (uint32_t)(row * 8 + (chunk ^ (row & 7))) * 16u;
+    return (uint32_t)(row * 8 + (chunk ^ ((row >> 1) & 7))) * 16u;
 }
 
 template <int R16, bool kNested>
@@ -390,14 +390,16 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
     // r <= 16: s X A is staged as bf16 hi/lo next to the K-loop buffers in the prologue;
     // larger ranks stage it in the K-loop buffers after the loop
     constexpr bool kTEarly = R16 == 1;
-    constexpr int kXBytes = 2 * TM * 128;              // two X tiles
-    constexpr int kTabBytes = 256 * kCopies * 8;       // fp32 level-pair table
-    constexpr int kTBytes = kTEarly ? 2 * TM * kTs * 2 : 0;
-    __shared__ __attribute__((aligned(1024))) uint4 lds[(kXBytes + kTabBytes + kTBytes) / 16];
+    static_assert(TM * kTs * 2 <= 2 * TM * 8 * 16 && TM * kTs * 2 <= 256 * kCopies * 8, "LoRA staging must fit");
+    constexpr int kTBytes = kTEarly ? 2 * TM * kTs * 2 : 16;
+    // The table is its own LDS object: reads of it then never wait for the
+    // direct-to-LDS X loads in flight (those only write the X buffers).
+    __shared__ __attribute__((aligned(1024))) uint4 lds[2 * TM * 8];        // two X tiles, 64 KB
+    __shared__ __attribute__((aligned(16))) uint2 tab[256 * kCopies];        // fp32 level pairs, 64 KB
+    __shared__ __attribute__((aligned(16))) uint4 tearly[kTBytes / 16];     // s X A (hi, lo) for r <= 16
     char* ldsb = reinterpret_cast<char*>(lds);
     uint4* xs0 = lds;                                               // X tile buffer 0
     uint4* xs1 = lds + TM * 8;                                      // X tile buffer 1
-    uint2* tab = reinterpret_cast<uint2*>(ldsb + kXBytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
     const float mean = kNested ? *a.w.dq_mean : 0.0f;
 
     // LoRA operands read in the prologue (r <= 16): B fragments and s X A as bf16 hi/lo in LDS
-    uint16_t* thi = reinterpret_cast<uint16_t*>(ldsb + (kTEarly ? kXBytes + kTabBytes : 0));
+    uint16_t* thi = reinterpret_cast<uint16_t*>(kTEarly ? reinterpret_cast<char*>(tearly) : ldsb);
     uint16_t* tlo = thi + TM * kTs;
     auto load_lora_b = [&](int kk, bf16x8_t (&bl)[2]) {
 #pragma unroll
@@ -451,7 +453,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
         const int64_t gm = m0 + tid < M ? m0 + tid : M - 1;
 #pragma unroll
         for (int c4 = 0; c4 < kRp / 4; ++c4) {
-            const float4 sum = *reinterpret_cast<const float4*>(T + gm * kRp + 4 * c4);
+            // s X A = sum of the pre-pass K splits, added in split order
+            float4 sum = *reinterpret_cast<const float4*>(T + gm * kRp + 4 * c4);
+#pragma unroll
+            for (int sp = 1; sp < kSplits; ++sp) {
+                const float4 t = *reinterpret_cast<const float4*>(T + (sp * M + gm) * kRp + 4 * c4);
+                sum.x += t.x; sum.y += t.y; sum.z += t.z; sum.w += t.w;
+            }
             const uint32_t h01 = pack_bf16x2(sum.x, sum.y), h23 = pack_bf16x2(sum.z, sum.w);
             const uint32_t l01 = pack_bf16x2(sum.x - as_float(h01 << 16), sum.y - as_float(h01 & 0xFFFF0000u));
             const uint32_t l23 = pack_bf16x2(sum.z - as_float(h23 << 16), sum.w - as_float(h23 & 0xFFFF0000u));
@@ -472,7 +480,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
     for (int v = 0; v < 8; ++v) {
         const int p = (v * 4 + wave) * 64 + lane;          // LDS 16-byte slot written by this lane
         const int row = p >> 3, slot = p & 7;
-        const int chunk = slot ^ (row & 7);
+        const int chunk = slot ^ ((row >> 1) & 7);
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         xsrc[v] = a.X + gm * K + chunk * 8;
     }
@@ -562,8 +570,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
             else dequant_q(c1, 0, bn);
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
-                const int row = 32 * rt + j;
-                const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(xbb + xoff(row, 4 * g + q));
+                const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(xbb + xoff(32 * rt + j, 4 * g + q));
                 acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bq[0], acc[rt][0], 0, 0, 0);
                 acc[rt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bq[1], acc[rt][1], 0, 0, 0);
             }
@@ -579,8 +586,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
     if constexpr (R16 > 0) {
         // LoRA: acc += (s X A) B, s X A as bf16 hi + lo (about 16 significant bits together)
         if constexpr (!kTEarly) {
-            thi = reinterpret_cast<uint16_t*>(ldsb);    // the K-loop buffers are free now
-            tlo = thi + TM * kTs;
+            // the K-loop buffers and the table are free now (TM * kTs * 2 <= 36 KB each)
+            thi = reinterpret_cast<uint16_t*>(ldsb);
+            tlo = reinterpret_cast<uint16_t*>(tab);
             stage_t();
             __syncthreads();
         }
@@ -607,35 +615,39 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
         __syncthreads();
     }
 
-    // epilogue: stage the bf16 tile in LDS (256 rows x 512 bytes = the K-loop buffers and the
-    // table), then write Y with 16-byte row-contiguous stores.  Register e of MFMA tile (rt, ct)
-    // holds C[32 rt + 8(e/4) + 4g + e%4][64 wave + 32 ct + j].
+    // epilogue: stage the bf16 tile in LDS, 128 rows at a time (128 rows x 512 bytes = the
+    // two X buffers), then write Y with 16-byte row-contiguous stores.  Register e of MFMA
+    // tile (rt, ct) holds C[32 rt + 8(e/4) + 4g + e%4][64 wave + 32 ct + j].
     uint16_t* cs = reinterpret_cast<uint16_t*>(ldsb);
+    const bool vec_ok = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
+    for (int half = 0; half < 2; ++half) {
+        if (half) __syncthreads();
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int col = 64 * wave + 32 * ct + j;
+        for (int rt = 4 * half; rt < 4 * half + 4; ++rt) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = 32 * rt + 8 * (e / 4) + 4 * g + (e % 4);
-                cs[row * TN + col] = (uint16_t)(pack_bf16x2(acc[rt][ct][e], 0.0f) & 0xFFFFu);
+            for (int ct = 0; ct < 2; ++ct) {
+                const int col = 64 * wave + 32 * ct + j;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 32 * (rt - 4 * half) + 8 * (e / 4) + 4 * g + (e % 4);
+                    cs[row * TN + col] = (uint16_t)(pack_bf16x2(acc[rt][ct][e], 0.0f) & 0xFFFFu);
+                }
             }
         }
-    }
-    __syncthreads();
-    const bool vec_ok = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
-    for (int c = tid; c < TM * (TN / 8); c += 256) {
-        const int row = c / (TN / 8), ch = c % (TN / 8);
-        const int64_t gm = m0 + row, gn = n0 + 8 * ch;
-        if (gm >= M || gn >= N) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(&cs[row * TN + 8 * ch]);
-        uint16_t* dst = a.Y + gm * N + gn;
-        if (vec_ok && gn + 8 <= N) {
-            *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-            for (int t = 0; t < 8 && gn + t < N; ++t) dst[t] = (uint16_t)(w4[t >> 1] >> ((t & 1) ? 16 : 0));
+        __syncthreads();
+        for (int c = tid; c < (TM / 2) * (TN / 8); c += 256) {
+            const int row = c / (TN / 8), ch = c % (TN / 8);
+            const int64_t gm = m0 + (TM / 2) * half + row, gn = n0 + 8 * ch;
+            if (gm >= M || gn >= N) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(&cs[row * TN + 8 * ch]);
+            uint16_t* dst = a.Y + gm * N + gn;
+            if (vec_ok && gn + 8 <= N) {
+                *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                for (int t = 0; t < 8 && gn + t < N; ++t) dst[t] = (uint16_t)(w4[t >> 1] >> ((t & 1) ? 16 : 0));
+            }
         }
     }
 }
@@ -644,8 +656,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
 // fp32, j < 16*R16 (columns >= r are 0).  Grid: (64-row groups, kSplits K
 // splits); a workgroup's 4 waves take 16 rows each and share the A tile of each
 // 64-deep step, transposed into LDS; the next step's X fragments are loaded
-// while the current step's MFMAs run.  lora_sum_kernel then adds the kSplits
-// partials in split order (deterministic).
+// while the current step's MFMAs run.  The GEMM kernel adds the kSplits partials
+// of its rows in split order (deterministic) when it stages s X A.
 template <int R16>
 __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restrict__ T) {
     constexpr int kRp = 16 * R16;
@@ -751,19 +763,6 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
     }
 }
 
-// T[0] += T[1] + ... + T[kSplits - 1], element by element in split order.
-__global__ __launch_bounds__(256) void lora_sum_kernel(float4* __restrict__ T, int64_t n4) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n4) return;
-    float4 acc = T[i];
-#pragma unroll
-    for (int p = 1; p < kSplits; ++p) {
-        const float4 t = T[(int64_t)p * n4 + i];
-        acc.x += t.x; acc.y += t.y; acc.z += t.z; acc.w += t.w;
-    }
-    T[i] = acc;
-}
-
 }  // namespace v4
 
 template <bool kNested>
@@ -793,9 +792,6 @@ hipError_t launch_fast(const GemmArgs& a, void* workspace, hipStream_t s) {
     float* T = reinterpret_cast<float*>(workspace);
     if (r16 > 0) {
         launch_lora_xa(a, T, s, r16);
-        const int64_t n4 = a.M * 16 * r16 / 4;
-        hipLaunchKernelGGL(v4::lora_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                           reinterpret_cast<float4*>(T), n4);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -37,7 +37,7 @@ namespace qk {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 32;          // rows per tile (MFMA 32x32)
 constexpr int kStep = 64;          // k per step
@@ -65,81 +65,141 @@ __device__ __forceinline__ void fill_pair_table(uint32_t* tab, const float* leve
     }
 }
 
-// MB = number of 8-row groups of the 32x32 output that hold real rows (M <= 8*MB)
-template <int MB, int S>
-__global__ __launch_bounds__(S * 64) void gemv_mfma_kernel(GemvArgs a) {
+// Fast path, 16 weight rows per workgroup (v_mfma_f32_16x16x32_bf16):
+//   A = x (16 x 32, rows m >= M are zero), B = W^T (32 x 16 rows of the tile), so the
+//   4 x 16 output registers of a wave are y[m][n] for m = 4(lane / 16) + r, n = lane % 16.
+//   Lane l holds row n = l % 16 and, in 64-k block b, the 16 weights
+//   k = 64 b + 16 h + [0, 16), h = l / 16 (8 code bytes, one 8-byte load); the two MFMAs
+//   of a block use k = 64 b + 16 h + 8 t + [0, 8), t = 0, 1, so both stay inside one block
+//   of 64 and the block scale of row n multiplies the block's partial product.
+//   The S waves of a workgroup take blocks b = wave, wave + S, ... and load the codes,
+//   scales and x of kBatch blocks ahead, so each wave keeps several HBM loads in flight.
+constexpr int kBatch = 4;
+
+struct GemvBatch {
+    uint2 c[kBatch];      // 8 code bytes of the lane's row
+    uint4 x0[kBatch];     // x[m][64 b + 16 h + 0..7]
+    uint4 x1[kBatch];     // x[m][64 b + 16 h + 8..15]
+    int32_t q[kBatch];    // q8 (nested) or absmax bits
+    float d[kBatch];      // dq scale (nested)
+};
+
+template <int S, bool kNested>
+__global__ __launch_bounds__(S * 64) void gemv16_kernel(GemvArgs a) {
     extern __shared__ uint32_t lds[];          // 64 KB pair table, reused for the reduction
-    fill_pair_table(lds, a.w.levels, S * 64);
-    __syncthreads();
-
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int j = lane & 31;                   // row of the tile / column of the MFMA output
-    const int g = lane >> 5;                   // which 32-weight half of the step
-    const int64_t n = (int64_t)blockIdx.x * kRows + j;
-    const bool row_ok = n < a.N;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;                   // weight row of the tile (and x row m of the A operand)
+    const int h = lane >> 4;                   // 16-weight group of a 64-k block
+    const int64_t row = (int64_t)blockIdx.x * 16 + n;
+    const bool row_ok = row < a.N;
+    const int64_t rowc = row_ok ? row : a.N - 1;
     const int64_t K = a.K;
-    const int64_t nsteps = K / kStep;
+    const int64_t nblk = K / 64;
+    const int64_t nbw = (nblk - wave + S - 1) / S;        // blocks of this wave
     const int M = a.M;
-    const uint8_t* row_codes = a.w.codes + (row_ok ? n : 0) * (K / 2);
-    const int64_t row_elem0 = (row_ok ? n : 0) * K;
-    const uint32_t lane_sel = (uint32_t)lane * 4u;         // low byte of the LDS address
-    const char* tab = reinterpret_cast<const char*>(lds);
-    const int xi = lane & 31;                                // x row held by this lane
-    const bool x_ok = xi < M;
-    const uint16_t* xrow = a.x + (int64_t)(x_ok ? xi : 0) * K;
+    const bool x_ok = n < M;
+    const uint16_t* xrow = a.x + (int64_t)(x_ok ? n : 0) * K + 16 * h;
+    const uint8_t* crow = a.w.codes + rowc * (K / 2) + 8 * h;
+    const int64_t qb0 = (rowc * K) >> a.w.blocksize_log2;  // first quantization block of the row
+    const int bshift = a.w.blocksize_log2 - 6;
+    const float mean = kNested ? *a.w.dq_mean : 0.0f;
 
-    floatx16_t acc;
+    auto load = [&](int64_t i0, GemvBatch& bt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-
-    for (int64_t s = wave; s < nsteps; s += S) {
-        const int64_t k0 = s * kStep + g * 32;
-        uint4 cw = make_uint4(0, 0, 0, 0);
-        if (row_ok) cw = *reinterpret_cast<const uint4*>(row_codes + k0 / 2);
-        uint4 xv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            xv[q] = x_ok ? *reinterpret_cast<const uint4*>(xrow + k0 + 8 * q) : make_uint4(0, 0, 0, 0);
-        }
-        const float sc = row_ok ? row_scale(a.w, (row_elem0 + s * kStep) >> a.w.blocksize_log2) : 0.0f;
-
-        floatx16_t part;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) part[r] = 0.0f;
-        const uint32_t cws[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t wv[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                // address = code byte b of the word << 8 | 4 * lane
-                const uint32_t addr = __builtin_amdgcn_perm(cws[q], lane_sel, 0x0C0C0400u | ((uint32_t)(4 + b) << 8));
-                wv[b] = *reinterpret_cast<const uint32_t*>(tab + addr);
+        for (int p = 0; p < kBatch; ++p) {
+            int64_t b = wave + (int64_t)S * (i0 + p);
+            b = b < nblk ? b : nblk - 1;
+            bt.c[p] = *reinterpret_cast<const uint2*>(crow + 32 * b);
+            const uint4* xp = reinterpret_cast<const uint4*>(xrow + 64 * b);
+            bt.x0[p] = xp[0];     // rows m >= M read row 0 and are zeroed at use
+            bt.x1[p] = xp[1];
+            const int64_t qb = qb0 + (b >> bshift);
+            if constexpr (kNested) {
+                bt.q[p] = (int32_t)a.w.q8[qb];
+                bt.d[p] = a.w.dq_scale[qb / QK_DQ_BLOCK];
+            } else {
+                bt.q[p] = (int32_t)as_uint(a.w.absmax[qb]);
+                bt.d[p] = 0.0f;
             }
-            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
-            const bf16x8_t aop = __builtin_bit_cast(bf16x8_t, xv[q]);
-            part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, part, 0, 0, 0);
         }
+    };
+
+    const uint32_t lane_sel = (uint32_t)lane * 4u;
+    const char* tab = reinterpret_cast<const char*>(lds);
+    floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](const GemvBatch& bt, int64_t i0) {
 #pragma unroll
-        for (int r = 0; r < 4 * MB; ++r) acc[r] = __builtin_fmaf(part[r], sc, acc[r]);
+        for (int p = 0; p < kBatch; ++p) {
+            const uint32_t cws[2] = {bt.c[p].x, bt.c[p].y};
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            const uint4 xs[2] = {x_ok ? bt.x0[p] : z, x_ok ? bt.x1[p] : z};
+            floatx4_t part = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const uint32_t addr = __builtin_amdgcn_perm(cws[t], lane_sel, 0x0C0C0400u | ((uint32_t)(4 + bb) << 8));
+                    wv[bb] = *reinterpret_cast<const uint32_t*>(tab + addr);
+                }
+                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs[t]),
+                                                               __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3])),
+                                                               part, 0, 0, 0);
+            }
+            float sc;
+            if constexpr (kNested) sc = __fadd_rn(__fmul_rn((float)bt.q[p], bt.d[p]), mean);
+            else sc = as_float((uint32_t)bt.q[p]);
+            const bool live = i0 + p < nbw;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = live ? __builtin_fmaf(part[r], sc, acc[r]) : acc[r];
+        }
+    };
+
+    // two batches in flight: while one is decoded, the loads of the next are outstanding
+    GemvBatch ba, bb;
+    load(0, ba);
+    load(kBatch, bb);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        // pair table, 64 copies: entry i = 64 b + copy for byte b.  With 8 waves, wave w
+        // writes the bytes b = w + 8 j, whose nibbles are (j / 2, w + 8 (j % 2)); the level
+        // reads are uniform (scalar loads), so they do not wait for the batches in flight.
+        static_assert(S == 8, "table fill assumes 8 waves");
+        const int w = wave;
+        const uint32_t lo0 = as_uint(a.w.levels[w]), lo1 = as_uint(a.w.levels[w + 8]);
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) {
+            const float hi_nib = a.w.levels[jj >> 1];
+            lds[(w + 8 * jj) * kTabCopies + lane] = pack_bf16x2(hi_nib, as_float((jj & 1) ? lo1 : lo0));
+        }
+    }
+    __syncthreads();
+    for (int64_t i0 = 0; i0 < nbw; i0 += 2 * kBatch) {
+        compute(ba, i0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i0 + 2 * kBatch < nbw) load(i0 + 2 * kBatch, ba);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(bb, i0 + kBatch);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i0 + 3 * kBatch < nbw) load(i0 + 3 * kBatch, bb);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // reduce the S partial tiles: red[wave][r][lane] for the kept registers
+    // reduce the S waves' tiles in a fixed order: red[wave][r][lane]
     __syncthreads();
     float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int r = 0; r < 4 * MB; ++r) red[(wave * 4 * MB + r) * 64 + lane] = acc[r];
+    for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
     __syncthreads();
-    // output element (i, j): register r = 4*(i/8) + i%4, lane = j + 32*((i/4)%2)
-    for (int e = threadIdx.x; e < M * kRows; e += S * 64) {
-        const int i = e / kRows, jj = e % kRows;
-        const int r = 4 * (i / 8) + (i % 4);
-        const int ln = jj + 32 * ((i / 4) % 2);
+    // output (m, nn): register r = m % 4 of lane nn + 16 (m / 4)
+    for (int e = threadIdx.x; e < M * 16; e += S * 64) {
+        const int m = e >> 4, nn = e & 15;
+        const int r = m & 3, ln = nn + 16 * (m >> 2);
         float v = 0.0f;
-        for (int w = 0; w < S; ++w) v += red[(w * 4 * MB + r) * 64 + ln];
-        const int64_t nn = (int64_t)blockIdx.x * kRows + jj;
-        if (nn < a.N) a.y[(int64_t)i * a.N + nn] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+        for (int w = 0; w < S; ++w) v += red[(w * 4 + r) * 64 + ln];
+        const int64_t on = (int64_t)blockIdx.x * 16 + nn;
+        if (on < a.N) a.y[(int64_t)m * a.N + on] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
     }
 }
 
@@ -176,11 +236,11 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
     }
 }
 
-template <int MB, int S>
-hipError_t launch_mfma(const GemvArgs& a, hipStream_t s) {
-    const unsigned grid = (unsigned)((a.N + kRows - 1) / kRows);
-    const size_t lds = 256 * kTabCopies * sizeof(uint32_t);   // 64 KB, >= S * 4MB * 64 * 4
-    hipLaunchKernelGGL((gemv_mfma_kernel<MB, S>), dim3(grid), dim3(S * 64), lds, s, a);
+template <int S, bool kNested>
+hipError_t launch16(const GemvArgs& a, hipStream_t s) {
+    const unsigned grid = (unsigned)((a.N + 15) / 16);
+    const size_t lds = 256 * kTabCopies * sizeof(uint32_t);   // 64 KB, >= S * 4 * 64 * 4
+    hipLaunchKernelGGL((gemv16_kernel<S, kNested>), dim3(grid), dim3(S * 64), lds, s, a);
     return hipGetLastError();
 }
 
@@ -195,16 +255,14 @@ hipError_t launch_gemv(const void* x, int32_t M, const MatArgs& w, void* y, hipS
     a.K = w.K;
     a.M = M;
     const bool fast = (w.K % kStep) == 0 && (w.K % w.w.blocksize) == 0 &&
-                      (reinterpret_cast<uintptr_t>(x) % 16) == 0 && (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0;
+                      (reinterpret_cast<uintptr_t>(x) % 16) == 0 && (reinterpret_cast<uintptr_t>(w.w.codes) % 8) == 0;
     if (!fast) {
         *variant = "generic (per-element dequantization, one wave per row)";
         hipLaunchKernelGGL(gemv_generic_kernel, dim3((unsigned)((w.N + 3) / 4)), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    const int64_t nsteps = w.K / kStep;
-    *variant = "mfma 32x32x16 bf16, LDS byte-pair table, split-K over 16 waves";
-    if (nsteps >= 16) return M <= 8 ? launch_mfma<1, 16>(a, s) : launch_mfma<2, 16>(a, s);
-    return M <= 8 ? launch_mfma<1, 4>(a, s) : launch_mfma<2, 4>(a, s);
+    *variant = "mfma 16x16x32 bf16, 16 rows per workgroup, LDS byte-pair table, 8 waves split-K, 4-block prefetch";
+    return w.w.nested ? launch16<8, true>(a, s) : launch16<8, false>(a, s);
 }
 
 }  // namespace qk
