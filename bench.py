@@ -395,36 +395,76 @@ def copy_calibration():
     return 0
 
 
-def summarize_pmc(directory, kernel_substr, out_path, source="gemm.hip"):
-    """Reads rocprofv3 --pmc counter CSVs (FETCH_SIZE pass and WRITE_SIZE pass,
-    plus a copy-calibration pass) and writes the per-dispatch HBM traffic of the
-    kernel whose name contains `kernel_substr`, scaled by the copy kernel."""
+def _csv_rows(directory, suffix):
     import csv
+    rows = []
+    for p in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(p) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
 
-    def rows_of(pattern):
-        out = []
-        for p in glob.glob(os.path.join(directory, "**", pattern), recursive=True):
-            with open(p) as fh:
-                out += list(csv.DictReader(fh))
-        return out
 
-    recs = rows_of("*counter_collection.csv")
-    vals = {}
-    for r in recs:
-        name = r.get("Kernel_Name", "")
-        cn = r.get("Counter_Name", "")
-        try:
-            v = float(r.get("Counter_Value", "nan"))
-        except ValueError:
-            continue
-        key = "copy" if ("copy" in name.lower() or "elementwise" in name.lower()) else (
-            "target" if kernel_substr in name else None)
-        if key is None:
-            continue
-        vals.setdefault((key, cn), []).append(v)
-    summary = {k[0] + ":" + k[1]: sum(v) / len(v) for k, v in vals.items()}
-    print(json.dumps(summary, indent=1))
-    return summary
+def summarize_trace(directory, out_path, command):
+    """Writes a short markdown summary of a `rocprofv3 --kernel-trace --stats`
+    output directory (its *_kernel_stats.csv) with the command that made it."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    if not rows:
+        print(f"no kernel_stats.csv under {directory}", file=sys.stderr)
+        return 1
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
+             "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("|", "/")
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out_path}")
+    return 0
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path, command):
+    """HBM traffic per dispatch of the GEMM main kernel from two rocprofv3 --pmc
+    runs of bench.py (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each
+    scaled by what the same counter reads for a plain 1 GiB device copy
+    (bench.py --copy-calibration) against the bytes that copy moves."""
+    def per_kernel(directory, counter):
+        vals = {}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    def pick(vals, key):
+        hits = [v for k, v in vals.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of a kernel matching {key!r}")
+        flat = [x for h in hits for x in h]
+        return sum(flat) / len(flat)
+
+    copy_bytes = 1 << 30
+    f_copy = pick(per_kernel(copy_fetch_dir, "FETCH_SIZE"), "copy") * 1024.0
+    w_copy = pick(per_kernel(copy_write_dir, "WRITE_SIZE"), "copy") * 1024.0
+    f_gemm = pick(per_kernel(fetch_dir, "FETCH_SIZE"), "gemm_fast_kernel") * 1024.0
+    w_gemm = pick(per_kernel(write_dir, "WRITE_SIZE"), "gemm_fast_kernel") * 1024.0
+    fetch_scale = copy_bytes / f_copy
+    write_scale = copy_bytes / w_copy
+    out = {
+        "kernel": "gemm_fast_kernel", "source": "gemm.hip", "source_sha": source_sha("gemm.hip"),
+        "command": command,
+        "copy_calibration": {"bytes": copy_bytes, "fetch_counter_bytes": f_copy, "write_counter_bytes": w_copy,
+                             "fetch_scale": fetch_scale, "write_scale": write_scale},
+        "fetch_bytes_per_dispatch": f_gemm * fetch_scale, "write_bytes_per_dispatch": w_gemm * write_scale,
+        "bytes_per_dispatch": f_gemm * fetch_scale + w_gemm * write_scale,
+        "note": "average over the dispatches of the bench step (7 weight shapes)",
+    }
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
 
 
 def main():
@@ -434,8 +474,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-isolated", action="store_true", help="skip the isolated GEMV HBM measurement")
-    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB device copy")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"),
+                    help="summarize a rocprofv3 --kernel-trace --stats directory into OUT")
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT"),
+                    help="GEMM HBM traffic per dispatch from rocprofv3 --pmc runs")
+    ap.add_argument("--command", default="", help="the command recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, command=args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the hot path here runs on a single "
               "device and this build has no multi-GPU path", file=sys.stderr)

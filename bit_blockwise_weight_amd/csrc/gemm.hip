@@ -25,6 +25,8 @@
 // A generic variant (template flag) loads X element by element and dequantizes
 // W with flat indexing, for K that is not a multiple of 64 or of the block size
 // (blocks straddling rows) and unaligned X.
+#include <type_traits>
+
 #include "qk_internal.h"
 #include "qk_device.h"
 
@@ -375,6 +377,8 @@ constexpr int TN = 256;
 constexpr int TK = 64;
 constexpr int kCopies = 32;
 constexpr int kSplits = 8;                // K splits of the LoRA X*A pre-pass
+constexpr int kXcds = 8;                  // MI355X: 8 XCDs, workgroups dealt round robin
+constexpr int kGroupM = 4;                // tile rows per group in the tile order
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -386,31 +390,44 @@ __device__ __forceinline__ uint32_t xoff(int row, int chunk) {   // byte offset 
 template <int R16, bool kNested>
 __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const float* __restrict__ T) {
     constexpr int kRp = 16 * R16;
-    constexpr int kTs = kRp + 8;                       // LoRA T rows in LDS (bf16 elements)
-    // r <= 16: s X A is staged as bf16 hi/lo next to the K-loop buffers in the prologue;
-    // larger ranks stage it in the K-loop buffers after the loop
+    constexpr int kTs = 16 + 8;                        // row pitch of a staged 16-rank chunk of s X A
+    // r <= 16: the one chunk of s X A is staged in the prologue; larger ranks stage
+    // their chunks one after another after the K loop
     constexpr bool kTEarly = R16 == 1;
-    static_assert(TM * kTs * 2 <= 2 * TM * 8 * 16 && TM * kTs * 2 <= 256 * kCopies * 8, "LoRA staging must fit");
-    constexpr int kTBytes = kTEarly ? 2 * TM * kTs * 2 : 16;
-    // The table is its own LDS object: reads of it then never wait for the
-    // direct-to-LDS X loads in flight (those only write the X buffers).
-    __shared__ __attribute__((aligned(1024))) uint4 lds[2 * TM * 8];        // two X tiles, 64 KB
-    __shared__ __attribute__((aligned(16))) uint2 tab[256 * kCopies];        // fp32 level pairs, 64 KB
-    __shared__ __attribute__((aligned(16))) uint4 tearly[kTBytes / 16];     // s X A (hi, lo) for r <= 16
-    char* ldsb = reinterpret_cast<char*>(lds);
-    uint4* xs0 = lds;                                               // X tile buffer 0
-    uint4* xs1 = lds + TM * 8;                                      // X tile buffer 1
+    constexpr int kCodeLoads = kNested ? 6 : 4;     // global loads issued by load_codes
+    // Separate LDS objects: the compiler then knows that reads of one X buffer, of the
+    // table or of the LoRA chunk never alias the direct-to-LDS loads into the other X
+    // buffer, and does not wait for those loads before every LDS read.
+    __shared__ __attribute__((aligned(1024))) uint4 xsA[TM * 8];          // X tile buffer 0, 32 KB
+    __shared__ __attribute__((aligned(1024))) uint4 xsB[TM * 8];          // X tile buffer 1, 32 KB
+    __shared__ __attribute__((aligned(16))) uint2 tab[256 * kCopies];     // fp32 level pairs, 64 KB
+    __shared__ __attribute__((aligned(16))) uint16_t tst[2 * TM * kTs];   // s X A chunk, bf16 hi | lo, 24 KB
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int j = lane & 31;
     const int g = lane >> 5;
-    const int64_t m0 = (int64_t)blockIdx.y * TM;
-    const int64_t n0 = (int64_t)blockIdx.x * TN;
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t nk = K / TK, nk1 = nk - 1;
     const int r = a.r;
+    int64_t m0, n0;
+    {
+        // Tile order.  Workgroup i runs on XCD i % 8, and each XCD has its own L2, so the
+        // tiles of an XCD are made a compact group: the 1-D id is first regrouped so that
+        // XCD x gets consecutive logical ids, then logical ids walk groups of kGroupM tile
+        // rows column by column.  The XCD's tiles then share X rows and W columns in L2.
+        const uint32_t tiles_n = (uint32_t)((N + TN - 1) / TN), tiles_m = (uint32_t)((M + TM - 1) / TM);
+        const uint32_t nt = tiles_n * tiles_m;
+        const uint32_t bid = blockIdx.x;
+        const uint32_t lid = (nt % kXcds == 0) ? (bid % kXcds) * (nt / kXcds) + bid / kXcds : bid;
+        const uint32_t per_group = kGroupM * tiles_n;
+        const uint32_t first_m = (lid / per_group) * kGroupM;
+        const uint32_t gm = tiles_m - first_m < (uint32_t)kGroupM ? tiles_m - first_m : (uint32_t)kGroupM;
+        const uint32_t in_group = lid % per_group;
+        m0 = (int64_t)(first_m + in_group % gm) * TM;
+        n0 = (int64_t)(in_group / gm) * TN;
+    }
 
     for (int i = tid; i < 256 * kCopies; i += 256) {
         const int b = i / kCopies;
@@ -429,9 +446,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
     const char* tabb = reinterpret_cast<const char*>(tab);
     const float mean = kNested ? *a.w.dq_mean : 0.0f;
 
-    // LoRA operands read in the prologue (r <= 16): B fragments and s X A as bf16 hi/lo in LDS
-    uint16_t* thi = reinterpret_cast<uint16_t*>(kTEarly ? reinterpret_cast<char*>(tearly) : ldsb);
-    uint16_t* tlo = thi + TM * kTs;
+    // LoRA: B fragments of a 16-rank chunk, and the chunk of s X A as bf16 hi / lo in LDS
+    uint16_t* thi = tst;
+    uint16_t* tlo = tst + TM * kTs;
     auto load_lora_b = [&](int kk, bf16x8_t (&bl)[2]) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
@@ -448,16 +465,16 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
                                                              e[4] | (e[5] << 16), e[6] | (e[7] << 16)));
         }
     };
-    auto stage_t = [&]() {
-        // thread t: row t of the tile; s X A already summed over the K splits
+    auto stage_t = [&](int kk) {
+        // thread t: row t of the tile, ranks [kk, kk + 16)
         const int64_t gm = m0 + tid < M ? m0 + tid : M - 1;
 #pragma unroll
-        for (int c4 = 0; c4 < kRp / 4; ++c4) {
+        for (int c4 = 0; c4 < 4; ++c4) {
             // s X A = sum of the pre-pass K splits, added in split order
-            float4 sum = *reinterpret_cast<const float4*>(T + gm * kRp + 4 * c4);
+            float4 sum = *reinterpret_cast<const float4*>(T + gm * kRp + kk + 4 * c4);
 #pragma unroll
             for (int sp = 1; sp < kSplits; ++sp) {
-                const float4 t = *reinterpret_cast<const float4*>(T + (sp * M + gm) * kRp + 4 * c4);
+                const float4 t = *reinterpret_cast<const float4*>(T + (sp * M + gm) * kRp + kk + 4 * c4);
                 sum.x += t.x; sum.y += t.y; sum.z += t.z; sum.w += t.w;
             }
             const uint32_t h01 = pack_bf16x2(sum.x, sum.y), h23 = pack_bf16x2(sum.z, sum.w);
@@ -470,7 +487,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
     bf16x8_t bl_early[2];
     if constexpr (kTEarly) {
         load_lora_b(0, bl_early);
-        stage_t();
+        stage_t(0);
     }
 
     // X tile rows loaded by this lane (clamped to the last valid row: rows past M
@@ -484,9 +501,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
         xsrc[v] = a.X + gm * K + chunk * 8;
     }
-    auto load_x = [&](int64_t s, int buf) {
+    auto load_x = [&](int64_t s, auto buf) {
         const int64_t k0 = (s < nk1 ? s : nk1) * TK;
-        char* base = reinterpret_cast<char*>(buf ? xs1 : xs0);
+        char* base = reinterpret_cast<char*>(decltype(buf)::value ? xsB : xsA);
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
             lptr_t dst = (lptr_t)((__attribute__((address_space(3))) char*)base + (v * 4 + wave) * 1024);
@@ -547,27 +564,37 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rt][ct][e] = 0.0f;
 
-    Codes c0, c1, c2;              // steps s, s + 1, s + 2
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
+    Codes c0, c1, c2, c3;          // codes of steps s .. s + 3
     load_codes(0, c0);
     load_codes(1, c1);
-    load_x(0, 0);
+    load_codes(2, c2);
+    load_x(0, Buf0{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();               // table and X(0) in LDS
     bf16x8_t bq[2];
     dequant_q(c0, 0, bq);
     __syncthreads();
 
-    for (int64_t s = 0; s < nk; ++s) {
-        const int buf = (int)(s & 1);
+    // One K step: ca = codes of step s, cb = codes of step s + 1, cn receives the codes
+    // of step s + 3; X of step s is in buffer s % 2.  Codes are loaded three steps ahead
+    // so that a load issued in step s is complete by the barrier of step s + 1, before
+    // anything of step s + 2 (its first user) runs.  The loop is unrolled four times so
+    // that the code buffers rotate by name (a register copy would wait for its load) and
+    // every X buffer is a fixed LDS object.
+    auto step = [&](int64_t s, auto buf, const Codes& ca, const Codes& cb, Codes& cn) {
+        constexpr bool kB = decltype(buf)::value;
         // loads for later steps, issued first so they have the whole step
-        load_codes(s + 2, c2);
-        load_x(s + 1, buf ^ 1);
-        const char* xbb = reinterpret_cast<const char*>(buf ? xs1 : xs0);
+        if constexpr (kB) load_x(s + 1, Buf0{});
+        else load_x(s + 1, Buf1{});
+        load_codes(s + 3, cn);
+        const char* xbb = reinterpret_cast<const char*>(kB ? xsB : xsA);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             bf16x8_t bn[2];
-            if (q < 3) dequant_q(c0, q + 1, bn);
-            else dequant_q(c1, 0, bn);
+            if (q < 3) dequant_q(ca, q + 1, bn);
+            else dequant_q(cb, 0, bn);
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
                 const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(xbb + xoff(32 * rt + j, 4 * g + q));
@@ -577,21 +604,28 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
             bq[0] = bn[0];
             bq[1] = bn[1];
         }
-        c0 = c1;
-        c1 = c2;
-        __builtin_amdgcn_s_waitcnt(0);     // X(s + 1) has landed in LDS
-        __syncthreads();
+        // X(s + 1) has landed in LDS once at most the code loads of step s + 3 (issued
+        // after it) are outstanding; those stay in flight across the barrier.  A plain
+        // s_barrier: __syncthreads() would add a release fence, which waits for every
+        // outstanding global load.  The empty asm statements keep the compiler from
+        // moving memory accesses across the barrier.
+        __builtin_amdgcn_s_waitcnt(kCodeLoads | 0x70);   // vmcnt(kCodeLoads) expcnt(7) lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    for (int64_t s = 0; s < nk; s += 4) {
+        step(s, Buf0{}, c0, c1, c3);
+        if (s + 1 < nk) step(s + 1, Buf1{}, c1, c2, c0);
+        if (s + 2 < nk) step(s + 2, Buf0{}, c2, c3, c1);
+        if (s + 3 < nk) step(s + 3, Buf1{}, c3, c0, c2);
     }
+    __builtin_amdgcn_s_waitcnt(0);   // the last (clamped, unused) prefetches
+    __syncthreads();
 
     if constexpr (R16 > 0) {
-        // LoRA: acc += (s X A) B, s X A as bf16 hi + lo (about 16 significant bits together)
-        if constexpr (!kTEarly) {
-            // the K-loop buffers and the table are free now (TM * kTs * 2 <= 36 KB each)
-            thi = reinterpret_cast<uint16_t*>(ldsb);
-            tlo = reinterpret_cast<uint16_t*>(tab);
-            stage_t();
-            __syncthreads();
-        }
+        // LoRA: acc += (s X A) B, 16 ranks at a time; s X A as bf16 hi + lo (about 16
+        // significant bits together)
 #pragma unroll
         for (int kk = 0; kk < kRp; kk += 16) {
             bf16x8_t bl[2];
@@ -599,12 +633,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
                 bl[0] = bl_early[0];
                 bl[1] = bl_early[1];
             } else {
+                if (kk > 0) __syncthreads();      // the previous chunk has been read
+                stage_t(kk);
                 load_lora_b(kk, bl);
+                __syncthreads();
             }
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
-                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&thi[(32 * rt + j) * kTs + kk + 8 * g]);
-                const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&tlo[(32 * rt + j) * kTs + kk + 8 * g]);
+                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&thi[(32 * rt + j) * kTs + 8 * g]);
+                const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&tlo[(32 * rt + j) * kTs + 8 * g]);
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[ct], acc[rt][ct], 0, 0, 0);
@@ -612,33 +649,31 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
                 }
             }
         }
-        __syncthreads();
     }
 
-    // epilogue: stage the bf16 tile in LDS, 128 rows at a time (128 rows x 512 bytes = the
-    // two X buffers), then write Y with 16-byte row-contiguous stores.  Register e of MFMA
-    // tile (rt, ct) holds C[32 rt + 8(e/4) + 4g + e%4][64 wave + 32 ct + j].
-    uint16_t* cs = reinterpret_cast<uint16_t*>(ldsb);
+    // epilogue: stage the bf16 tile in LDS 64 rows at a time (64 rows x 512 bytes = one X
+    // buffer, alternating), then write Y with 16-byte row-contiguous stores.  Register e
+    // of MFMA tile (rt, ct) holds C[32 rt + 8(e/4) + 4g + e%4][64 wave + 32 ct + j].
     const bool vec_ok = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (half) __syncthreads();
+    for (int pass = 0; pass < 4; ++pass) {
+        uint16_t* cs = reinterpret_cast<uint16_t*>((pass & 1) ? xsB : xsA);
 #pragma unroll
-        for (int rt = 4 * half; rt < 4 * half + 4; ++rt) {
+        for (int rt = 2 * pass; rt < 2 * pass + 2; ++rt) {
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
                 const int col = 64 * wave + 32 * ct + j;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int row = 32 * (rt - 4 * half) + 8 * (e / 4) + 4 * g + (e % 4);
+                    const int row = 32 * (rt - 2 * pass) + 8 * (e / 4) + 4 * g + (e % 4);
                     cs[row * TN + col] = (uint16_t)(pack_bf16x2(acc[rt][ct][e], 0.0f) & 0xFFFFu);
                 }
             }
         }
         __syncthreads();
-        for (int c = tid; c < (TM / 2) * (TN / 8); c += 256) {
+        for (int c = tid; c < (TM / 4) * (TN / 8); c += 256) {
             const int row = c / (TN / 8), ch = c % (TN / 8);
-            const int64_t gm = m0 + (TM / 2) * half + row, gn = n0 + 8 * ch;
+            const int64_t gm = m0 + (TM / 4) * pass + row, gn = n0 + 8 * ch;
             if (gm >= M || gn >= N) continue;
             const uint4 v = *reinterpret_cast<const uint4*>(&cs[row * TN + 8 * ch]);
             uint16_t* dst = a.Y + gm * N + gn;
@@ -767,12 +802,13 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
 
 template <bool kNested>
 void launch_fast_r(const GemmArgs& a, const float* T, hipStream_t s, dim3 grid, int r16) {
+    const dim3 block(256);
     switch (r16) {
-        case 0: hipLaunchKernelGGL((v4::gemm_fast_kernel<0, kNested>), grid, dim3(256), 0, s, a, T); break;
-        case 1: hipLaunchKernelGGL((v4::gemm_fast_kernel<1, kNested>), grid, dim3(256), 0, s, a, T); break;
-        case 2: hipLaunchKernelGGL((v4::gemm_fast_kernel<2, kNested>), grid, dim3(256), 0, s, a, T); break;
-        case 3: hipLaunchKernelGGL((v4::gemm_fast_kernel<3, kNested>), grid, dim3(256), 0, s, a, T); break;
-        default: hipLaunchKernelGGL((v4::gemm_fast_kernel<4, kNested>), grid, dim3(256), 0, s, a, T); break;
+        case 0: hipLaunchKernelGGL((v4::gemm_fast_kernel<0, kNested>), grid, block, 0, s, a, T); break;
+        case 1: hipLaunchKernelGGL((v4::gemm_fast_kernel<1, kNested>), grid, block, 0, s, a, T); break;
+        case 2: hipLaunchKernelGGL((v4::gemm_fast_kernel<2, kNested>), grid, block, 0, s, a, T); break;
+        case 3: hipLaunchKernelGGL((v4::gemm_fast_kernel<3, kNested>), grid, block, 0, s, a, T); break;
+        default: hipLaunchKernelGGL((v4::gemm_fast_kernel<4, kNested>), grid, block, 0, s, a, T); break;
     }
 }
 
@@ -787,7 +823,7 @@ void launch_lora_xa(const GemmArgs& a, float* T, hipStream_t s, int r16) {
 }
 
 hipError_t launch_fast(const GemmArgs& a, void* workspace, hipStream_t s) {
-    const dim3 grid((unsigned)((a.N + v4::TN - 1) / v4::TN), (unsigned)((a.M + v4::TM - 1) / v4::TM));
+    const dim3 grid((unsigned)(((a.N + v4::TN - 1) / v4::TN) * ((a.M + v4::TM - 1) / v4::TM)));
     const int r16 = a.A ? (a.r + 15) / 16 : 0;
     float* T = reinterpret_cast<float*>(workspace);
     if (r16 > 0) {
@@ -819,7 +855,7 @@ hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A
     a.K = w.K;
     a.r = A ? r : 0;
     a.lora_scale = lora_scale;
-    if (a.M > 65535LL * BM) return hipErrorInvalidValue;
+    if (a.M > 65535LL * BM || a.N > 65535LL * BN) return hipErrorInvalidValue;   // grid limits of both paths
     const bool fast = (w.K % BK) == 0 && (w.K % w.w.blocksize) == 0 && (reinterpret_cast<uintptr_t>(X) % 16) == 0 &&
                       (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0;
     if (fast) {
