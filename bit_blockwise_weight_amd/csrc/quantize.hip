@@ -10,8 +10,10 @@
 // loads elements [8l, 8l+8) of the unit with one 16-byte load (bf16 / fp16) or
 // two (fp32), so each load instruction reads 1 KB contiguous.  The B/8 lanes
 // that share a block reduce its absmax with DPP moves (no LDS, no atomics).
-// Each wave takes kUnroll consecutive units per iteration of a grid-stride loop
-// so several loads are in flight per lane.
+// The grid is a few workgroups per CU (the LDS table is filled once per
+// workgroup); each wave takes kUnroll consecutive units per iteration of a
+// grid-stride loop and loads the next iteration's units before it processes the
+// current ones, so two batches are in flight per lane.
 //
 // Division.  For bf16 and fp16 inputs t = RN(x/a) is computed from one IEEE
 // reciprocal per block and Markstein's correction
@@ -36,6 +38,7 @@ namespace {
 constexpr int kQThreads = 256;
 constexpr int kLutCopies = 32;
 constexpr int kUnroll = 4;
+constexpr int kWgsPerCu = 4;
 constexpr int kUnitElems = kWave * 8;
 
 constexpr float kAMin = 0x1p-36f;
@@ -46,47 +49,56 @@ struct Bf16In {};
 struct F16In {};
 struct F32In {};
 
-template <typename T>
-__device__ __forceinline__ void load8_full(const void* x, int64_t base, float v[8]);
-
-template <>
-__device__ __forceinline__ void load8_full<Bf16In>(const void* x, int64_t base, float v[8]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
-    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-}
-
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-template <>
-__device__ __forceinline__ void load8_full<F16In>(const void* x, int64_t base, float v[8]) {
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
-    v[0] = h2f(w.x & 0xFFFF); v[1] = h2f(w.x >> 16);
-    v[2] = h2f(w.y & 0xFFFF); v[3] = h2f(w.y >> 16);
-    v[4] = h2f(w.z & 0xFFFF); v[5] = h2f(w.z >> 16);
-    v[6] = h2f(w.w & 0xFFFF); v[7] = h2f(w.w >> 16);
-}
+// Raw 8-element input of one lane: one 16-byte word for 16-bit types, two for fp32.
+// A lane whose 8 elements run past n loads them one by one (zeros past n).
+template <typename T> struct RawOf { typedef uint4 type; };
+template <> struct RawOf<F32In> { typedef uint4 type[2]; };
 
-template <>
-__device__ __forceinline__ void load8_full<F32In>(const void* x, int64_t base, float v[8]) {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+template <typename T>
+__device__ __forceinline__ void load_raw(const void* x, int64_t n, int64_t base, typename RawOf<T>::type& r) {
+    if constexpr (__is_same(T, F32In)) {
+        if (base + 8 <= n) {
+            const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + base);
+            r[0] = p[0];
+            r[1] = p[1];
+        } else {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] = (base + i < n) ? as_uint(reinterpret_cast<const float*>(x)[base + i]) : 0u;
+            r[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            r[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+    } else {
+        if (base + 8 <= n) {
+            r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
+        } else {
+            uint32_t h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = (base + i < n) ? (uint32_t)reinterpret_cast<const uint16_t*>(x)[base + i] : 0u;
+            r = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        }
+    }
 }
 
 template <typename T>
-__device__ __forceinline__ float load1(const void* x, int64_t i) {
-    if constexpr (__is_same(T, Bf16In)) {
-        return as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
+__device__ __forceinline__ void unpack_raw(const typename RawOf<T>::type& r, float v[8]) {
+    if constexpr (__is_same(T, F32In)) {
+        v[0] = as_float(r[0].x); v[1] = as_float(r[0].y); v[2] = as_float(r[0].z); v[3] = as_float(r[0].w);
+        v[4] = as_float(r[1].x); v[5] = as_float(r[1].y); v[6] = as_float(r[1].z); v[7] = as_float(r[1].w);
     } else if constexpr (__is_same(T, F16In)) {
-        return h2f(reinterpret_cast<const uint16_t*>(x)[i]);
+        v[0] = h2f(r.x & 0xFFFF); v[1] = h2f(r.x >> 16);
+        v[2] = h2f(r.y & 0xFFFF); v[3] = h2f(r.y >> 16);
+        v[4] = h2f(r.z & 0xFFFF); v[5] = h2f(r.z >> 16);
+        v[6] = h2f(r.w & 0xFFFF); v[7] = h2f(r.w >> 16);
     } else {
-        return reinterpret_cast<const float*>(x)[i];
+        v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
+        v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+        v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
+        v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
     }
 }
 
@@ -116,18 +128,21 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
     const int64_t nwaves = (int64_t)gridDim.x * (kQThreads / kWave);
     const char* lds_bytes = reinterpret_cast<const char*>(lut_lds);
 
-    for (int64_t u0 = wave * kUnroll; u0 < nunits; u0 += nwaves * kUnroll) {
-        float v[kUnroll][8];
+    // Raw input of kUnroll units per lane; the batch after the current one is loaded
+    // before the current one is processed, so each wave keeps two batches in flight.
+    using Raw = typename RawOf<InT>::type;
+    Raw cur[kUnroll], nxt[kUnroll];
+    auto load_batch = [&](int64_t u0, Raw (&r)[kUnroll]) {
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            const int64_t base = (u0 + k) * kUnitElems + lane * 8;
-            if ((u0 + k + 1) * kUnitElems <= n) {
-                load8_full<InT>(x, base, v[k]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[k][i] = (base + i < n) ? load1<InT>(x, base + i) : 0.0f;
-            }
+            const int64_t unit = u0 + k < nunits ? u0 + k : nunits - 1;
+            load_raw<InT>(x, n, unit * kUnitElems + lane * 8, r[k]);
         }
+    };
+    auto process = [&](int64_t u0, const Raw (&raw)[kUnroll]) {
+        float v[kUnroll][8];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) unpack_raw<InT>(raw[k], v[k]);
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
             const int64_t unit = u0 + k;
@@ -195,6 +210,17 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
                 if (blk < nblocks) absmax[blk] = am;
             }
         }
+    };
+    // two batches in flight, the buffers alternating by name (a copy would wait for the load)
+    const int64_t stride = nwaves * kUnroll;
+    int64_t u0 = wave * kUnroll;
+    if (u0 < nunits) load_batch(u0, cur);
+    for (; u0 < nunits; u0 += 2 * stride) {
+        if (u0 + stride < nunits) load_batch(u0 + stride, nxt);
+        process(u0, cur);
+        if (u0 + stride >= nunits) break;
+        if (u0 + 2 * stride < nunits) load_batch(u0 + 2 * stride, cur);
+        process(u0 + stride, nxt);
     }
 }
 
@@ -218,7 +244,7 @@ hipError_t launch_typed(const void* x, int64_t n, const QuantLut& lut, uint8_t* 
     const int64_t nunits = (n + kUnitElems - 1) / kUnitElems;
     const int64_t waves_needed = (nunits + kUnroll - 1) / kUnroll;
     const int64_t wgs_needed = (waves_needed + (kQThreads / kWave) - 1) / (kQThreads / kWave);
-    const int64_t cap = (int64_t)num_cus() * 8;
+    const int64_t cap = (int64_t)num_cus() * kWgsPerCu;   // persistent: the LDS table is filled once per workgroup
     const int grid = (int)(wgs_needed < cap ? wgs_needed : cap);
     const size_t lds = (size_t)lut.nbins * kLutCopies * sizeof(uint2);
     if (lut.sorted)

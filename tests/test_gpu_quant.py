@@ -219,6 +219,38 @@ def test_ragged_sizes_and_guard_bands(n):
         assert np.all(yo[n:] == 12345.0), "dequant guard band overwritten"
 
 
+@pytest.mark.parametrize("offset", [0, 4, 8, 12])
+def test_dequant_codes_alignment(offset):
+    """Codes only need 4-byte alignment in a state; 16-byte aligned codes take the
+    vectorized kernel, others the per-element one.  Both must match the oracle."""
+    n = 3 * 2048 + 517
+    say(f"case: dequant codes offset {offset}, n={n}")
+    g = np.random.default_rng(77 + offset)
+    bits = ofl.f32_to_bf16_bits(g.standard_normal(n).astype(np.float32) * np.float32(0.02))
+    xf = bf16_bits_to_f32(bits)
+    lv = _levels(ocb.NF4)
+    B = 64
+    nbytes, nb = (n + 1) // 2, (n + B - 1) // B
+    codes_buf = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
+    codes = codes_buf[offset:offset + nbytes]
+    absmax = torch.empty(nb, dtype=torch.float32, device="cuda")
+    qk.qk_quantize_blockwise(dev_bf16(bits), B, torch.from_numpy(lv), codes, absmax)
+    want_c, want_a = obw.quantize_blockwise(xf, B, lv)
+    assert_bits_equal(host(codes), want_c, "codes")
+    st = qk.qk_state_init(qk.NF4, lv, 1, n, B, codes, absmax)
+    want_y = odq.dequantize_f32(want_c, n, B, lv, want_a)
+    out32 = torch.full((n + 64,), 999.0, dtype=torch.float32, device="cuda")
+    qk.qk_dequantize(st, torch.float32, out32[:n])
+    y = host(out32)
+    assert_bits_equal(y[:n], want_y, "fp32 dequant")
+    assert np.all(y[n:] == 999.0), "fp32 guard band overwritten"
+    out16 = torch.full((n + 64,), 7.0, dtype=torch.bfloat16, device="cuda")
+    qk.qk_dequantize(st, torch.bfloat16, out16[:n])
+    y16 = host(out16.view(torch.int16)).view(np.uint16)
+    assert_bits_equal(y16[:n], ofl.f32_to_bf16_bits(want_y), "bf16 dequant")
+    assert np.all(y16[n:] == 0x40E0), "bf16 guard band overwritten"
+
+
 def test_deterministic_repeat():
     W, _ = workloads.single_1024()
     xd = dev_bf16(W)
