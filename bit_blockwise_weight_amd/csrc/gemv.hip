@@ -5,24 +5,27 @@
 // QLoRA 降低 LLM 訓練門檻？", section on speed (unpacking and dequantizing must be
 // fused, or 4-bit can be slower than 16-bit).  The weight is never written out.
 //
-// Fast path (K a multiple of 64 and of the block size):
-//   * A workgroup owns a tile of 32 weight rows; its S waves split K in
-//     interleaved steps of 64 (wave w takes steps w, w+S, ...), so at any time
-//     the waves of a workgroup read neighbouring bytes of each row.
-//   * In a step, lane l (row j = l % 32 of the tile, half g = l / 32) loads the
-//     16 code bytes of weights [64s + 32g, 64s + 32g + 32) of its row: the two
-//     lanes of a row read one 32-byte run, and one step of a row lies inside one
-//     absmax block.
+// Fast path (K a multiple of 64 and of the block size, 16-byte aligned codes and x):
+//   * A workgroup owns 16 weight rows; its 8 waves split K in chunks of 512
+//     (wave w takes chunks w, w + 8, ...).
+//   * Codes are loaded so that one instruction fetches 256 contiguous bytes from
+//     each of 4 rows; each wave writes its chunk to its own LDS area (no barrier)
+//     and reads it back in MFMA layout.  In that area the 16-byte piece p of row r
+//     sits in slot 16 r + (p ^ r), so the 16 rows a fragment read touches fall in
+//     16 different bank groups.  The next chunk's codes, x and scales are loaded
+//     before the current chunk is computed.
+//   * v_mfma_f32_16x16x32_bf16 with A = x (16 x 32, rows m >= M are zero) and
+//     B = W^T (32 x 16 rows), so the 4 output registers of lane l are y[m][n] for
+//     m = 4(l / 16) + r, n = l % 16.  Lane l holds row n = l % 16 and, in 64-k block
+//     b, the 16 weights k = 64 b + 16 h + [0, 16), h = l / 16; the block's two MFMAs
+//     take k = 64 b + 16 h + 8 t + [0, 8), t = 0, 1, so both stay inside one block of
+//     64 and the row's block scale a' (fp32) multiplies the block's partial product:
+//     one FMA per output register per block, none per weight.
 //   * Decoding: an LDS table maps a code byte to the pair (bf16 level of the high
 //     nibble, bf16 level of the low nibble) as one dword, replicated 64 times and
-//     interleaved so that lane l reads copy l: the address (byte << 8 | 4l) is
-//     one v_perm, the read never conflicts.
-//   * Four v_mfma_f32_32x32x16_bf16 per step: B = the lane's 8 weights of that
-//     MFMA, A = x[i = l % 32][same 8 k] (rows i >= M are zero).  The step's
-//     32 x 32 partial is multiplied by the row's block scale a' (fp32) and added
-//     to the accumulator, so the scale costs one FMA per kept output register
-//     per step instead of one multiply per weight.
-//   * The S partial tiles are summed through LDS in a fixed order (deterministic).
+//     interleaved so that lane l reads copy l: the address (byte << 8 | 4l) is one
+//     v_perm, the read never conflicts.
+//   * The 8 waves' partial tiles are summed through LDS in a fixed order.
 // The levels are used as bf16 and the block scale is applied in fp32 after the
 // bf16 products; the result agrees with the fp64 product on the bf16-dequantized
 // weight within the documented tolerance.
@@ -30,6 +33,8 @@
 // Generic path (any K, blocks straddling rows): one wave per row, each lane walks
 // k = lane, lane + 64, ... and dequantizes each weight exactly as the dequantize
 // kernel does (bf16 of level * a'), with fp32 accumulation.
+#include <type_traits>
+
 #include "qk_internal.h"
 #include "qk_device.h"
 
@@ -39,7 +44,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRows = 32;          // rows per tile (MFMA 32x32)
 constexpr int kStep = 64;          // k per step
 constexpr int kTabCopies = 64;
 
@@ -57,83 +61,93 @@ __device__ __forceinline__ float row_scale(const DeqArgs& a, int64_t blk) {
     return __fadd_rn(__fmul_rn((float)a.q8[blk], a.dq_scale[blk / QK_DQ_BLOCK]), *a.dq_mean);
 }
 
-// Fill the byte -> (bf16 level hi nibble | bf16 level lo nibble << 16) table, 64 copies.
-__device__ __forceinline__ void fill_pair_table(uint32_t* tab, const float* levels, int nthreads) {
-    for (int i = threadIdx.x; i < 256 * kTabCopies; i += nthreads) {
-        const int b = i / kTabCopies;
-        tab[i] = pack_bf16x2(levels[b >> 4], levels[b & 15]);
-    }
-}
+// Fast path kernel (see the top of the file).
+constexpr int kChunkK = 512;                   // k per chunk (8 blocks of 64)
+constexpr int kChunkBlocks = kChunkK / 64;
 
-// Fast path, 16 weight rows per workgroup (v_mfma_f32_16x16x32_bf16):
-//   A = x (16 x 32, rows m >= M are zero), B = W^T (32 x 16 rows of the tile), so the
-//   4 x 16 output registers of a wave are y[m][n] for m = 4(lane / 16) + r, n = lane % 16.
-//   Lane l holds row n = l % 16 and, in 64-k block b, the 16 weights
-//   k = 64 b + 16 h + [0, 16), h = l / 16 (8 code bytes, one 8-byte load); the two MFMAs
-//   of a block use k = 64 b + 16 h + 8 t + [0, 8), t = 0, 1, so both stay inside one block
-//   of 64 and the block scale of row n multiplies the block's partial product.
-//   The S waves of a workgroup take blocks b = wave, wave + S, ... and load the codes,
-//   scales and x of kBatch blocks ahead, so each wave keeps several HBM loads in flight.
-constexpr int kBatch = 4;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-struct GemvBatch {
-    uint2 c[kBatch];      // 8 code bytes of the lane's row
-    uint4 x0[kBatch];     // x[m][64 b + 16 h + 0..7]
-    uint4 x1[kBatch];     // x[m][64 b + 16 h + 8..15]
-    int32_t q[kBatch];    // q8 (nested) or absmax bits
-    float d[kBatch];      // dq scale (nested)
+struct ChunkRegs {
+    u32x4_t c[4];                // 16-byte code pieces of this lane (4 rows x 256 bytes per wave load)
+    uint4 x[kChunkBlocks][2];    // x[m][c0 + 64 b + 16 h + 8 t .. +8], t = 0, 1
+    int32_t q[kChunkBlocks];     // q8 (nested) or absmax bits
+    float d[kChunkBlocks];       // dq scale (nested)
 };
 
-template <int S, bool kNested>
-__global__ __launch_bounds__(S * 64) void gemv16_kernel(GemvArgs a) {
-    extern __shared__ uint32_t lds[];          // 64 KB pair table, reused for the reduction
+template <bool kNested>
+__global__ __launch_bounds__(512) void gemv_lds_kernel(GemvArgs a) {
+    constexpr int S = 8;
+    __shared__ __attribute__((aligned(16))) uint32_t tab[256 * kTabCopies];   // 64 KB byte -> bf16 pair
+    __shared__ __attribute__((aligned(1024))) uint4 cb[S][256];               // codes chunk, 4 KB per wave
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;                   // weight row of the tile (and x row m of the A operand)
     const int h = lane >> 4;                   // 16-weight group of a 64-k block
-    const int64_t row = (int64_t)blockIdx.x * 16 + n;
-    const bool row_ok = row < a.N;
-    const int64_t rowc = row_ok ? row : a.N - 1;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t K = a.K;
     const int64_t nblk = K / 64;
-    const int64_t nbw = (nblk - wave + S - 1) / S;        // blocks of this wave
+    const int64_t nchunk = (K + kChunkK - 1) / kChunkK;
+    const int64_t ncw = (nchunk - wave + S - 1) / S;       // chunks of this wave
     const int M = a.M;
     const bool x_ok = n < M;
     const uint16_t* xrow = a.x + (int64_t)(x_ok ? n : 0) * K + 16 * h;
-    const uint8_t* crow = a.w.codes + rowc * (K / 2) + 8 * h;
+    const int64_t rowc = n0 + n < a.N ? n0 + n : a.N - 1;
     const int64_t qb0 = (rowc * K) >> a.w.blocksize_log2;  // first quantization block of the row
     const int bshift = a.w.blocksize_log2 - 6;
     const float mean = kNested ? *a.w.dq_mean : 0.0f;
+    const int64_t row_bytes = K / 2;
 
-    auto load = [&](int64_t i0, GemvBatch& bt) {
+    // code loads: load i, lane L fetches piece (L % 16) ^ r of row r = 4 i + L / 16
+    const uint8_t* csrc[4];
 #pragma unroll
-        for (int p = 0; p < kBatch; ++p) {
-            int64_t b = wave + (int64_t)S * (i0 + p);
-            b = b < nblk ? b : nblk - 1;
-            bt.c[p] = *reinterpret_cast<const uint2*>(crow + 32 * b);
-            const uint4* xp = reinterpret_cast<const uint4*>(xrow + 64 * b);
-            bt.x0[p] = xp[0];     // rows m >= M read row 0 and are zeroed at use
-            bt.x1[p] = xp[1];
-            const int64_t qb = qb0 + (b >> bshift);
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int64_t gr = n0 + r < a.N ? n0 + r : a.N - 1;
+        csrc[i] = a.w.codes + gr * row_bytes + 16 * ((lane & 15) ^ r);
+    }
+    auto load = [&](int64_t c, ChunkRegs& cr) {
+        const int64_t cc = c < nchunk ? c : nchunk - 1;
+        const int64_t cbase = cc * (kChunkK / 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // pieces past the end of a row (last, partial chunk) are clamped and never used
+            const int64_t off = cbase + 16 * ((lane & 15) ^ (4 * i + (lane >> 4)));
+            const int64_t adj = off + 16 <= row_bytes ? 0 : row_bytes - 16 - off;
+            cr.c[i] = *reinterpret_cast<const u32x4_t*>(csrc[i] + cbase + adj);
+        }
+#pragma unroll
+        for (int b = 0; b < kChunkBlocks; ++b) {
+            int64_t blk = cc * kChunkBlocks + b;
+            blk = blk < nblk ? blk : nblk - 1;
+            const uint4* xp = reinterpret_cast<const uint4*>(xrow + 64 * blk);
+            cr.x[b][0] = xp[0];     // rows m >= M read row 0 and are zeroed at use
+            cr.x[b][1] = xp[1];
+            const int64_t qb = qb0 + (blk >> bshift);
             if constexpr (kNested) {
-                bt.q[p] = (int32_t)a.w.q8[qb];
-                bt.d[p] = a.w.dq_scale[qb / QK_DQ_BLOCK];
+                cr.q[b] = (int32_t)a.w.q8[qb];
+                cr.d[b] = a.w.dq_scale[qb / QK_DQ_BLOCK];
             } else {
-                bt.q[p] = (int32_t)as_uint(a.w.absmax[qb]);
-                bt.d[p] = 0.0f;
+                cr.q[b] = (int32_t)as_uint(a.w.absmax[qb]);
+                cr.d[b] = 0.0f;
             }
         }
     };
-
-    const uint32_t lane_sel = (uint32_t)lane * 4u;
-    const char* tab = reinterpret_cast<const char*>(lds);
-    floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto compute = [&](const GemvBatch& bt, int64_t i0) {
+    u32x4_t* mine = reinterpret_cast<u32x4_t*>(cb[wave]);
+    auto stage = [&](const ChunkRegs& cr) {
 #pragma unroll
-        for (int p = 0; p < kBatch; ++p) {
-            const uint32_t cws[2] = {bt.c[p].x, bt.c[p].y};
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            const uint4 xs[2] = {x_ok ? bt.x0[p] : z, x_ok ? bt.x1[p] : z};
+        for (int i = 0; i < 4; ++i) mine[i * 64 + lane] = cr.c[i];    // slot 64 i + L = 16 r + (piece ^ r)
+    };
+
+    floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t lane_sel = (uint32_t)lane * 4u;
+    const char* tabb = reinterpret_cast<const char*>(tab);
+    const char* mb = reinterpret_cast<const char*>(mine);
+    auto compute = [&](int64_t c, const ChunkRegs& cr) {
+#pragma unroll
+        for (int b = 0; b < kChunkBlocks; ++b) {
+            const int piece = 2 * b + (h >> 1);
+            const uint2 cw = *reinterpret_cast<const uint2*>(mb + (16 * n + (piece ^ n)) * 16 + 8 * (h & 1));
+            const uint32_t cws[2] = {cw.x, cw.y};
             floatx4_t part = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -141,54 +155,61 @@ __global__ __launch_bounds__(S * 64) void gemv16_kernel(GemvArgs a) {
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
                     const uint32_t addr = __builtin_amdgcn_perm(cws[t], lane_sel, 0x0C0C0400u | ((uint32_t)(4 + bb) << 8));
-                    wv[bb] = *reinterpret_cast<const uint32_t*>(tab + addr);
+                    wv[bb] = *reinterpret_cast<const uint32_t*>(tabb + addr);
                 }
-                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xs[t]),
+                const uint4 z = make_uint4(0, 0, 0, 0);
+                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x_ok ? cr.x[b][t] : z),
                                                                __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3])),
                                                                part, 0, 0, 0);
             }
             float sc;
-            if constexpr (kNested) sc = __fadd_rn(__fmul_rn((float)bt.q[p], bt.d[p]), mean);
-            else sc = as_float((uint32_t)bt.q[p]);
-            const bool live = i0 + p < nbw;
+            if constexpr (kNested) sc = __fadd_rn(__fmul_rn((float)cr.q[b], cr.d[b]), mean);
+            else sc = as_float((uint32_t)cr.q[b]);
+            const bool live = c * kChunkBlocks + b < nblk;
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = live ? __builtin_fmaf(part[r], sc, acc[r]) : acc[r];
         }
     };
 
-    // two batches in flight: while one is decoded, the loads of the next are outstanding
-    GemvBatch ba, bb;
-    load(0, ba);
-    load(kBatch, bb);
-    __builtin_amdgcn_sched_barrier(0);
+    const int64_t c0 = wave;
+    ChunkRegs ra, rb;
+    if (ncw > 0) load(c0, ra);
     {
         // pair table, 64 copies: entry i = 64 b + copy for byte b.  With 8 waves, wave w
         // writes the bytes b = w + 8 j, whose nibbles are (j / 2, w + 8 (j % 2)); the level
-        // reads are uniform (scalar loads), so they do not wait for the batches in flight.
-        static_assert(S == 8, "table fill assumes 8 waves");
+        // reads are uniform (scalar loads), so they do not wait for the loads in flight.
         const int w = wave;
         const uint32_t lo0 = as_uint(a.w.levels[w]), lo1 = as_uint(a.w.levels[w + 8]);
 #pragma unroll
         for (int jj = 0; jj < 32; ++jj) {
             const float hi_nib = a.w.levels[jj >> 1];
-            lds[(w + 8 * jj) * kTabCopies + lane] = pack_bf16x2(hi_nib, as_float((jj & 1) ? lo1 : lo0));
+            tab[(w + 8 * jj) * kTabCopies + lane] = pack_bf16x2(hi_nib, as_float((jj & 1) ? lo1 : lo0));
         }
     }
-    __syncthreads();
-    for (int64_t i0 = 0; i0 < nbw; i0 += 2 * kBatch) {
-        compute(ba, i0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (i0 + 2 * kBatch < nbw) load(i0 + 2 * kBatch, ba);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(bb, i0 + kBatch);
-        __builtin_amdgcn_sched_barrier(0);
-        if (i0 + 3 * kBatch < nbw) load(i0 + 3 * kBatch, bb);
-        __builtin_amdgcn_sched_barrier(0);
+    // a bare barrier: __syncthreads() would add a fence that waits for the loads in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) (the table writes), vmcnt and expcnt untouched
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ncw > 0) stage(ra);
+    // two chunks per iteration, the register sets alternating by name (a copy would wait
+    // for its loads): load the next chunk, compute this one from LDS, then stage the next
+    for (int64_t i = 0; i < ncw; i += 2) {
+        const int64_t c = c0 + (int64_t)S * i;
+        const bool has1 = i + 1 < ncw, has2 = i + 2 < ncw;
+        if (has1) load(c + S, rb);
+        compute(c, ra);
+        if (has1) {
+            stage(rb);
+            if (has2) load(c + 2 * S, ra);
+            compute(c + S, rb);
+            if (has2) stage(ra);
+        }
     }
 
-    // reduce the S waves' tiles in a fixed order: red[wave][r][lane]
+    // reduce the S waves' tiles in a fixed order: red[wave][r][lane] (over the table)
     __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);
+    float* red = reinterpret_cast<float*>(tab);
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
     __syncthreads();
@@ -198,7 +219,7 @@ __global__ __launch_bounds__(S * 64) void gemv16_kernel(GemvArgs a) {
         const int r = m & 3, ln = nn + 16 * (m >> 2);
         float v = 0.0f;
         for (int w = 0; w < S; ++w) v += red[(w * 4 + r) * 64 + ln];
-        const int64_t on = (int64_t)blockIdx.x * 16 + nn;
+        const int64_t on = n0 + nn;
         if (on < a.N) a.y[(int64_t)m * a.N + on] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
     }
 }
@@ -236,14 +257,6 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
     }
 }
 
-template <int S, bool kNested>
-hipError_t launch16(const GemvArgs& a, hipStream_t s) {
-    const unsigned grid = (unsigned)((a.N + 15) / 16);
-    const size_t lds = 256 * kTabCopies * sizeof(uint32_t);   // 64 KB, >= S * 4 * 64 * 4
-    hipLaunchKernelGGL((gemv16_kernel<S, kNested>), dim3(grid), dim3(S * 64), lds, s, a);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_gemv(const void* x, int32_t M, const MatArgs& w, void* y, hipStream_t s, const char** variant) {
@@ -255,14 +268,17 @@ hipError_t launch_gemv(const void* x, int32_t M, const MatArgs& w, void* y, hipS
     a.K = w.K;
     a.M = M;
     const bool fast = (w.K % kStep) == 0 && (w.K % w.w.blocksize) == 0 &&
-                      (reinterpret_cast<uintptr_t>(x) % 16) == 0 && (reinterpret_cast<uintptr_t>(w.w.codes) % 8) == 0;
+                      (reinterpret_cast<uintptr_t>(x) % 16) == 0 && (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0;
     if (!fast) {
         *variant = "generic (per-element dequantization, one wave per row)";
         hipLaunchKernelGGL(gemv_generic_kernel, dim3((unsigned)((w.N + 3) / 4)), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    *variant = "mfma 16x16x32 bf16, 16 rows per workgroup, LDS byte-pair table, 8 waves split-K, 4-block prefetch";
-    return w.w.nested ? launch16<8, true>(a, s) : launch16<8, false>(a, s);
+    *variant = "mfma 16x16x32 bf16, 16 rows per workgroup, codes staged through LDS in 512-k chunks, 8 waves split-K";
+    const unsigned grid = (unsigned)((a.N + 15) / 16);
+    if (w.w.nested) hipLaunchKernelGGL((gemv_lds_kernel<true>), dim3(grid), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gemv_lds_kernel<false>), dim3(grid), dim3(512), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace qk
