@@ -355,7 +355,10 @@ def bench(args):
     traffic, tinfo = load_traffic("gemm")
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
             "frac": round(achieved * 1e12 / MFMA_BF16_FLOPS, 4), "traffic": traffic,
-            "kernel": "qk gemm_kernel (fused dequant + LoRA)", "us_per_launch": round(g["s"] / g["launches"] * 1e6, 2),
+            "kernel": "qk_gemm_nf4 call = lora_xa_kernel (s*X*A pre-pass) + gemm_fast_kernel (dequant-fused GEMM, "
+                      "LoRA epilogue)",
+            "traffic_kernel": "gemm_fast_kernel (FETCH_SIZE + WRITE_SIZE per dispatch, copy-calibrated)",
+            "us_per_launch": round(g["s"] / g["launches"] * 1e6, 2),
             "flops_per_launch": g["flops"] // g["launches"]}
 
     extra = {"ms_per_step_without_events": round(step_noev_s * 1e3, 3)}
