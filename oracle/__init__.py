@@ -29,6 +29,7 @@ blockwise     block absmax, normalisation, nearest level, packing (a2-a4)
 double_quant  mean-centred int8 quantization of the absmax array (a5)
 dequant       absmax reconstruction and dequantization to fp32 / bf16 (a6)
 matmul        Y = X·deq(W)^T + s·(X·A)·B in fp64 (a7, a8)
+merge         LoRA merge into the dequantized weight, and requantization
 floats        exact rounding helpers (Fraction -> fp32, fp32 -> bf16 RNE)
 memory        storage arithmetic (bytes of a quantized tensor, bits/param)
 
@@ -37,4 +38,4 @@ does not re-type its formula (closed forms, invariants, brute force, the
 values the pages print).  No function is "parity unpinned".
 """
 
-from . import floats, codebook, blockwise, double_quant, dequant, matmul, memory  # noqa: F401
+from . import floats, codebook, blockwise, double_quant, dequant, matmul, memory, merge  # noqa: F401
