@@ -194,6 +194,40 @@ def work_of(op, m, wl):
     raise KeyError(op)
 
 
+def merge_rate(torch, qk, wl, iters=5):
+    """qk_lora_merge over the layer set (r = 16) and the requantization of the
+    merged weights (quantize + double quant).  Algorithmic bytes of the merge:
+    the quantized state read and the bf16 result written."""
+    mats = wl["mats"]
+    outs = [torch.empty((m["N"], m["K"]), dtype=torch.bfloat16, device="cuda") for m in mats]
+    lv = wl["levels_c"]
+
+    def merge_all():
+        for m, o in zip(mats, outs):
+            A, Bm = wl["lora"][m["name"]]
+            qk.qk_lora_merge(m["state"], A, Bm, 2.0, o)
+
+    def requant_all():
+        for m, o in zip(mats, outs):
+            qk.qk_quantize_blockwise(o, 64, lv, m["codes"], m["absmax"])
+            qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])
+
+    res = {}
+    for name, fn in (("merge", merge_all), ("requantize", requant_all)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / iters * 1e3
+    nbytes = sum(bytes_state(m["N"] * m["K"]) + 2 * m["N"] * m["K"] for m in mats)
+    return {"merge_us_per_layer_set": round(res["merge"], 1), "merge_gb_per_s": round(nbytes / res["merge"] / 1e3, 1),
+            "requantize_us_per_layer_set": round(res["requantize"], 1), "rank": wl["r"]}
+
+
 def gemv_isolated(torch, qk, workloads, reps=6, iters=20):
     """GEMV M=1 over `reps` copies of the layer set (607 MB of NF4 state at 6),
     cycled so the 256 MB last-level cache cannot hold them; HBM rate."""
@@ -364,6 +398,8 @@ def bench(args):
     extra = {"ms_per_step_without_events": round(step_noev_s * 1e3, 3)}
     if not args.skip_isolated:
         extra["gemv_m1_isolated_607MB"] = gemv_isolated(torch, qk, workloads)
+
+    extra["lora_merge"] = merge_rate(torch, qk, wl)
 
     cpu = None
     if not args.skip_cpu:

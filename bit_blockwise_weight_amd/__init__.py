@@ -100,6 +100,7 @@ def lib():
         "qk_gemv_nf4": [vp, i32, st_p, vp, vp],
         "qk_gemm_nf4_workspace_size": [i64, i32, ctypes.POINTER(ctypes.c_size_t)],
         "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp, ctypes.c_size_t, vp],
+        "qk_lora_merge": [st_p, vp, vp, i32, f32, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -279,6 +280,26 @@ def qk_gemm_nf4(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: 
     return Y
 
 
+def qk_lora_merge(state: QuantState, A: torch.Tensor, B: torch.Tensor, lora_scale: float, out=None,
+                  device=None) -> torch.Tensor:
+    """bf16 W_new [N, K] = bf16(D + s * (A B)^T) of the quantized weight `state`,
+    A [K, r], B [r, N] (bf16)."""
+    _require_cuda(A, B)
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("A and B must be bf16")
+    K, r = A.shape
+    if B.shape[0] != r or B.shape[1] != state.rows or K != state.cols:
+        raise ValueError(f"shapes A {tuple(A.shape)}, B {tuple(B.shape)} do not match W [{state.rows}, {state.cols}]")
+    dev = A.device if device is None else device
+    if out is None:
+        out = torch.empty((state.rows, state.cols), dtype=torch.bfloat16, device=dev)
+    _require_cuda(out)
+    with _on(out.device):
+        _check(lib().qk_lora_merge(ctypes.byref(state), _ptr(A), _ptr(B), int(r), float(lora_scale), _ptr(out),
+                                   ctypes.c_void_p(_stream(out))))
+    return out
+
+
 class QuantizedWeight:
     """A weight W[N, K] quantized on the device: its buffers and its descriptor."""
 
@@ -298,6 +319,13 @@ class QuantizedWeight:
 
     def gemm(self, X, A=None, B=None, lora_scale=0.0, Y=None, workspace=None):
         return qk_gemm_nf4(X, self.state, A, B, lora_scale, Y, workspace)
+
+    def merge_lora(self, A, B, lora_scale, double_quant=True):
+        """Merges the adapter into the weight and quantizes the merged bf16 weight
+        again with the same codebook and block size.  Returns (W_new, QuantizedWeight)."""
+        w_new = qk_lora_merge(self.state, A, B, lora_scale)
+        levels = torch.tensor(list(self.state.levels), dtype=torch.float32)
+        return w_new, quantize(w_new, self.state.blocksize, self.state.codebook_kind, double_quant, levels)
 
 
 def quantize(w: torch.Tensor, blocksize: int = 64, kind: int = NF4, double_quant: bool = True,

@@ -26,7 +26,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqk.so")
 
-SOURCES = ["api.cpp", "codebook.cpp", "quantize.hip", "double_quant.hip", "dequantize.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "codebook.cpp", "quantize.hip", "double_quant.hip", "dequantize.hip", "gemv.hip", "gemm.hip",
+           "merge.hip"]
 
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -220,6 +220,22 @@ qk_status qk_dequantize(const qk_quant_state* st, void* out, int32_t out_dtype, 
                     "qk_dequantize");
 }
 
+qk_status qk_lora_merge(const qk_quant_state* st, const void* A, const void* B, int32_t r, float lora_scale,
+                        void* out, void* stream) {
+    const qk_status v = validate_state(st);
+    if (v != QK_OK) return v;
+    if (!A || !B || !out) return fail(QK_ERR_INVALID_ARG, "qk_lora_merge: NULL A, B or out");
+    if (r < 1 || r > 1024) return fail(QK_ERR_INVALID_ARG, "qk_lora_merge: rank must be in 1..1024 (got %d)", r);
+    if (!std::isfinite(lora_scale)) return fail(QK_ERR_INVALID_ARG, "qk_lora_merge: lora_scale is not finite");
+    if (!aligned(A, 2) || !aligned(B, 2) || !aligned(out, 2))
+        return fail(QK_ERR_INVALID_ARG, "qk_lora_merge: bf16 buffers must be 2-byte aligned");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    qk::MatArgs w{deq_args(st), st->rows, st->cols};
+    return launched(qk::launch_lora_merge(w, A, B, r, lora_scale, out, reinterpret_cast<hipStream_t>(stream)),
+                    "qk_lora_merge");
+}
+
 qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* y, void* stream) {
     const qk_status v = validate_state(st);
     if (v != QK_OK) return v;

@@ -86,4 +86,7 @@ hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A
                        int32_t r, float lora_scale, void* Y, void* workspace, hipStream_t s,
                        const char** variant);
 
+hipError_t launch_lora_merge(const MatArgs& w, const void* A, const void* B, int32_t r, float scale, void* out,
+                             hipStream_t s);
+
 }  // namespace qk

@@ -253,6 +253,26 @@ qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const 
                       const void* B, int32_t r, float lora_scale, void* Y, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * qk_lora_merge — device.  Merges a LoRA adapter into the dequantized weight,
+ * [DEQ] section 8 (merge: dequantize the 4-bit weight to BF16, add the LoRA
+ * product, W_new is BF16; requantize it with qk_quantize_blockwise when a
+ * 4-bit weight is wanted) and section 9 (the QLoRA life cycle):
+ *     D[n, k] = bf16( RN_fp32(levels[code] * a') )      (qk_dequantize's bf16 value)
+ *     P[n, k] = sum_{j = 0 .. r-1} B[j, n] * A[k, j]    (fp32, j increasing; the
+ *                                                        products of bf16 values are exact)
+ *     out[n, k] = bf16( RN_fp32( D + RN_fp32(lora_scale * P) ) )   (round to nearest even)
+ *   Bit-exact: the same inputs give the same bits on every call.
+ *   st: host pointer to a valid descriptor of W [N, K].
+ *   A:  device, [K, r] bf16 row-major.   B: device, [r, N] bf16 row-major.
+ *   r:  1..1024.   lora_scale: finite (alpha / r).
+ *   out: device, [N, K] bf16 row-major, written (2-byte aligned; 16-byte alignment
+ *     and K % 8 == 0 select the vectorized path).
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_HIP.
+ */
+qk_status qk_lora_merge(const qk_quant_state* st, const void* A, const void* B, int32_t r,
+                        float lora_scale, void* out, void* stream);
+
 /* Message for the calling thread's last failed call ("" if none).  The
  * string stays valid until the thread's next qk_* call. */
 const char* qk_last_error(void);

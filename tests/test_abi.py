@@ -144,6 +144,7 @@ def test_corrupted_descriptor_is_rejected_by_every_consumer(L, field, value):
     assert L.qk_dequantize(ctypes.byref(st), y, qk.QK_BF16, None) == qk.QK_ERR_BAD_STATE
     assert L.qk_gemv_nf4(FAKE, 1, ctypes.byref(st), y, None) == qk.QK_ERR_BAD_STATE
     assert L.qk_gemm_nf4(FAKE, 4, ctypes.byref(st), None, None, 0, 0.0, y, None, 0, None) == qk.QK_ERR_BAD_STATE
+    assert L.qk_lora_merge(ctypes.byref(st), FAKE, FAKE, 16, 2.0, y, None) == qk.QK_ERR_BAD_STATE
     assert "quant state" in qk.qk_last_error()
 
 
@@ -177,6 +178,20 @@ def test_consumer_argument_errors(L):
     assert "workspace" in qk.qk_last_error()
     out = ctypes.c_size_t()
     assert L.qk_gemm_nf4_workspace_size(8, 65, ctypes.byref(out)) == qk.QK_ERR_INVALID_ARG
+
+
+def test_lora_merge_argument_errors(L):
+    st = _state()
+    assert L.qk_lora_merge(ctypes.byref(st), None, FAKE, 16, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_lora_merge(ctypes.byref(st), FAKE, None, 16, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_lora_merge(ctypes.byref(st), FAKE, FAKE, 16, 2.0, None, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_lora_merge(ctypes.byref(st), FAKE, FAKE, 0, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_lora_merge(ctypes.byref(st), FAKE, FAKE, 1025, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert "rank" in qk.qk_last_error()
+    assert L.qk_lora_merge(ctypes.byref(st), FAKE, FAKE, 16, float("nan"), FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_lora_merge(ctypes.byref(st), FAKE, FAKE, 16, 2.0, ctypes.c_void_p(0x10001), None) \
+        == qk.QK_ERR_INVALID_ARG
+    assert L.qk_lora_merge(None, FAKE, FAKE, 16, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
 
 
 def test_missing_library_error_is_deferred(tmp_path, monkeypatch):

@@ -37,6 +37,7 @@ WORKLOAD_IDS = {
     "qlora_prefill": 3,
     "llama70b_stack": 4,
     "edge_3000x4099": 5,
+    "lora_merge": 6,
 }
 
 LLAMA7B_SHAPES = [
@@ -118,6 +119,15 @@ def edge_weight(N: int = 3000, K: int = 4099, zero_frac: float = 0.01, spike_fra
     for c in chunks:
         flat[c * 256:(c + 1) * 256] = 0.0
     return to_bf16_bits(w)
+
+
+def lora_merge_case(N: int, K: int, r: int, tag: int = 0):
+    """A frozen weight W [N, K] ~ N(0, 0.02) and a trained-looking adapter A [K, r],
+    B [r, N] ~ N(0, 0.01), all bf16 bit patterns."""
+    W = normal_bf16("lora_merge", (N, K), 0.02, tensor=TENSOR_W, extra=tag)
+    A = normal_bf16("lora_merge", (K, r), 0.01, tensor=TENSOR_A, extra=tag)
+    B = normal_bf16("lora_merge", (r, N), 0.01, tensor=TENSOR_B, extra=tag)
+    return W, A, B
 
 
 def edge_activations(M: int = 512, K: int = 4099) -> np.ndarray:
