@@ -30,6 +30,7 @@ double_quant  mean-centred int8 quantization of the absmax array (a5)
 dequant       absmax reconstruction and dequantization to fp32 / bf16 (a6)
 matmul        Y = X·deq(W)^T + s·(X·A)·B in fp64 (a7, a8)
 merge         LoRA merge into the dequantized weight, and requantization
+backward      gradients of the QLoRA layer for the input and the adapter
 floats        exact rounding helpers (Fraction -> fp32, fp32 -> bf16 RNE)
 memory        storage arithmetic (bytes of a quantized tensor, bits/param)
 
@@ -38,4 +39,4 @@ does not re-type its formula (closed forms, invariants, brute force, the
 values the pages print).  No function is "parity unpinned".
 """
 
-from . import floats, codebook, blockwise, double_quant, dequant, matmul, memory, merge  # noqa: F401
+from . import floats, codebook, blockwise, double_quant, dequant, matmul, memory, merge, backward  # noqa: F401
