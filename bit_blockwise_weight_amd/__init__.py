@@ -101,6 +101,8 @@ def lib():
         "qk_gemm_nf4_workspace_size": [i64, i32, ctypes.POINTER(ctypes.c_size_t)],
         "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp, ctypes.c_size_t, vp],
         "qk_lora_merge": [st_p, vp, vp, i32, f32, vp, vp],
+        "qk_qlora_backward_workspace_size": [i64, st_p, i32, ctypes.POINTER(ctypes.c_size_t)],
+        "qk_qlora_backward": [vp, i64, st_p, vp, vp, vp, i32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -300,6 +302,53 @@ def qk_lora_merge(state: QuantState, A: torch.Tensor, B: torch.Tensor, lora_scal
     return out
 
 
+def qk_qlora_backward_workspace_size(M: int, state: QuantState, r: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().qk_qlora_backward_workspace_size(int(M), ctypes.byref(state), int(r), ctypes.byref(out)))
+    return int(out.value)
+
+
+def qk_qlora_backward(dY: torch.Tensor, state: QuantState, X=None, A=None, B=None, lora_scale: float = 0.0,
+                      dX=None, dA=None, dB=None, workspace=None):
+    """Gradients of Y = X deq(W)^T + s (X A) B for the upstream gradient dY [M, N]
+    (bf16): dX bf16 [M, K] and, with an adapter (A [K, r], B [r, N], X [M, K],
+    all bf16), dA fp32 [K, r] and dB fp32 [r, N].  Returns (dX, dA, dB)."""
+    _require_cuda(dY, X, A, B)
+    if (A is None) != (B is None):
+        raise ValueError("give both LoRA A and B, or neither")
+    for name, t in (("dY", dY), ("X", X), ("A", A), ("B", B)):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16")
+    dY2 = dY.reshape(-1, state.rows)
+    M = dY2.shape[0]
+    dev = dY.device
+    r = 0
+    X2 = None
+    if A is not None:
+        if X is None:
+            raise ValueError("the adapter gradients need X")
+        r = A.shape[1]
+        X2 = X.reshape(-1, state.cols)
+        if X2.shape[0] != M or tuple(A.shape) != (state.cols, r) or tuple(B.shape) != (r, state.rows):
+            raise ValueError(f"shapes X {tuple(X.shape)}, A {tuple(A.shape)}, B {tuple(B.shape)} do not match "
+                             f"dY {tuple(dY.shape)} and W [{state.rows}, {state.cols}]")
+        if dA is None:
+            dA = torch.empty((state.cols, r), dtype=torch.float32, device=dev)
+        if dB is None:
+            dB = torch.empty((r, state.rows), dtype=torch.float32, device=dev)
+    if dX is None:
+        dX = torch.empty((M, state.cols), dtype=torch.bfloat16, device=dev)
+    need = qk_qlora_backward_workspace_size(M, state, r)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _require_cuda(dX, dA, dB, workspace)
+    with _on(dev):
+        _check(lib().qk_qlora_backward(_ptr(dY2), M, ctypes.byref(state), _ptr(X2), _ptr(A), _ptr(B), int(r),
+                                       float(lora_scale), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(workspace),
+                                       0 if workspace is None else workspace.numel(), ctypes.c_void_p(_stream(dY))))
+    return dX, dA, dB
+
+
 class QuantizedWeight:
     """A weight W[N, K] quantized on the device: its buffers and its descriptor."""
 
@@ -319,6 +368,9 @@ class QuantizedWeight:
 
     def gemm(self, X, A=None, B=None, lora_scale=0.0, Y=None, workspace=None):
         return qk_gemm_nf4(X, self.state, A, B, lora_scale, Y, workspace)
+
+    def backward(self, dY, X=None, A=None, B=None, lora_scale=0.0, workspace=None):
+        return qk_qlora_backward(dY, self.state, X, A, B, lora_scale, workspace=workspace)
 
     def merge_lora(self, A, B, lora_scale, double_quant=True):
         """Merges the adapter into the weight and quantizes the merged bf16 weight

@@ -236,6 +236,49 @@ qk_status qk_lora_merge(const qk_quant_state* st, const void* A, const void* B, 
                     "qk_lora_merge");
 }
 
+qk_status qk_qlora_backward_workspace_size(int64_t M, const qk_quant_state* st, int32_t r, size_t* bytes) {
+    if (!bytes) return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward_workspace_size: bytes is NULL");
+    const qk_status v = validate_state(st);
+    if (v != QK_OK) return v;
+    if (M < 1 || r < 0 || r > 64)
+        return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward_workspace_size: M >= 1, r in 0..64");
+    *bytes = qk::qlora_backward_workspace_bytes(M, st->rows, st->cols, r);
+    return ok();
+}
+
+qk_status qk_qlora_backward(const void* dY, int64_t M, const qk_quant_state* st, const void* X, const void* A,
+                            const void* B, int32_t r, float lora_scale, void* dX, float* dA, float* dB,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    const qk_status v = validate_state(st);
+    if (v != QK_OK) return v;
+    if (!dY || !dX) return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward: NULL dY or dX");
+    if (M < 1 || M > 65535LL * 128) return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward: M must be in 1..8388480");
+    if ((A == nullptr) != (B == nullptr))
+        return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward: give both LoRA A and B, or neither");
+    const bool lora = A != nullptr;
+    if (lora && (r < 1 || r > 64)) return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward: LoRA rank must be in 1..64");
+    if (lora && (!X || !dA || !dB)) return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward: LoRA needs X, dA and dB");
+    if (lora && !std::isfinite(lora_scale)) return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward: lora_scale is not finite");
+    if (st->rows % 64 != 0 || st->cols % 64 != 0)
+        return fail(QK_ERR_UNSUPPORTED, "qk_qlora_backward: W [%lld, %lld] needs both sizes multiples of 64",
+                    (long long)st->rows, (long long)st->cols);
+    if (!aligned(dY, 16) || !aligned(dX, 2) || (lora && (!aligned(X, 16) || !aligned(A, 2) || !aligned(B, 2) ||
+                                                         !aligned(dA, 4) || !aligned(dB, 4))))
+        return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward: dY and X must be 16-byte aligned, the others element-aligned");
+    const size_t need = qk::qlora_backward_workspace_bytes(M, st->rows, st->cols, lora ? r : 0);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(QK_ERR_WORKSPACE, "qk_qlora_backward: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 16))
+        return fail(QK_ERR_INVALID_ARG, "qk_qlora_backward: workspace must be 16-byte aligned");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    qk::MatArgs w{deq_args(st), st->rows, st->cols};
+    return launched(qk::launch_qlora_backward(dY, M, w, X, A, B, lora ? r : 0, lora_scale, dX, dA, dB, workspace,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                    "qk_qlora_backward");
+}
+
 qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* y, void* stream) {
     const qk_status v = validate_state(st);
     if (v != QK_OK) return v;

@@ -367,8 +367,8 @@ hipError_t launch_typed(const GemmArgs& a, hipStream_t s) {
 //   * the B fragments of the next quarter are dequantized while the 16 MFMAs of
 //     the current quarter run.
 // X rows are 128 bytes in LDS with the 16-byte chunks XOR-swizzled by the row
-// (chunk c of row r sits in slot c ^ (r & 7)), so the fragment reads of 8
-// consecutive rows hit 8 different bank groups.
+// (chunk c of row r sits in slot c ^ ((r >> 1) & 7)), so the fragment reads of
+// 16 consecutive rows hit 16 different bank groups (no LDS bank conflicts).
 // ---------------------------------------------------------------------------
 namespace v4 {
 
@@ -836,7 +836,32 @@ hipError_t launch_fast(const GemmArgs& a, void* workspace, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Ts[i] = T_0[i] + ... + T_{kSplits-1}[i], split order (the same order the GEMM uses).
+__global__ __launch_bounds__(256) void lora_split_sum_kernel(const float* __restrict__ T, int64_t n, float* __restrict__ Ts) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float acc = T[i];
+    for (int p = 1; p < v4::kSplits; ++p) acc += T[(int64_t)p * n + i];
+    Ts[i] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_lora_xa_sum(const void* X, int64_t M, int64_t K, const void* A, int32_t r, float lora_scale,
+                              float* T_splits, float* Ts, hipStream_t s) {
+    GemmArgs a{};
+    a.X = reinterpret_cast<const uint16_t*>(X);
+    a.A = reinterpret_cast<const uint16_t*>(A);
+    a.M = M;
+    a.K = K;
+    a.r = r;
+    a.lora_scale = lora_scale;
+    const int r16 = (r + 15) / 16;
+    launch_lora_xa(a, T_splits, s, r16);
+    const int64_t n = M * 16 * r16;
+    hipLaunchKernelGGL(lora_split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T_splits, n, Ts);
+    return hipGetLastError();
+}
 
 size_t gemm_workspace_bytes(int64_t M, int32_t r) {
     return r > 0 ? (size_t)v4::kSplits * (size_t)M * (size_t)(((r + 15) / 16) * 16) * sizeof(float) : 0;

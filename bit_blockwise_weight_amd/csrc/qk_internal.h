@@ -86,6 +86,14 @@ hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A
                        int32_t r, float lora_scale, void* Y, void* workspace, hipStream_t s,
                        const char** variant);
 
+// s * X * A in fp32 ([M, 16 * ceil(r / 16)], ranks >= r zero): K % 64 == 0, X 16-byte
+// aligned; T_splits holds the per-K-split partials (gemm_workspace_bytes(M, r) bytes).
+hipError_t launch_lora_xa_sum(const void* X, int64_t M, int64_t K, const void* A, int32_t r, float lora_scale,
+                              float* T_splits, float* Ts, hipStream_t s);
+size_t qlora_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
+hipError_t launch_qlora_backward(const void* dY, int64_t M, const MatArgs& w, const void* X, const void* A,
+                                 const void* B, int32_t r, float lora_scale, void* dX, float* dA, float* dB,
+                                 void* workspace, hipStream_t s);
 hipError_t launch_lora_merge(const MatArgs& w, const void* A, const void* B, int32_t r, float scale, void* out,
                              hipStream_t s);
 

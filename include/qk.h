@@ -273,6 +273,45 @@ qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const 
 qk_status qk_lora_merge(const qk_quant_state* st, const void* A, const void* B, int32_t r,
                         float lora_scale, void* out, void* stream);
 
+/*
+ * qk_qlora_backward_workspace_size — host.  Bytes of device workspace
+ * qk_qlora_backward needs for M token rows, the weight of `st` and LoRA rank r
+ * (0 when r == 0).
+ */
+qk_status qk_qlora_backward_workspace_size(int64_t M, const qk_quant_state* st, int32_t r,
+                                           size_t* bytes);
+
+/*
+ * qk_qlora_backward — device.  Backward of the layer qk_gemm_nf4 computes,
+ * Y = X · deq(W)^T + s · (X · A) · B, for an upstream gradient dY; the 4-bit
+ * base stays frozen and is dequantized tile by tile as in the forward ([YOLO]
+ * section "QLoRA 把 frozen 4-bit base 與可訓練 adapter 分開": dequantized in the
+ * forward and the backward pass; [DEQ] section 4: the INT4 base is frozen, only
+ * the BF16 A and B train; section 5: the base is restored to BF16 per layer):
+ *     G  = dY · B^T
+ *     dX = dY · deq(W) + s · G · A^T        (bf16)
+ *     dA = s · X^T · G                      (fp32)
+ *     dB = s · (X · A)^T · dY               (fp32)
+ *   Agreement with the fp64 reference: rel. Frobenius <= 5e-3 and max error
+ *   <= 2e-2 * max|ref| for each output.  Deterministic.
+ *   dY: device, [M, N] bf16 row-major (N = st->rows), 16-byte aligned.
+ *   X:  device, [M, K] bf16 row-major (K = st->cols), 16-byte aligned; needed
+ *       only with an adapter.
+ *   A, B: device, [K, r] and [r, N] bf16 row-major, or both NULL (dX only).
+ *   r: 1..64 with an adapter.   lora_scale: finite (alpha / r).
+ *   dX: device, [M, K] bf16, written.   dA: device, [K, r] fp32, written.
+ *   dB: device, [r, N] fp32, written (dA, dB ignored without an adapter).
+ *   workspace: device, >= qk_qlora_backward_workspace_size(M, st, r) bytes,
+ *     16-byte aligned (NULL allowed without an adapter).
+ *   N and K must be multiples of 64 (else QK_ERR_UNSUPPORTED).
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED,
+ *   QK_ERR_WORKSPACE, QK_ERR_HIP.
+ */
+qk_status qk_qlora_backward(const void* dY, int64_t M, const qk_quant_state* st, const void* X,
+                            const void* A, const void* B, int32_t r, float lora_scale, void* dX,
+                            float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Message for the calling thread's last failed call ("" if none).  The
  * string stays valid until the thread's next qk_* call. */
 const char* qk_last_error(void);

@@ -202,3 +202,37 @@ def test_missing_library_error_is_deferred(tmp_path, monkeypatch):
     with pytest.raises(qk.QKError) as ei:
         qk.qk_make_codebook(qk.NF4)
     assert "not built" in str(ei.value)
+
+
+def test_qlora_backward_argument_errors(L):
+    st = qk.QuantState()
+    assert L.qk_state_init(ctypes.byref(st), qk.NF4, _levels(), 128, 64, 64, FAKE, None, FAKE, FAKE, FAKE) == qk.QK_OK
+    ws = ctypes.c_size_t(0)
+    assert L.qk_qlora_backward_workspace_size(8, ctypes.byref(st), 16, ctypes.byref(ws)) == qk.QK_OK
+    need = ws.value
+    assert need > 0
+    assert L.qk_qlora_backward_workspace_size(8, ctypes.byref(st), 0, ctypes.byref(ws)) == qk.QK_OK and ws.value == 0
+    assert L.qk_qlora_backward_workspace_size(8, ctypes.byref(st), 65, ctypes.byref(ws)) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_qlora_backward_workspace_size(0, ctypes.byref(st), 16, ctypes.byref(ws)) == qk.QK_ERR_INVALID_ARG
+
+    def call(dY=FAKE, M=8, s=st, X=FAKE, A=FAKE, B=FAKE, r=16, scale=2.0, dX=FAKE, dA=FAKE, dB=FAKE, w=FAKE,
+             wb=need):
+        return L.qk_qlora_backward(dY, M, None if s is None else ctypes.byref(s), X, A, B, r, scale, dX, dA, dB,
+                                   w, wb, None)
+
+    assert call(dY=None) == qk.QK_ERR_INVALID_ARG
+    assert call(dX=None) == qk.QK_ERR_INVALID_ARG
+    assert call(M=0) == qk.QK_ERR_INVALID_ARG
+    assert call(B=None) == qk.QK_ERR_INVALID_ARG
+    assert call(r=65) == qk.QK_ERR_INVALID_ARG
+    assert "rank" in qk.qk_last_error()
+    assert call(X=None) == qk.QK_ERR_INVALID_ARG
+    assert call(dA=None) == qk.QK_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == qk.QK_ERR_INVALID_ARG
+    assert call(dY=ctypes.c_void_p(0x10008)) == qk.QK_ERR_INVALID_ARG          # not 16-byte aligned
+    assert call(wb=need - 1) == qk.QK_ERR_WORKSPACE
+    assert call(w=None) == qk.QK_ERR_WORKSPACE
+    assert call(s=None) == qk.QK_ERR_INVALID_ARG
+    small = _state()                                                            # W [4, 64]: N % 64 != 0
+    assert call(s=small) == qk.QK_ERR_UNSUPPORTED
+    assert "multiples of 64" in qk.qk_last_error()

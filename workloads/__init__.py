@@ -12,7 +12,8 @@ Recipes (one per workload; sizes are the ones the tests and the benchmark use):
                      activations [M, K] ~ N(0, 1), M in {1, 16}.
 * ``qlora_prefill``  X [4096, 4096] ~ N(0, 1); W [4096, 4096] and [11008, 4096]
                      ~ N(0, 0.02); LoRA A [4096, 16], B [16, N] ~ N(0, 0.01),
-                     alpha / r = 2.
+                     alpha / r = 2.  The backward adds an upstream gradient
+                     dY [4096, N] ~ N(0, 1).
 * ``llama70b_stack`` 8 layers of {4 x [8192, 8192], 2 x [28672, 8192],
                      [8192, 28672]} ~ N(0, 0.015), activations M in {1, 4, 8}.
 * ``edge_3000x4099`` W [3000, 4099] = Student-t(3) x 0.02 with 0.1% of the
@@ -51,7 +52,7 @@ LLAMA70B_LAYER_SHAPES = [
 ]
 LLAMA70B_LAYERS = 8
 
-TENSOR_W, TENSOR_X, TENSOR_A, TENSOR_B, TENSOR_MASK = 0, 1, 2, 3, 4
+TENSOR_W, TENSOR_X, TENSOR_A, TENSOR_B, TENSOR_MASK, TENSOR_DY = 0, 1, 2, 3, 4, 5
 
 
 def rng(workload: str, layer: int = 0, tensor: int = 0, extra: int = 0) -> np.random.Generator:
@@ -101,6 +102,11 @@ def qlora_prefill(N: int, M: int = 4096, K: int = 4096, r: int = 16):
 
 
 QLORA_ALPHA_OVER_R = 2.0
+
+
+def qlora_upstream_grad(N: int, M: int = 4096) -> np.ndarray:
+    """dY [M, N] ~ N(0, 1), the gradient arriving at the layer output."""
+    return normal_bf16("qlora_prefill", (M, N), 1.0, tensor=TENSOR_DY, extra=N)
 
 
 def edge_weight(N: int = 3000, K: int = 4099, zero_frac: float = 0.01, spike_frac: float = 0.001,
