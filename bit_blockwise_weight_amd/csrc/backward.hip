@@ -19,9 +19,8 @@
 // into LDS as W^T: thread t reads 8 rows x 4 columns of codes (4 nibbles per row),
 // computes bf16(RN(level * a')) exactly as qk_dequantize does, and writes each
 // column's 8 values (8 consecutive n) as one 16-byte LDS store.  The LoRA term:
-// G accumulates in the same n loop from the dY tile already in LDS (B tile staged
-// [rank][n]), s·G is split into bf16 hi + lo and multiplied by A^T in the epilogue;
-// the workgroups of the first column tile also write s·G (fp32) for dA.
+// s·G comes from a pre-pass (the MFMA kernel of the forward's s·X·A, run on dY
+// and B^T), is split into bf16 hi + lo in the epilogue and multiplied by A^T.
 // dA and dB are reductions over the M token rows with r outputs per column: a
 // VALU kernel takes 256 columns x one slice of rows per workgroup (fp32 FMAs, rows
 // in increasing order) and writes per-slice partials, which a second kernel adds
@@ -50,12 +49,10 @@ struct DxArgs {
     const uint16_t* dY;   // [M, N]
     DeqArgs w;            // W [N, K]
     const uint16_t* A;    // [K, r] or null
-    const uint16_t* B;    // [r, N] or null
     uint16_t* dX;         // [M, K]
-    float* Gs;            // [M, rpad]: s * dY B^T, written by the workgroups of column tile 0
+    const float* Gs;      // [M, rpad]: s * dY B^T (fp32, ranks >= r zero)
     int64_t M, N, K;
     int32_t r;
-    float s;
 };
 
 __device__ __forceinline__ float block_scale(const DeqArgs& a, int64_t blk) {
@@ -67,7 +64,6 @@ template <bool kLora>
 __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ys[2][BM * kStride];
     __shared__ __attribute__((aligned(16))) uint16_t wt[2][BN * kStride];
-    __shared__ __attribute__((aligned(16))) uint16_t bs[kLora ? kMaxRank * kStride : 8];
     __shared__ float lev[16];
 
     const int tid = threadIdx.x;
@@ -85,12 +81,10 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     const int rg = tid >> 5, kq = tid & 31;
     const int64_t wk = k0 + 4 * kq;
     const bool wk_ok = wk < K;               // K % 4 == 0: the 4 columns are all in range or all out
-    constexpr int kBPer = kLora ? kMaxRank * BK / kThreads : 1;   // 16
 
     uint4 yr[4];
     uint32_t cw[8];
     float sc[8];
-    uint16_t bg[kBPer];
     auto load_step = [&](int64_t st) {
         const int64_t n0 = st * BK;
 #pragma unroll
@@ -105,14 +99,6 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
             const int64_t e = (n0 + 8 * rg + i) * K + wk;       // even: 2 code bytes, one block
             cw[i] = wk_ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(a.w.codes + e / 2) : 0u;
             sc[i] = wk_ok ? block_scale(a.w, e >> a.w.blocksize_log2) : 0.0f;
-        }
-        if constexpr (kLora) {
-#pragma unroll
-            for (int v = 0; v < kBPer; ++v) {
-                const int e = tid + kThreads * v;
-                const int j = e / BK, nn = e % BK;
-                bg[v] = (j < a.r) ? a.B[(int64_t)j * N + n0 + nn] : (uint16_t)0;
-            }
         }
     };
     auto store_step = [&](int buf) {
@@ -135,13 +121,6 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
             }
             *reinterpret_cast<uint4*>(&wt[buf][(4 * kq + c) * kStride + 8 * rg]) = make_uint4(o[0], o[1], o[2], o[3]);
         }
-        if constexpr (kLora) {
-#pragma unroll
-            for (int v = 0; v < kBPer; ++v) {
-                const int e = tid + kThreads * v;
-                if (e < rpad * BK) bs[(e / BK) * kStride + (e % BK)] = bg[v];
-            }
-        }
     };
 
     floatx16_t acc[2][2];
@@ -151,14 +130,6 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    // G accumulators: this wave owns G rows [32 wave, +32) as 2 x (rpad / 16) 16x16 tiles
-    floatx4_t gacc[2][kMaxRank / 16];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < kMaxRank / 16; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gacc[i][j][e] = 0.0f;
 
     __syncthreads();   // lev ready
     load_step(0);
@@ -187,25 +158,6 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if constexpr (kLora) {
-            // G[32 wave + 16 i + (l % 16)][16 j + ..] += dY[..][n] B[j][n], 16x16x32 tiles
-            const int l16 = lane & 15, q4 = lane >> 4;
-#pragma unroll
-            for (int kk = 0; kk < BK; kk += 32) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const bf16x8_t ya =
-                        *reinterpret_cast<const bf16x8_t*>(&yb[(wave * 32 + i * 16 + l16) * kStride + kk + 8 * q4]);
-#pragma unroll
-                    for (int j = 0; j < kMaxRank / 16; ++j) {
-                        if (16 * j >= rpad) break;
-                        const bf16x8_t bb =
-                            *reinterpret_cast<const bf16x8_t*>(&bs[(16 * j + l16) * kStride + kk + 8 * q4]);
-                        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, bb, gacc[i][j], 0, 0, 0);
-                    }
-                }
-            }
-        }
         __syncthreads();
         if (st + 1 < nsteps) {
             store_step(buf ^ 1);
@@ -214,29 +166,16 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     }
 
     if constexpr (kLora) {
-        // s*G -> LDS as bf16 hi / lo in ys[0] / ys[1] (and fp32 to Gs from column tile 0)
+        // s*G rows of this tile -> LDS as bf16 hi / lo in ys[0] / ys[1] (hi + lo = s*G to 2^-16)
         uint16_t* ghi = ys[0];
         uint16_t* glo = ys[1];
-        const int l16 = lane & 15, q4 = lane >> 4;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int j = 0; j < kMaxRank / 16; ++j) {
-                if (16 * j >= rpad) break;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // 16x16 output: lane holds C[4 (l / 16) + e][l % 16]
-                    const int row = wave * 32 + i * 16 + 4 * q4 + e;
-                    const int col = 16 * j + l16;
-                    const float v = gacc[i][j][e] * a.s;
-                    const uint32_t hb = pack_bf16x2(v, 0.0f) & 0xFFFFu;
-                    const float h = as_float(hb << 16);
-                    const uint32_t lb = pack_bf16x2(v - h, 0.0f) & 0xFFFFu;
-                    ghi[row * kStride + col] = (uint16_t)hb;
-                    glo[row * kStride + col] = (uint16_t)lb;
-                    if (blockIdx.x == 0 && m0 + row < M) a.Gs[(m0 + row) * rpad + col] = v;
-                }
-            }
+        for (int e = tid; e < BM * rpad; e += kThreads) {
+            const int row = e / rpad, col = e % rpad;
+            const float v = m0 + row < M ? a.Gs[(m0 + row) * rpad + col] : 0.0f;
+            const uint32_t hb = pack_bf16x2(v, 0.0f) & 0xFFFFu;
+            const float h = as_float(hb << 16);
+            ghi[row * kStride + col] = (uint16_t)hb;
+            glo[row * kStride + col] = (uint16_t)(pack_bf16x2(v - h, 0.0f) & 0xFFFFu);
         }
         // A^T tile: wt[0][col][j] = A[k0 + col][j]
         for (int e = tid; e < BN * rpad; e += kThreads) {
@@ -350,12 +289,24 @@ hipError_t launch_tn(const uint16_t* P, int64_t L, const float* Q, int64_t M, in
 
 }  // namespace
 
+// B [r, N] -> Bt [N, r] (bf16), so that s dY B^T has the layout of the forward's s X A.
+__global__ __launch_bounds__(256) void transpose_b_kernel(const uint16_t* __restrict__ B, int64_t N, int32_t r,
+                                                          uint16_t* __restrict__ Bt) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= N * r) return;
+    const int64_t n = e / r;
+    const int j = (int)(e % r);
+    Bt[e] = B[(int64_t)j * N + n];
+}
+
 // workspace: T splits [8][M][rpad] | Ts [M][rpad] | Gs [M][rpad] | partials [kSlices][max(N, K)][rpad] (fp32)
+//            | Bt [N][r] (bf16)
 size_t qlora_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
     if (r <= 0) return 0;
     const size_t rpad = (size_t)((r + 15) / 16) * 16;
     const size_t L = (size_t)(N > K ? N : K);
-    return gemm_workspace_bytes(M, r) + 2 * (size_t)M * rpad * sizeof(float) + (size_t)kSlices * L * rpad * sizeof(float);
+    return gemm_workspace_bytes(M, r) + 2 * (size_t)M * rpad * sizeof(float) +
+           (size_t)kSlices * L * rpad * sizeof(float) + (size_t)N * rpad * sizeof(uint16_t);
 }
 
 hipError_t launch_qlora_backward(const void* dY, int64_t M, const MatArgs& w, const void* X, const void* A,
@@ -369,25 +320,34 @@ hipError_t launch_qlora_backward(const void* dY, int64_t M, const MatArgs& w, co
     float* Ts = lora ? reinterpret_cast<float*>(ws + gemm_workspace_bytes(M, r)) : nullptr;
     float* Gs = lora ? Ts + (size_t)M * rpad : nullptr;
     float* part = lora ? Gs + (size_t)M * rpad : nullptr;
+    uint16_t* Bt = lora ? reinterpret_cast<uint16_t*>(part + (size_t)kSlices * (N > K ? N : K) * rpad) : nullptr;
+    hipError_t e = hipSuccess;
+    if (lora) {
+        // s G = s dY B^T first: the dX epilogue and dA read it
+        hipLaunchKernelGGL(transpose_b_kernel, dim3((unsigned)((N * r + 255) / 256)), dim3(256), 0, s,
+                           reinterpret_cast<const uint16_t*>(B), N, r, Bt);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_lora_xa_sum(dY, M, N, Bt, r, lora_scale, Tsplit, Gs, s);
+        if (e != hipSuccess) return e;
+    }
 
     DxArgs a;
     a.dY = reinterpret_cast<const uint16_t*>(dY);
     a.w = w.w;
     a.A = reinterpret_cast<const uint16_t*>(A);
-    a.B = reinterpret_cast<const uint16_t*>(B);
     a.dX = reinterpret_cast<uint16_t*>(dX);
     a.Gs = Gs;
     a.M = M;
     a.N = N;
     a.K = K;
     a.r = lora ? r : 0;
-    a.s = lora_scale;
     const int64_t gy = (M + BM - 1) / BM;
     if (gy > 65535) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((K + BN - 1) / BN), (unsigned)gy);
     if (lora) hipLaunchKernelGGL(dx_kernel<true>, grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(dx_kernel<false>, grid, dim3(kThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess || !lora) return e;
     // dA = X^T (s G): columns l = k of X
     e = launch_tn(reinterpret_cast<const uint16_t*>(X), K, Gs, M, r, part, dA, false, s);
