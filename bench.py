@@ -228,6 +228,51 @@ def merge_rate(torch, qk, wl, iters=5):
             "requantize_us_per_layer_set": round(res["requantize"], 1), "rank": wl["r"]}
 
 
+def backward_rate(torch, qk, wl, iters=5):
+    """qk_qlora_backward (dX, dA, dB for the upstream gradient dY [M, N]) over the
+    layer set, M = 4096, r = 16.  FLOPs: 2MNK for dX plus the LoRA products
+    (2MNr + 2MrK for dX's term, 2MKr for dA, 2MKr + 2MrN for dB)."""
+    mats = wl["mats"]
+    M, r = wl["M"], wl["r"]
+    dys, dxs, das, dbs = {}, {}, [], []
+    for m in mats:
+        if m["N"] not in dys:
+            dys[m["N"]] = torch.randn((M, m["N"]), device="cuda").to(torch.bfloat16)
+        if m["K"] not in dxs:
+            dxs[m["K"]] = torch.empty((M, m["K"]), dtype=torch.bfloat16, device="cuda")
+        das.append(torch.empty((m["K"], r), dtype=torch.float32, device="cuda"))
+        dbs.append(torch.empty((r, m["N"]), dtype=torch.float32, device="cuda"))
+    ws = torch.empty(max(qk.qk_qlora_backward_workspace_size(M, m["state"], r) for m in mats), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(lora):
+        for m, dA, dB in zip(mats, das, dbs):
+            X = wl["acts"][m["K"]]["X"]
+            if lora:
+                A, Bm = wl["lora"][m["name"]]
+                qk.qk_qlora_backward(dys[m["N"]], m["state"], X, A, Bm, 2.0, dxs[m["K"]], dA, dB, ws)
+            else:
+                qk.qk_qlora_backward(dys[m["N"]], m["state"], dX=dxs[m["K"]])
+
+    res = {}
+    for lora in (False, True):
+        run(lora)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            run(lora)
+        e1.record()
+        torch.cuda.synchronize()
+        res[lora] = e0.elapsed_time(e1) / iters * 1e-3
+    f_base = sum(2 * M * m["N"] * m["K"] for m in mats)
+    f_lora = f_base + sum(2 * M * r * (2 * m["N"] + 3 * m["K"]) for m in mats)
+    return {"dx_only_us_per_layer_set": round(res[False] * 1e6, 1),
+            "dx_only_tflop_per_s": round(f_base / res[False] / 1e12, 1),
+            "with_lora_us_per_layer_set": round(res[True] * 1e6, 1),
+            "with_lora_tflop_per_s": round(f_lora / res[True] / 1e12, 1), "M": M, "rank": r}
+
+
 def gemv_isolated(torch, qk, workloads, reps=6, iters=20):
     """GEMV M=1 over `reps` copies of the layer set (607 MB of NF4 state at 6),
     cycled so the 256 MB last-level cache cannot hold them; HBM rate."""
@@ -400,6 +445,7 @@ def bench(args):
         extra["gemv_m1_isolated_607MB"] = gemv_isolated(torch, qk, workloads)
 
     extra["lora_merge"] = merge_rate(torch, qk, wl)
+    extra["qlora_backward"] = backward_rate(torch, qk, wl)
 
     cpu = None
     if not args.skip_cpu:
