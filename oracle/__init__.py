@@ -10,7 +10,8 @@ Everything here is plain, slow and written to be checked by eye against the
 pages it follows:
 
 * "篇2-bitsandbytes-具体观-算法与实现剖析" (xyzblog), §2.2 QLoRA / NF4 and
-  figure 2-2 (the quantization pipeline and the nested quant_state);
+  figure 2-2 (the quantization pipeline and the nested quant_state), §2.3 and
+  figure 2-3 (8-bit blockwise states with the dynamic map);
 * "Tim Dettmers 如何用 bitsandbytes 與 QLoRA 降低 LLM 訓練門檻？" (yololab),
   the sections on NF4, double quantization and QLoRA;
 * "bitsandbytes：让大语言模型在消费级硬件上运行的量化神器" (zingnex), the
@@ -31,6 +32,7 @@ dequant       absmax reconstruction and dequantization to fp32 / bf16 (a6)
 matmul        Y = X·deq(W)^T + s·(X·A)·B in fp64 (a7, a8)
 merge         LoRA merge into the dequantized weight, and requantization
 backward      gradients of the QLoRA layer for the input and the adapter
+blockwise8    8-bit blockwise quantization with the dynamic (quantile) map
 floats        exact rounding helpers (Fraction -> fp32, fp32 -> bf16 RNE)
 memory        storage arithmetic (bytes of a quantized tensor, bits/param)
 
@@ -39,4 +41,4 @@ does not re-type its formula (closed forms, invariants, brute force, the
 values the pages print).  No function is "parity unpinned".
 """
 
-from . import floats, codebook, blockwise, double_quant, dequant, matmul, memory, merge, backward  # noqa: F401
+from . import floats, codebook, blockwise, double_quant, dequant, matmul, memory, merge, backward, blockwise8  # noqa: F401
