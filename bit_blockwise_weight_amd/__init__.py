@@ -103,6 +103,9 @@ def lib():
         "qk_lora_merge": [st_p, vp, vp, i32, f32, vp, vp],
         "qk_qlora_backward_workspace_size": [i64, st_p, i32, ctypes.POINTER(ctypes.c_size_t)],
         "qk_qlora_backward": [vp, i64, st_p, vp, vp, vp, i32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "qk_make_dynamic_map": [i32, ctypes.POINTER(ctypes.c_float)],
+        "qk_quantize_blockwise_8bit": [vp, i32, i64, i32, ctypes.POINTER(ctypes.c_float), vp, vp, vp],
+        "qk_dequantize_blockwise_8bit": [vp, vp, i64, i32, ctypes.POINTER(ctypes.c_float), vp, i32, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -144,15 +147,15 @@ def _require_cuda(*ts):
             raise ValueError("tensors passed to libqk must be contiguous")
 
 
-def _levels_arg(levels):
-    if isinstance(levels, ctypes.Array):      # already a float[16]
-        if len(levels) != 16:
-            raise ValueError("a level table has 16 entries")
+def _levels_arg(levels, count: int = 16):
+    if isinstance(levels, ctypes.Array):      # already a float[count]
+        if len(levels) != count:
+            raise ValueError(f"a level table has {count} entries")
         return levels, torch.tensor(list(levels), dtype=torch.float32)
     lv = torch.as_tensor(levels, dtype=torch.float32).detach().cpu().contiguous()
-    if lv.numel() != 16:
-        raise ValueError("a level table has 16 entries")
-    return (ctypes.c_float * 16)(*lv.tolist()), lv
+    if lv.numel() != count:
+        raise ValueError(f"a level table has {count} entries")
+    return (ctypes.c_float * count)(*lv.tolist()), lv
 
 
 def qk_last_error() -> str:
@@ -191,6 +194,54 @@ def qk_quantize_blockwise(x: torch.Tensor, blocksize: int = 64, levels=None, cod
         _check(lib().qk_quantize_blockwise(_ptr(x), _DTYPE_CODE[x.dtype], n, int(blocksize), lv, _ptr(codes),
                                            _ptr(absmax), ctypes.c_void_p(_stream(x))))
     return codes, absmax
+
+
+def qk_make_dynamic_map(signed: bool = True) -> torch.Tensor:
+    """The 256-level dynamic map (equal-mass quantiles of N(0,1), or of |N(0,1)|
+    when unsigned), float32 on the host."""
+    buf = (ctypes.c_float * 256)()
+    _check(lib().qk_make_dynamic_map(1 if signed else 0, buf))
+    return torch.tensor(list(buf), dtype=torch.float32)
+
+
+def qk_quantize_blockwise_8bit(x: torch.Tensor, blocksize: int = 2048, levels=None, codes=None, absmax=None):
+    """Returns (codes uint8[n], absmax fp32[ceil(n/B)]) on x's device; levels
+    defaults to the signed dynamic map."""
+    _require_cuda(x)
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported input dtype {x.dtype}")
+    n = x.numel()
+    if levels is None:
+        levels = qk_make_dynamic_map(True)
+    lv, _ = _levels_arg(levels, 256)
+    if codes is None:
+        codes = torch.empty(n, dtype=torch.uint8, device=x.device)
+    if absmax is None:
+        absmax = torch.empty((n + blocksize - 1) // blocksize, dtype=torch.float32, device=x.device)
+    _require_cuda(codes, absmax)
+    with _on(x.device):
+        _check(lib().qk_quantize_blockwise_8bit(_ptr(x), _DTYPE_CODE[x.dtype], n, int(blocksize), lv, _ptr(codes),
+                                                _ptr(absmax), ctypes.c_void_p(_stream(x))))
+    return codes, absmax
+
+
+def qk_dequantize_blockwise_8bit(codes: torch.Tensor, absmax: torch.Tensor, blocksize: int = 2048, levels=None,
+                                 dtype=torch.float32, out=None, n=None) -> torch.Tensor:
+    """out[k] = RN(levels[codes[k]] * absmax[k // B]) as fp32 or bf16."""
+    _require_cuda(codes, absmax)
+    n = codes.numel() if n is None else int(n)
+    if levels is None:
+        levels = qk_make_dynamic_map(True)
+    lv, _ = _levels_arg(levels, 256)
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=codes.device)
+    _require_cuda(out)
+    with _on(codes.device):
+        _check(lib().qk_dequantize_blockwise_8bit(_ptr(codes), _ptr(absmax), n, int(blocksize), lv, _ptr(out),
+                                                  _DTYPE_CODE[out.dtype], ctypes.c_void_p(_stream(codes))))
+    return out
 
 
 def qk_double_quant_workspace_size(nblocks: int) -> int:

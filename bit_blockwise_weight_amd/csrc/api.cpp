@@ -148,6 +148,61 @@ qk_status qk_quantize_blockwise(const void* x, int32_t x_dtype, int64_t n, int32
                     "qk_quantize_blockwise");
 }
 
+qk_status qk_make_dynamic_map(int32_t is_signed, float* levels_out) {
+    if (!levels_out) return fail(QK_ERR_INVALID_ARG, "qk_make_dynamic_map: levels_out is NULL");
+    qk::make_dynamic_map(is_signed != 0 ? 1 : 0, levels_out);
+    return ok();
+}
+
+namespace {
+bool valid_blocksize8(int32_t b) { return b == 256 || b == 512 || b == 1024 || b == 2048 || b == 4096; }
+}  // namespace
+
+qk_status qk_quantize_blockwise_8bit(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize,
+                                     const float* levels, uint8_t* codes, float* absmax, void* stream) {
+    if (!x || !levels || !codes || !absmax)
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise_8bit: NULL pointer argument");
+    if (n < 1) return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise_8bit: n must be >= 1 (got %lld)", (long long)n);
+    if (x_dtype != QK_BF16 && x_dtype != QK_F16 && x_dtype != QK_F32)
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise_8bit: unknown x dtype %d", x_dtype);
+    if (!valid_blocksize8(blocksize))
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise_8bit: block size %d (expected 256, 512, 1024, 2048 or 4096)",
+                    blocksize);
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(absmax, 4))
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise_8bit: x must be 16-byte aligned, codes 8-byte, absmax 4-byte");
+    qk::QuantLut8 lut;
+    const char* why = "";
+    const qk_status lst = qk::build_quant_lut8(levels, &lut, &why);
+    if (lst != QK_OK) return fail(lst, "qk_quantize_blockwise_8bit: %s", why);
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_quantize8(x, x_dtype, n, blocksize, lut, codes, absmax,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                    "qk_quantize_blockwise_8bit");
+}
+
+qk_status qk_dequantize_blockwise_8bit(const uint8_t* codes, const float* absmax, int64_t n, int32_t blocksize,
+                                       const float* levels, void* out, int32_t out_dtype, void* stream) {
+    if (!codes || !absmax || !levels || !out)
+        return fail(QK_ERR_INVALID_ARG, "qk_dequantize_blockwise_8bit: NULL pointer argument");
+    if (n < 1) return fail(QK_ERR_INVALID_ARG, "qk_dequantize_blockwise_8bit: n must be >= 1 (got %lld)", (long long)n);
+    if (!valid_blocksize8(blocksize))
+        return fail(QK_ERR_INVALID_ARG, "qk_dequantize_blockwise_8bit: block size %d (expected 256, 512, 1024, 2048 or 4096)",
+                    blocksize);
+    if (out_dtype != QK_F32 && out_dtype != QK_BF16)
+        return fail(QK_ERR_INVALID_ARG, "qk_dequantize_blockwise_8bit: out dtype %d (expected QK_F32 or QK_BF16)", out_dtype);
+    for (int i = 0; i < 256; ++i)
+        if (!std::isfinite(levels[i]))
+            return fail(QK_ERR_INVALID_ARG, "qk_dequantize_blockwise_8bit: levels[%d] is not finite", i);
+    if (!aligned(codes, 8) || !aligned(absmax, 4) || !aligned(out, 16))
+        return fail(QK_ERR_INVALID_ARG, "qk_dequantize_blockwise_8bit: codes must be 8-byte aligned, out 16-byte, absmax 4-byte");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_dequantize8(codes, absmax, n, blocksize, levels, out, out_dtype,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    "qk_dequantize_blockwise_8bit");
+}
+
 qk_status qk_double_quant_workspace_size(int64_t nblocks, size_t* bytes) {
     if (!bytes) return fail(QK_ERR_INVALID_ARG, "qk_double_quant_workspace_size: bytes is NULL");
     if (nblocks < 1) return fail(QK_ERR_INVALID_ARG, "qk_double_quant_workspace_size: nblocks must be >= 1");

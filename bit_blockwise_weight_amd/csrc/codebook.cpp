@@ -85,6 +85,21 @@ qk_status make_fp4(float out[16]) {
     return QK_OK;
 }
 
+qk_status make_dynamic_map(int32_t is_signed, float out[256]) {
+    // "篇2-bitsandbytes-具体观-算法与实现剖析", §2.3 8-bit Optimizers, 【原理】: 256
+    // non-uniform levels shaped by the distribution, dense at zero, sparse in the
+    // tails, maximising the code entropy.  Equal probability mass per level:
+    // signed   q_i = Phi^-1((2i + 1) / 512)
+    // unsigned q_i = Phi^-1(1/2 + (2i + 1) / 1024)   (the half-normal)
+    double q[256];
+    for (int i = 0; i < 256; ++i)
+        q[i] = is_signed ? normal_quantile((2.0 * i + 1.0) / 512.0) : normal_quantile(0.5 + (2.0 * i + 1.0) / 1024.0);
+    for (int i = 0; i < 256; ++i) out[i] = (float)(q[i] / q[255]);
+    if (is_signed) out[0] = -1.0f;   // q_0 = -q_255 by symmetry of the quantile
+    out[255] = 1.0f;
+    return QK_OK;
+}
+
 namespace {
 
 // bin index computed exactly as the kernel does: low 24 bits of fmaf(t, S, S + 2^23)
@@ -197,6 +212,84 @@ qk_status build_quant_lut(const float levels[16], QuantLut* lut, const char** wh
                 lut->c[bi] = sorted ? (uint32_t)clo : ((uint32_t)clo | ((uint32_t)clo << 16));
             }
         }
+        return QK_OK;
+    }
+    *why = "level thresholds are too close together for the lookup table";
+    return QK_ERR_UNSUPPORTED;
+}
+
+namespace {
+
+// Distinct values of a level table in increasing order, the smallest code carrying
+// each, and the binary32 decision threshold between neighbours (the least t that
+// maps to the upper value, the tie rule "smaller code wins" included).
+qk_status sorted_thresholds(const float* levels, int nlev, std::vector<float>& u, std::vector<int>& code_of,
+                            std::vector<float>& T, const char** why) {
+    for (int i = 0; i < nlev; ++i) {
+        if (!std::isfinite(levels[i]) || levels[i] < -1.0f || levels[i] > 1.0f) {
+            *why = "levels must be finite and within [-1, 1]";
+            return QK_ERR_INVALID_ARG;
+        }
+    }
+    u.clear();
+    for (int i = 0; i < nlev; ++i) u.push_back(levels[i]);
+    std::sort(u.begin(), u.end());
+    u.erase(std::unique(u.begin(), u.end(), [](float a, float b) { return a == b; }), u.end());   // +0 == -0
+    const int U = (int)u.size();
+    code_of.assign(U, nlev);
+    for (int s = 0; s < U; ++s)
+        for (int i = 0; i < nlev; ++i)
+            if (levels[i] == u[s]) code_of[s] = std::min(code_of[s], i);
+    T.assign(U > 1 ? U - 1 : 0, 0.0f);
+    for (int s = 0; s + 1 < U; ++s) {
+        const double a = u[s], b = u[s + 1];
+        const double sum = a + b, bb = sum - a;
+        if (bb != b || (sum - bb) != a) {
+            *why = "a level midpoint is not exact in binary64";
+            return QK_ERR_UNSUPPORTED;
+        }
+        const double m = sum * 0.5;
+        const bool tie_goes_up = code_of[s + 1] < code_of[s];
+        float t = (float)m;
+        if (tie_goes_up) {
+            while ((double)t < m) t = next_up(t);
+            while ((double)next_down(t) >= m) t = next_down(t);
+        } else {
+            while ((double)t <= m) t = next_up(t);
+            while ((double)next_down(t) > m) t = next_down(t);
+        }
+        T[s] = t;
+    }
+    return QK_OK;
+}
+
+}  // namespace
+
+qk_status build_quant_lut8(const float levels[256], QuantLut8* lut, const char** why) {
+    std::vector<float> u, T;
+    std::vector<int> code_of;
+    const qk_status st = sorted_thresholds(levels, 256, u, code_of, T, why);
+    if (st != QK_OK) return st;
+    const int U = (int)u.size();
+    for (int S = 8; S <= kLut8MaxS; S *= 2) {
+        const float Sf = (float)S, Cf = (float)S + 8388608.0f;
+        // a threshold inside a bin (not at its first value) must be the only one there
+        bool ok = true;
+        uint32_t last_inside_bin = 0xFFFFFFFFu;
+        for (int s = 0; s + 1 < U && ok; ++s) {
+            const uint32_t bt = bin_of(T[s], Sf, Cf);
+            if (bin_of(next_down(T[s]), Sf, Cf) == bt) {
+                if (bt == last_inside_bin) ok = false;
+                last_inside_bin = bt;
+            }
+        }
+        if (!ok) continue;
+        lut->S = Sf;
+        lut->C = Cf;
+        lut->nbins = 2 * S + 1;
+        lut->nthr = U - 1;
+        for (int s = 0; s < 255; ++s) lut->T[s] = s < U - 1 ? T[s] : 2.0f;
+        for (int s = 0; s < 256; ++s) lut->code_of[s] = (uint8_t)code_of[std::min(s, U - 1)];
         return QK_OK;
     }
     *why = "level thresholds are too close together for the lookup table";

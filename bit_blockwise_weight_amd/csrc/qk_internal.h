@@ -40,6 +40,32 @@ struct QuantLut {
 // midpoint that is not exact in binary64, or thresholds too close for S <= 64).
 qk_status build_quant_lut(const float levels[16], QuantLut* lut, const char** why);
 
+// ---------------------------------------------------------------------------
+// 8-bit quantization (256 levels).  The same exact decision as above, but the
+// per-bin table (up to 2049 bins) is too large for kernel arguments: the host
+// passes the sorted thresholds and the code of each sorted value, validated to
+// put at most one threshold in any bin of width 1/S, and each workgroup builds
+// the bin table in LDS.  With S a power of two, bin(t) = round-half-even(t S + S),
+// so the least t of bin b is (b - S - 1/2) / S when b is even and the next binary32
+// value above it when b is odd.
+// ---------------------------------------------------------------------------
+constexpr int kLut8MaxS = 1024;
+constexpr int kLut8MaxBins = 2 * kLut8MaxS + 1;
+
+struct QuantLut8 {
+    float S;                 // bins per unit of t (power of two)
+    float C;                 // S + 2^23
+    int32_t nbins;           // 2S + 1
+    int32_t nthr;            // distinct level values - 1
+    float T[255];            // increasing: t >= T[s] puts t above the s-th smallest value
+    uint8_t code_of[256];    // smallest code carrying the s-th smallest value
+};
+
+qk_status build_quant_lut8(const float levels[256], QuantLut8* lut, const char** why);
+// Dynamic 8-bit map: 256 equal-mass quantiles of N(0, 1) (signed) or of |N(0, 1)|
+// (unsigned), divided by the largest.
+qk_status make_dynamic_map(int32_t is_signed, float out[256]);
+
 // Level tables.
 qk_status make_nf4(float out[16]);
 qk_status make_fp4(float out[16]);
@@ -55,6 +81,11 @@ int device_cu_count();
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize,
                            const QuantLut& lut, uint8_t* codes, float* absmax, hipStream_t s);
+
+hipError_t launch_quantize8(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize, const QuantLut8& lut,
+                            uint8_t* codes, float* absmax, hipStream_t s);
+hipError_t launch_dequantize8(const uint8_t* codes, const float* absmax, int64_t n, int32_t blocksize,
+                              const float levels[256], void* out, int32_t out_dtype, hipStream_t s);
 
 size_t dq_workspace_bytes(int64_t nblocks);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int8_t* q8, float* scale,

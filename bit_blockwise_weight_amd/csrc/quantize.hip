@@ -31,6 +31,7 @@
 // the random bin indexes of a wave never collide in a bank.
 #include "qk_internal.h"
 #include "qk_device.h"
+#include "qk_quant_io.h"
 
 namespace qk {
 namespace {
@@ -44,63 +45,6 @@ constexpr int kUnitElems = kWave * 8;
 constexpr float kAMin = 0x1p-36f;
 constexpr float kAMax = 0x1p64f;
 constexpr float kXRel = 0x1p-64f;
-
-struct Bf16In {};
-struct F16In {};
-struct F32In {};
-
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
-// Raw 8-element input of one lane: one 16-byte word for 16-bit types, two for fp32.
-// A lane whose 8 elements run past n loads them one by one (zeros past n).
-template <typename T> struct RawOf { typedef uint4 type; };
-template <> struct RawOf<F32In> { typedef uint4 type[2]; };
-
-template <typename T>
-__device__ __forceinline__ void load_raw(const void* x, int64_t n, int64_t base, typename RawOf<T>::type& r) {
-    if constexpr (__is_same(T, F32In)) {
-        if (base + 8 <= n) {
-            const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + base);
-            r[0] = p[0];
-            r[1] = p[1];
-        } else {
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w[i] = (base + i < n) ? as_uint(reinterpret_cast<const float*>(x)[base + i]) : 0u;
-            r[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            r[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        }
-    } else {
-        if (base + 8 <= n) {
-            r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
-        } else {
-            uint32_t h[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[i] = (base + i < n) ? (uint32_t)reinterpret_cast<const uint16_t*>(x)[base + i] : 0u;
-            r = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-        }
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void unpack_raw(const typename RawOf<T>::type& r, float v[8]) {
-    if constexpr (__is_same(T, F32In)) {
-        v[0] = as_float(r[0].x); v[1] = as_float(r[0].y); v[2] = as_float(r[0].z); v[3] = as_float(r[0].w);
-        v[4] = as_float(r[1].x); v[5] = as_float(r[1].y); v[6] = as_float(r[1].z); v[7] = as_float(r[1].w);
-    } else if constexpr (__is_same(T, F16In)) {
-        v[0] = h2f(r.x & 0xFFFF); v[1] = h2f(r.x >> 16);
-        v[2] = h2f(r.y & 0xFFFF); v[3] = h2f(r.y >> 16);
-        v[4] = h2f(r.z & 0xFFFF); v[5] = h2f(r.z >> 16);
-        v[6] = h2f(r.w & 0xFFFF); v[7] = h2f(r.w >> 16);
-    } else {
-        v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
-        v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
-        v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
-        v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
-    }
-}
 
 template <typename InT, int B, bool kSorted>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restrict__ x, int64_t n,

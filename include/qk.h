@@ -20,6 +20,11 @@
  *          the 4-bit base is restored to BF16 layer by layer right before its
  *          matmul; section 2-2 LoRA and section 8 (merge / no-merge): the
  *          layer output is the base output plus the LoRA output X·A·B.
+ *  [OPT8]  "篇2-bitsandbytes-具体观-算法与实现剖析", §2.3 8-bit Optimizers,
+ *          【原理】 and figure 2-3: optimizer states in blocks of 2048, one local
+ *          absmax per block, 8-bit codes through a dynamic map of 256
+ *          non-uniform levels (dense at zero, sparse in the tails, maximising the
+ *          code entropy; signed "dynamic" and unsigned "udynamic" variants).
  *  [YOLO]  "Tim Dettmers 如何用 bitsandbytes 與 QLoRA 降低 LLM 訓練門檻？"
  *          (yololab), sections on NF4, double quantization and QLoRA: the
  *          quantizer, loader and kernel must share exactly one definition of
@@ -311,6 +316,48 @@ qk_status qk_qlora_backward(const void* dY, int64_t M, const qk_quant_state* st,
                             const void* A, const void* B, int32_t r, float lora_scale, void* dX,
                             float* dA, float* dB, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * qk_make_dynamic_map — host.  [OPT8]: the page names the map and its
+ * properties but gives no construction; the levels are equal-mass quantiles,
+ *   signed   (is_signed != 0): levels[i] = RN_fp32( Phi^-1((2i+1)/512) / Phi^-1(511/512) )
+ *   unsigned (is_signed == 0): levels[i] = RN_fp32( Phi^-1(1/2 + (2i+1)/1024) / Phi^-1(1/2 + 511/1024) )
+ *   i = 0..255, increasing; the signed map is antisymmetric with levels[0] = -1,
+ *   levels[255] = 1 and no zero level; the unsigned map lies in (0, 1].
+ *   levels_out: host, float[256], written.
+ *   Errors: QK_ERR_INVALID_ARG (NULL levels_out).
+ */
+qk_status qk_make_dynamic_map(int32_t is_signed, float* levels_out);
+
+/*
+ * qk_quantize_blockwise_8bit — device.  [OPT8]: per block j of `blocksize`
+ * consecutive elements of the flattened x (the last block may be partial),
+ *   absmax[j] = max |x_k|  (fp32),
+ *   t_k = RN_fp32(x_k / absmax[j])  (IEEE division; t = +0 when absmax[j] == 0),
+ *   codes[k] = the index of the nearest level to t_k, ties to the smaller index.
+ *   x:         device, [n] elements of x_dtype (QK_BF16, QK_F16 or QK_F32), 16-byte aligned.
+ *   n:         >= 1.   blocksize: 256, 512, 1024, 2048 or 4096 (2048 in [OPT8]).
+ *   levels:    host, float[256] in [-1, 1], code order (any order; ties between
+ *              equal values go to the smaller code); copied at the call.
+ *              Thresholds closer than 1/1024 are refused (QK_ERR_UNSUPPORTED);
+ *              both qk_make_dynamic_map tables qualify.
+ *   codes:     device, uint8[n], one code per byte, 8-byte aligned, written.
+ *   absmax:    device, float[ceil(n / blocksize)], 4-byte aligned, written.
+ *   Errors: QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED, QK_ERR_NO_DEVICE, QK_ERR_HIP.
+ */
+qk_status qk_quantize_blockwise_8bit(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize,
+                                     const float* levels, uint8_t* codes, float* absmax, void* stream);
+
+/*
+ * qk_dequantize_blockwise_8bit — device.  [OPT8]: out[k] = RN_fp32(levels[codes[k]] *
+ *   absmax[k / blocksize]), written as fp32 or as bf16 (RNE).
+ *   codes:  device, uint8[n], 8-byte aligned.   absmax: device, float[ceil(n / blocksize)].
+ *   n >= 1; blocksize as for quantize; levels: host, float[256], copied at the call.
+ *   out:    device, [n] elements of out_dtype (QK_F32 or QK_BF16), 16-byte aligned, written.
+ *   Errors: QK_ERR_INVALID_ARG, QK_ERR_NO_DEVICE, QK_ERR_HIP.
+ */
+qk_status qk_dequantize_blockwise_8bit(const uint8_t* codes, const float* absmax, int64_t n, int32_t blocksize,
+                                       const float* levels, void* out, int32_t out_dtype, void* stream);
 
 /* Message for the calling thread's last failed call ("" if none).  The
  * string stays valid until the thread's next qk_* call. */

@@ -236,3 +236,34 @@ def test_qlora_backward_argument_errors(L):
     small = _state()                                                            # W [4, 64]: N % 64 != 0
     assert call(s=small) == qk.QK_ERR_UNSUPPORTED
     assert "multiples of 64" in qk.qk_last_error()
+
+
+def test_dynamic_map_matches_oracle_bitwise(L):
+    """The library's host map (AS 241 quantiles in binary64) equals the oracle's
+    (mpmath, 50 digits) after rounding to binary32."""
+    from oracle import blockwise8 as o8
+    for signed in (True, False):
+        got = qk.qk_make_dynamic_map(signed).numpy()
+        assert np.array_equal(got.view(np.uint32), o8.dynamic_map(signed).view(np.uint32))
+
+
+def test_quantize8_argument_errors(L):
+    lv = (ctypes.c_float * 256)(*qk.qk_make_dynamic_map(True).tolist())
+    q = L.qk_quantize_blockwise_8bit
+    assert q(None, qk.QK_F32, 10, 2048, lv, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert q(FAKE, qk.QK_F32, 0, 2048, lv, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert q(FAKE, 7, 10, 2048, lv, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert q(FAKE, qk.QK_F32, 10, 64, lv, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert "block size" in qk.qk_last_error()
+    assert q(FAKE, qk.QK_F32, 10, 2048, lv, ctypes.c_void_p(0x10004), FAKE, None) == qk.QK_ERR_INVALID_ARG
+    bad = (ctypes.c_float * 256)(*([0.5] * 255 + [1.5]))
+    assert q(FAKE, qk.QK_F32, 10, 2048, bad, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    close = (ctypes.c_float * 256)(*[i * 1e-5 for i in range(256)])     # thresholds 1e-5 apart
+    assert q(FAKE, qk.QK_F32, 10, 2048, close, FAKE, FAKE, None) == qk.QK_ERR_UNSUPPORTED
+    d = L.qk_dequantize_blockwise_8bit
+    assert d(None, FAKE, 10, 2048, lv, FAKE, qk.QK_F32, None) == qk.QK_ERR_INVALID_ARG
+    assert d(FAKE, FAKE, 10, 2048, lv, FAKE, qk.QK_F16, None) == qk.QK_ERR_INVALID_ARG
+    assert d(FAKE, FAKE, 10, 100, lv, FAKE, qk.QK_F32, None) == qk.QK_ERR_INVALID_ARG
+    assert d(ctypes.c_void_p(0x10004), FAKE, 10, 2048, lv, FAKE, qk.QK_F32, None) == qk.QK_ERR_INVALID_ARG
+    nan = (ctypes.c_float * 256)(*([float("nan")] + [0.0] * 255))
+    assert d(FAKE, FAKE, 10, 2048, nan, FAKE, qk.QK_F32, None) == qk.QK_ERR_INVALID_ARG

@@ -16,6 +16,10 @@ Recipes (one per workload; sizes are the ones the tests and the benchmark use):
                      dY [4096, N] ~ N(0, 1).
 * ``llama70b_stack`` 8 layers of {4 x [8192, 8192], 2 x [28672, 8192],
                      [8192, 28672]} ~ N(0, 0.015), activations M in {1, 4, 8}.
+* ``adam_states``    optimizer states of a parameter vector: g = Student-t(3) x 1e-3
+                     (gradient-like, heavy tails), m = g (signed), v = g * g
+                     (non-negative); fp32.  The full size is the Llama-7B layer
+                     set's 202,375,168 parameters, drawn on the device.
 * ``edge_3000x4099`` W [3000, 4099] = Student-t(3) x 0.02 with 0.1% of the
                      columns (4 of 4099) multiplied by 50 and then 1% of the
                      256-element-aligned chunks set to zero (so 1% of the
@@ -39,6 +43,7 @@ WORKLOAD_IDS = {
     "llama70b_stack": 4,
     "edge_3000x4099": 5,
     "lora_merge": 6,
+    "adam_states": 7,
 }
 
 LLAMA7B_SHAPES = [
@@ -152,3 +157,29 @@ def device_normal_bf16(shape, std: float, seed: int, device="cuda"):
 
 def llama70b_seed(layer: int, index: int) -> int:
     return WORKLOAD_IDS["llama70b_stack"] * 1_000_003 + layer * 101 + index
+
+
+LLAMA7B_LAYER_PARAMS = sum(N * K for _, N, K in LLAMA7B_SHAPES)
+
+
+def adam_states(n: int, tag: int = 0):
+    """(m, v) fp32 [n]: g ~ Student-t(3) * 1e-3, m = g, v = g * g."""
+    g = rng("adam_states", tensor=TENSOR_X, extra=tag).standard_t(3, size=n).astype(np.float32) * np.float32(1e-3)
+    return g, (g * g).astype(np.float32)
+
+
+def device_adam_states(n: int, seed: int, device="cuda"):
+    """The same recipe drawn on the device (torch Philox), for the full size:
+    a Student-t(3) draw is z / sqrt(chi2_3 / 3) with chi2_3 a sum of 3 squared normals."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(WORKLOAD_IDS["adam_states"] * 1_000_003 + int(seed))
+    z = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+    chi = torch.zeros(n, device=device, dtype=torch.float32)
+    for _ in range(3):
+        w = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+        chi.addcmul_(w, w)
+    g = z.div_(chi.div_(3.0).sqrt_()).mul_(1e-3)
+    del chi
+    return g, g * g
+
