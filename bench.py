@@ -273,6 +273,41 @@ def backward_rate(torch, qk, wl, iters=5):
             "with_lora_tflop_per_s": round(f_lora / res[True] / 1e12, 1), "M": M, "rank": r}
 
 
+def quant8_rate(torch, qk, workloads, iters=10):
+    """8-bit blockwise states with the dynamic map, block 2048: Adam's m (signed
+    map) and v (unsigned map) for the layer set's 202,375,168 parameters, fp32.
+    Algorithmic bytes: quantize 4 B read + 1 B code + 4/2048 B absmax per element;
+    dequantize to fp32 the same in reverse."""
+    n = workloads.LLAMA7B_LAYER_PARAMS
+    B = 2048
+    m, v = workloads.device_adam_states(n, seed=1)
+    res = {}
+    for name, x, signed in (("m", m, True), ("v", v, False)):
+        lv = qk.qk_make_dynamic_map(signed)
+        codes, am = qk.qk_quantize_blockwise_8bit(x, B, lv)
+        out = torch.empty(n, device="cuda")
+        for op, fn in (("quantize", lambda: qk.qk_quantize_blockwise_8bit(x, B, lv, codes, am)),
+                       ("dequantize_f32", lambda: qk.qk_dequantize_blockwise_8bit(codes, am, B, lv, out=out))):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / iters * 1e-3
+            nbytes = 5 * n + 4 * ((n + B - 1) // B)
+            res[f"{name}_{op}_us"] = round(t * 1e6, 1)
+            res[f"{name}_{op}_tb_per_s"] = round(nbytes / t / 1e12, 2)
+        del out, codes, am
+    del m, v
+    torch.cuda.empty_cache()
+    res["n"] = n
+    res["blocksize"] = B
+    return res
+
+
 def gemv_isolated(torch, qk, workloads, reps=6, iters=20):
     """GEMV M=1 over `reps` copies of the layer set (607 MB of NF4 state at 6),
     cycled so the 256 MB last-level cache cannot hold them; HBM rate."""
@@ -446,6 +481,7 @@ def bench(args):
 
     extra["lora_merge"] = merge_rate(torch, qk, wl)
     extra["qlora_backward"] = backward_rate(torch, qk, wl)
+    extra["quant8_adam_states"] = quant8_rate(torch, qk, workloads)
 
     cpu = None
     if not args.skip_cpu:
