@@ -11,7 +11,8 @@ pages it follows:
 
 * "篇2-bitsandbytes-具体观-算法与实现剖析" (xyzblog), §2.2 QLoRA / NF4 and
   figure 2-2 (the quantization pipeline and the nested quant_state), §2.3 and
-  figure 2-3 (8-bit blockwise states with the dynamic map);
+  figure 2-3 (8-bit blockwise states with the dynamic map), §2.1 and figure 2-1
+  (LLM.int8() vector-wise quantization with outlier decomposition);
 * "Tim Dettmers 如何用 bitsandbytes 與 QLoRA 降低 LLM 訓練門檻？" (yololab),
   the sections on NF4, double quantization and QLoRA;
 * "bitsandbytes：让大语言模型在消费级硬件上运行的量化神器" (zingnex), the
@@ -33,6 +34,7 @@ matmul        Y = X·deq(W)^T + s·(X·A)·B in fp64 (a7, a8)
 merge         LoRA merge into the dequantized weight, and requantization
 backward      gradients of the QLoRA layer for the input and the adapter
 blockwise8    8-bit blockwise quantization with the dynamic (quantile) map
+int8          LLM.int8(): vector-wise int8 matmul with outlier decomposition
 floats        exact rounding helpers (Fraction -> fp32, fp32 -> bf16 RNE)
 memory        storage arithmetic (bytes of a quantized tensor, bits/param)
 
@@ -41,4 +43,4 @@ does not re-type its formula (closed forms, invariants, brute force, the
 values the pages print).  No function is "parity unpinned".
 """
 
-from . import floats, codebook, blockwise, double_quant, dequant, matmul, memory, merge, backward, blockwise8  # noqa: F401
+from . import floats, codebook, blockwise, double_quant, dequant, matmul, memory, merge, backward, blockwise8, int8  # noqa: F401
