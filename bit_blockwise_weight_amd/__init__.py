@@ -104,6 +104,9 @@ def lib():
         "qk_qlora_backward_workspace_size": [i64, st_p, i32, ctypes.POINTER(ctypes.c_size_t)],
         "qk_qlora_backward": [vp, i64, st_p, vp, vp, vp, i32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "qk_make_dynamic_map": [i32, ctypes.POINTER(ctypes.c_float)],
+        "qk_int8_quantize_rows": [vp, i32, i64, i64, vp, vp, vp, vp],
+        "qk_int8_outlier_columns": [vp, i32, i64, i64, f32, vp, vp, vp, vp, vp],
+        "qk_int8_matmul": [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp],
         "qk_quantize_blockwise_8bit": [vp, i32, i64, i32, ctypes.POINTER(ctypes.c_float), vp, vp, vp],
         "qk_dequantize_blockwise_8bit": [vp, vp, i64, i32, ctypes.POINTER(ctypes.c_float), vp, i32, vp],
     }
@@ -242,6 +245,75 @@ def qk_dequantize_blockwise_8bit(codes: torch.Tensor, absmax: torch.Tensor, bloc
         _check(lib().qk_dequantize_blockwise_8bit(_ptr(codes), _ptr(absmax), n, int(blocksize), lv, _ptr(out),
                                                   _DTYPE_CODE[out.dtype], ctypes.c_void_p(_stream(codes))))
     return out
+
+
+def qk_int8_quantize_rows(x: torch.Tensor, skip_cols=None, q=None, absmax=None):
+    """Row-wise int8 quantization of a 2-D tensor: (q int8 [rows, cols], absmax fp32 [rows])."""
+    _require_cuda(x, skip_cols)
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported input dtype {x.dtype}")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if absmax is None:
+        absmax = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _require_cuda(q, absmax)
+    with _on(x.device):
+        _check(lib().qk_int8_quantize_rows(_ptr(x), _DTYPE_CODE[x.dtype], rows, cols, _ptr(skip_cols), _ptr(q),
+                                           _ptr(absmax), ctypes.c_void_p(_stream(x))))
+    return q, absmax
+
+
+def qk_int8_outlier_columns(x: torch.Tensor, threshold: float):
+    """(colmax fp32 [K], flags uint8 [K], idx int32 [K], count int32 [1]) for x [M, K];
+    the first count entries of idx are the outlier columns in increasing order."""
+    _require_cuda(x)
+    M, K = x.shape
+    dev = x.device
+    colmax = torch.empty(K, dtype=torch.float32, device=dev)
+    flags = torch.empty(K, dtype=torch.uint8, device=dev)
+    idx = torch.empty(K, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    with _on(dev):
+        _check(lib().qk_int8_outlier_columns(_ptr(x), _DTYPE_CODE[x.dtype], M, K, float(threshold), _ptr(colmax),
+                                             _ptr(flags), _ptr(idx), _ptr(count), ctypes.c_void_p(_stream(x))))
+    return colmax, flags, idx, count
+
+
+def qk_int8_matmul(Xq, SX, CB, SCB, X=None, outlier_idx=None, outlier_count=None, Y=None) -> torch.Tensor:
+    """fp16 Y [M, N] of the int8 product plus the fp16 outlier product."""
+    _require_cuda(Xq, SX, CB, SCB, X, outlier_idx, outlier_count)
+    M, K = Xq.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K:
+        raise ValueError(f"Xq {tuple(Xq.shape)} and CB {tuple(CB.shape)} disagree on K")
+    if X is not None and X.dtype != torch.float16:
+        raise ValueError("X must be fp16")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=Xq.device)
+    _require_cuda(Y)
+    with _on(Xq.device):
+        _check(lib().qk_int8_matmul(_ptr(Xq), _ptr(SX), _ptr(CB), _ptr(SCB), M, N, K, _ptr(X), _ptr(outlier_idx),
+                                    _ptr(outlier_count), _ptr(Y), ctypes.c_void_p(_stream(Xq))))
+    return Y
+
+
+class Int8Weight:
+    """A weight [N, K] kept as int8 rows (CB) and their absmax (SCB)."""
+
+    def __init__(self, w: torch.Tensor):
+        self.CB, self.SCB = qk_int8_quantize_rows(w)
+        self.N, self.K = w.shape
+
+    def forward(self, X: torch.Tensor, threshold: float = 6.0) -> torch.Tensor:
+        """Y = X W^T by the mixed-precision decomposition (X fp16 [M, K])."""
+        X2 = X.reshape(-1, self.K)
+        if threshold > 0:
+            _, flags, idx, count = qk_int8_outlier_columns(X2, threshold)
+            Xq, SX = qk_int8_quantize_rows(X2, flags)
+            return qk_int8_matmul(Xq, SX, self.CB, self.SCB, X2, idx, count)
+        Xq, SX = qk_int8_quantize_rows(X2)
+        return qk_int8_matmul(Xq, SX, self.CB, self.SCB)
 
 
 def qk_double_quant_workspace_size(nblocks: int) -> int:

@@ -27,7 +27,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqk.so")
 
 SOURCES = ["api.cpp", "codebook.cpp", "quantize.hip", "double_quant.hip", "dequantize.hip", "gemv.hip", "gemm.hip",
-           "merge.hip", "backward.hip", "quantize8.hip"]
+           "merge.hip", "backward.hip", "quantize8.hip", "int8mm.hip"]
 
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

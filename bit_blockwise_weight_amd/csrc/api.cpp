@@ -203,6 +203,60 @@ qk_status qk_dequantize_blockwise_8bit(const uint8_t* codes, const float* absmax
                     "qk_dequantize_blockwise_8bit");
 }
 
+qk_status qk_int8_quantize_rows(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const uint8_t* skip_cols,
+                                int8_t* q, float* absmax, void* stream) {
+    if (!x || !q || !absmax) return fail(QK_ERR_INVALID_ARG, "qk_int8_quantize_rows: NULL pointer argument");
+    if (x_dtype != QK_BF16 && x_dtype != QK_F16 && x_dtype != QK_F32)
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_quantize_rows: unknown x dtype %d", x_dtype);
+    if (rows < 1 || cols < 1 || cols % 8 != 0)
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_quantize_rows: rows >= 1 and cols >= 1 with cols %% 8 == 0");
+    if (!aligned(x, 16) || !aligned(q, 8) || !aligned(absmax, 4) || (skip_cols && !aligned(skip_cols, 8)))
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_quantize_rows: x must be 16-byte aligned, q and skip_cols 8-byte");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_int8_rowquant(x, x_dtype, rows, cols, skip_cols, q, absmax,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                    "qk_int8_quantize_rows");
+}
+
+qk_status qk_int8_outlier_columns(const void* x, int32_t x_dtype, int64_t M, int64_t K, float threshold, float* colmax,
+                                  uint8_t* flags, int32_t* idx, int32_t* count, void* stream) {
+    if (!x || !colmax || !flags || !idx || !count)
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_outlier_columns: NULL pointer argument");
+    if (x_dtype != QK_BF16 && x_dtype != QK_F16 && x_dtype != QK_F32)
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_outlier_columns: unknown x dtype %d", x_dtype);
+    if (M < 1 || K < 1 || K % 8 != 0)
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_outlier_columns: M >= 1 and K >= 1 with K %% 8 == 0");
+    if (!std::isfinite(threshold) || threshold < 0.0f)
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_outlier_columns: threshold must be finite and >= 0");
+    if (!aligned(x, 16) || !aligned(colmax, 4) || !aligned(idx, 4) || !aligned(count, 4))
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_outlier_columns: x must be 16-byte aligned, colmax, idx, count 4-byte");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_int8_outliers(x, x_dtype, M, K, threshold, colmax, flags, idx, count,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                    "qk_int8_outlier_columns");
+}
+
+qk_status qk_int8_matmul(const int8_t* Xq, const float* SX, const int8_t* CB, const float* SCB, int64_t M, int64_t N,
+                         int64_t K, const void* X, const int32_t* outlier_idx, const int32_t* outlier_count, void* Y,
+                         void* stream) {
+    if (!Xq || !SX || !CB || !SCB || !Y) return fail(QK_ERR_INVALID_ARG, "qk_int8_matmul: NULL pointer argument");
+    const bool any = X || outlier_idx || outlier_count;
+    if (any && !(X && outlier_idx && outlier_count))
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_matmul: give X, outlier_idx and outlier_count together, or none");
+    if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_matmul: M, N >= 1 and K >= 16 with K %% 16 == 0");
+    if (!aligned(Xq, 16) || !aligned(CB, 16) || !aligned(SX, 4) || !aligned(SCB, 4) || !aligned(Y, 2) ||
+        (any && (!aligned(X, 2) || !aligned(outlier_idx, 4) || !aligned(outlier_count, 4))))
+        return fail(QK_ERR_INVALID_ARG, "qk_int8_matmul: Xq and CB must be 16-byte aligned, the others element-aligned");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_int8_matmul(Xq, SX, CB, SCB, M, N, K, X, outlier_idx, outlier_count, Y,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    "qk_int8_matmul");
+}
+
 qk_status qk_double_quant_workspace_size(int64_t nblocks, size_t* bytes) {
     if (!bytes) return fail(QK_ERR_INVALID_ARG, "qk_double_quant_workspace_size: bytes is NULL");
     if (nblocks < 1) return fail(QK_ERR_INVALID_ARG, "qk_double_quant_workspace_size: nblocks must be >= 1");

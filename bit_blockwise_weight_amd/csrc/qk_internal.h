@@ -87,6 +87,14 @@ hipError_t launch_quantize8(const void* x, int32_t x_dtype, int64_t n, int32_t b
 hipError_t launch_dequantize8(const uint8_t* codes, const float* absmax, int64_t n, int32_t blocksize,
                               const float levels[256], void* out, int32_t out_dtype, hipStream_t s);
 
+hipError_t launch_int8_rowquant(const void* x, int32_t dtype, int64_t rows, int64_t cols, const uint8_t* skip,
+                                int8_t* q, float* absmax, hipStream_t s);
+hipError_t launch_int8_outliers(const void* x, int32_t dtype, int64_t M, int64_t K, float threshold, float* colmax,
+                                uint8_t* flags, int32_t* idx, int32_t* count, hipStream_t s);
+hipError_t launch_int8_matmul(const int8_t* Xq, const float* SX, const int8_t* CB, const float* SCB, int64_t M,
+                              int64_t N, int64_t K, const void* X, const int32_t* oidx, const int32_t* ocount, void* Y,
+                              hipStream_t s);
+
 size_t dq_workspace_bytes(int64_t nblocks);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int8_t* q8, float* scale,
                                float* mean, void* workspace, hipStream_t s);

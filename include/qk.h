@@ -25,6 +25,13 @@
  *          absmax per block, 8-bit codes through a dynamic map of 256
  *          non-uniform levels (dense at zero, sparse in the tails, maximising the
  *          code entropy; signed "dynamic" and unsigned "udynamic" variants).
+ *  [INT8]  "篇2-bitsandbytes-具体观-算法与实现剖析", §2.1 LLM.int8(), 【原理】,
+ *          【代码】, 【例子】 and figure 2-1: activation columns whose largest
+ *          magnitude exceeds a threshold go through a 16-bit matmul with the
+ *          matching weight columns; the rest is quantized vector-wise (one absmax
+ *          per row, scaled to [-127, 127], int8) and multiplied with the int8
+ *          weight (CB, with one absmax per weight row SCB); the results are added;
+ *          threshold 0 disables the decomposition.
  *  [YOLO]  "Tim Dettmers 如何用 bitsandbytes 與 QLoRA 降低 LLM 訓練門檻？"
  *          (yololab), sections on NF4, double quantization and QLoRA: the
  *          quantizer, loader and kernel must share exactly one definition of
@@ -358,6 +365,59 @@ qk_status qk_quantize_blockwise_8bit(const void* x, int32_t x_dtype, int64_t n, 
  */
 qk_status qk_dequantize_blockwise_8bit(const uint8_t* codes, const float* absmax, int64_t n, int32_t blocksize,
                                        const float* levels, void* out, int32_t out_dtype, void* stream);
+
+/*
+ * qk_int8_quantize_rows — device.  [INT8] vector-wise quantization: for each row r
+ * of the row-major matrix x [rows, cols],
+ *   absmax[r] = max |x[r, k]| over the columns k with skip_cols[k] == 0,
+ *   q[r, k]   = rint_even( RN_fp32( RN_fp32(x[r, k] / absmax[r]) * 127 ) ) in [-127, 127],
+ *               0 when absmax[r] == 0 or skip_cols[k] != 0.
+ *   Used for the weight (CB = q, SCB = absmax, skip_cols NULL) and for the
+ *   activations (skip_cols = the outlier flags of qk_int8_outlier_columns).
+ *   x: device, x_dtype QK_F16, QK_BF16 or QK_F32, 16-byte aligned.   rows, cols >= 1, cols % 8 == 0.
+ *   skip_cols: device, uint8[cols], 8-byte aligned, or NULL.
+ *   q: device, int8[rows * cols], 8-byte aligned, written.   absmax: device, float[rows], written.
+ *   Errors: QK_ERR_INVALID_ARG, QK_ERR_NO_DEVICE, QK_ERR_HIP.
+ */
+qk_status qk_int8_quantize_rows(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const uint8_t* skip_cols,
+                                int8_t* q, float* absmax, void* stream);
+
+/*
+ * qk_int8_outlier_columns — device.  [INT8] 【例子】 and figure 2-1: column k of x
+ * [M, K] is an outlier when max_m |x[m, k]| > threshold (strictly; none when
+ * threshold == 0).
+ *   x: device, x_dtype as above, 16-byte aligned; M >= 1, K >= 1, K % 8 == 0.
+ *   threshold: finite, >= 0.
+ *   colmax: device, float[K], written (the column maxima).
+ *   flags:  device, uint8[K], written (1 = outlier).
+ *   idx:    device, int32[K]; its first *count entries are written with the
+ *           outlier columns in increasing order.
+ *   count:  device, int32[1], written.  Deterministic.
+ *   Errors: QK_ERR_INVALID_ARG, QK_ERR_NO_DEVICE, QK_ERR_HIP.
+ */
+qk_status qk_int8_outlier_columns(const void* x, int32_t x_dtype, int64_t M, int64_t K, float threshold, float* colmax,
+                                  uint8_t* flags, int32_t* idx, int32_t* count, void* stream);
+
+/*
+ * qk_int8_matmul — device.  [INT8] mixed-precision decomposition, for X [M, K]
+ * (fp16) against the int8 weight (CB [N, K], SCB [N]):
+ *   Y[m, n] = sum_{k not outlier} Xq[m, k] CB[n, k] * SX[m] * SCB[n] / 127^2
+ *           + sum_{k outlier} X[m, k] * fp16(CB[n, k] * SCB[n] / 127),
+ *   the int8 products summed exactly in int32, the rest in fp32; Y is written
+ *   in fp16.  Agreement with the fp64 reference: rel. Frobenius <= 5e-3, max
+ *   error <= 2e-2 * max |ref|.
+ *   Xq, SX: device, from qk_int8_quantize_rows of X with the outlier columns
+ *           skipped (int8 [M, K] 16-byte aligned; float[M]).
+ *   CB, SCB: device, from qk_int8_quantize_rows of W [N, K] (int8 [N, K] 16-byte aligned; float[N]).
+ *   M, N >= 1; K >= 16, K % 16 == 0.
+ *   X, outlier_idx, outlier_count: device, the fp16 X [M, K], and idx / count from
+ *           qk_int8_outlier_columns; all three NULL for no outlier path.
+ *   Y: device, fp16 [M, N], written.
+ *   Errors: QK_ERR_INVALID_ARG, QK_ERR_NO_DEVICE, QK_ERR_HIP.
+ */
+qk_status qk_int8_matmul(const int8_t* Xq, const float* SX, const int8_t* CB, const float* SCB, int64_t M, int64_t N,
+                         int64_t K, const void* X, const int32_t* outlier_idx, const int32_t* outlier_count, void* Y,
+                         void* stream);
 
 /* Message for the calling thread's last failed call ("" if none).  The
  * string stays valid until the thread's next qk_* call. */

@@ -53,15 +53,24 @@ def outlier_columns(x: np.ndarray, threshold: float) -> np.ndarray:
     return np.abs(x).max(axis=0) > np.float32(threshold)
 
 
-def int8_matmul_f64(x: np.ndarray, CB: np.ndarray, SCB: np.ndarray, threshold: float):
-    """Y [M, N] in fp64 for X [M, K] (fp16 values given as fp32) and the int8
-    weight (CB [N, K], SCB [N]).  Returns (Y, outlier mask, Xq, SX)."""
+def decomposed_product_f64(x: np.ndarray, out: np.ndarray, CB: np.ndarray, SCB: np.ndarray):
+    """Y for the rows of x given the outlier mask `out` (found over all rows of
+    the activation).  Returns (Y, Xq, SX)."""
     x = np.asarray(x, dtype=np.float32)
-    out = outlier_columns(x, threshold)
+    out = np.asarray(out, dtype=bool)
     Xq, SX = quantize_rows(x, ~out)
     acc = Xq.astype(np.float64) @ np.asarray(CB, dtype=np.float64).T          # exact: |sum| < 2^53
     Y = acc * SX.astype(np.float64)[:, None] * np.asarray(SCB, dtype=np.float64)[None, :] / (127.0 * 127.0)
     if out.any():
         Wd = np.asarray(CB, dtype=np.float64)[:, out] * np.asarray(SCB, dtype=np.float64)[:, None] / 127.0
         Y = Y + x[:, out].astype(np.float64) @ Wd.T
+    return Y, Xq, SX
+
+
+def int8_matmul_f64(x: np.ndarray, CB: np.ndarray, SCB: np.ndarray, threshold: float):
+    """Y [M, N] in fp64 for X [M, K] (fp16 values given as fp32) and the int8
+    weight (CB [N, K], SCB [N]).  Returns (Y, outlier mask, Xq, SX)."""
+    x = np.asarray(x, dtype=np.float32)
+    out = outlier_columns(x, threshold)
+    Y, Xq, SX = decomposed_product_f64(x, out, CB, SCB)
     return Y, out, Xq, SX

@@ -20,6 +20,10 @@ Recipes (one per workload; sizes are the ones the tests and the benchmark use):
                      (gradient-like, heavy tails), m = g (signed), v = g * g
                      (non-negative); fp32.  The full size is the Llama-7B layer
                      set's 202,375,168 parameters, drawn on the device.
+* ``llm_int8``       activations X [M, K] ~ N(0, 1) in fp16 with 0.1% of the columns
+                     (seeded) multiplied by 20, so their maxima exceed the
+                     threshold 6 while the other columns stay below it; the
+                     weights are the QLoRA prefill weights.
 * ``edge_3000x4099`` W [3000, 4099] = Student-t(3) x 0.02 with 0.1% of the
                      columns (4 of 4099) multiplied by 50 and then 1% of the
                      256-element-aligned chunks set to zero (so 1% of the
@@ -44,6 +48,7 @@ WORKLOAD_IDS = {
     "edge_3000x4099": 5,
     "lora_merge": 6,
     "adam_states": 7,
+    "llm_int8": 8,
 }
 
 LLAMA7B_SHAPES = [
@@ -182,4 +187,14 @@ def device_adam_states(n: int, seed: int, device="cuda"):
     g = z.div_(chi.div_(3.0).sqrt_()).mul_(1e-3)
     del chi
     return g, g * g
+
+
+def int8_activations(M: int, K: int, frac: float = 0.001, mult: float = 20.0, tag: int = 0):
+    """X [M, K] fp32 values exactly representable in fp16, and the scaled columns."""
+    g = rng("llm_int8", tensor=TENSOR_X, extra=tag)
+    x = g.standard_normal((M, K), dtype=np.float32)
+    n_out = max(1, int(round(frac * K)))
+    cols = np.sort(rng("llm_int8", tensor=TENSOR_MASK, extra=tag).choice(K, size=n_out, replace=False))
+    x[:, cols] *= np.float32(mult)
+    return x.astype(np.float16).astype(np.float32), cols
 
