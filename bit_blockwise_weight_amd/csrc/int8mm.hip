@@ -12,9 +12,10 @@
 // Quantization of a row with absmax a: q = rint(RN(RN(x / a) * 127)) (IEEE
 // division, round half to even), 0 when a == 0 or the column is excluded.
 //
-// Outlier columns: column maxima by atomicMax on the bits of non-negative floats
-// (the maximum does not depend on the order), then one workgroup lists the columns
-// over the threshold in increasing order (a prefix sum, deterministic).
+// Outlier columns: column maxima reduced inside a workgroup, then by atomicMax on
+// the bits of non-negative floats across row slices (the maximum does not depend
+// on the order), then one workgroup lists the columns over the threshold in
+// increasing order (a prefix sum, deterministic).
 //
 // Matmul: 128 x 128 output tiles, 128 k per step, 4 waves as 2 x 2, each 64 x 64
 // = 2 x 2 tiles of v_mfma_i32_32x32x32_i8 (exact int32 sums); both operands
@@ -100,28 +101,41 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint32_t* __restric
     if (i < n) p[i] = 0u;
 }
 
-// Column maxima of |x| over a slice of rows per workgroup row of the grid; thread t
-// of workgroup (bx, s) takes columns [8 (256 bx + t), + 8).  K % 8 == 0.
+// Column maxima of |x|: workgroup (bx, s) takes 512 columns (lane l: [512 bx + 8 l, + 8))
+// and slice s of the rows, its 4 waves every 4th row of the slice; the 4 wave maxima
+// meet in LDS and one atomicMax per column and slice goes to memory.  K % 8 == 0.
 template <typename InT>
 __global__ __launch_bounds__(kThreads) void colmax_kernel(const void* __restrict__ x, int64_t M, int64_t K,
                                                           int32_t nslices, uint32_t* __restrict__ colmax_bits) {
-    const int64_t k = 8 * ((int64_t)blockIdx.x * kThreads + threadIdx.x);
-    if (k >= K) return;
+    __shared__ float part[3][512];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t k = 512 * (int64_t)blockIdx.x + 8 * lane;
+    const bool ok = k < K;
     const int s = blockIdx.y;
     const int64_t r0 = M * s / nslices, r1 = M * (s + 1) / nslices;
     using Raw = typename RawOf<InT>::type;
     float mx[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t m = r0; m < r1; ++m) {
-        Raw r;
-        load_raw<InT>(x, (m + 1) * K, m * K + k, r);
-        float v[8];
-        unpack_raw<InT>(r, v);
+    if (ok) {
+        for (int64_t m = r0 + wave; m < r1; m += 4) {
+            Raw r;
+            load_raw<InT>(x, (m + 1) * K, m * K + k, r);
+            float v[8];
+            unpack_raw<InT>(r, v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(v[i]));
+            for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(v[i]));
+        }
     }
-    if (r1 > r0) {
+    if (wave > 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) atomicMax(colmax_bits + k + i, as_uint(mx[i]));   // non-negative: bit order = value order
+        for (int i = 0; i < 8; ++i) part[wave - 1][8 * lane + i] = mx[i];
+    }
+    __syncthreads();
+    if (wave == 0 && ok && r1 > r0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float m4 = fmaxf(fmaxf(mx[i], part[0][8 * lane + i]), fmaxf(part[1][8 * lane + i], part[2][8 * lane + i]));
+            atomicMax(colmax_bits + k + i, as_uint(m4));   // non-negative: bit order = value order
+        }
     }
 }
 
@@ -333,11 +347,10 @@ template <typename InT>
 hipError_t launch_colmax_t(const void* x, int64_t M, int64_t K, uint32_t* colmax_bits, hipStream_t s) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((K + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
                        colmax_bits, K);
-    // about 512 workgroups, at least 32 rows per slice: each column takes at most
-    // M / 32 atomics (contention on one address serializes them)
-    const int64_t colblocks = (K / 8 + kThreads - 1) / kThreads;
+    // about 512 workgroups, at least 64 rows per slice
+    const int64_t colblocks = (K + 511) / 512;
     int64_t slices = (512 + colblocks - 1) / colblocks;
-    if (slices > M / 32) slices = M / 32;
+    if (slices > M / 64) slices = M / 64;
     if (slices < 1) slices = 1;
     if (slices > 65535) slices = 65535;
     hipLaunchKernelGGL((colmax_kernel<InT>), dim3((unsigned)colblocks, (unsigned)slices), dim3(kThreads), 0, s, x, M, K,
