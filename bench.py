@@ -308,6 +308,45 @@ def quant8_rate(torch, qk, workloads, iters=10):
     return res
 
 
+def int8_rate(torch, qk, workloads, iters=10):
+    """LLM.int8() on the prefill shape: X [4096, 4096] fp16 with 0.1% outlier
+    columns (threshold 6), the int8 weight of W [N, 4096], N in {4096, 11008}:
+    outlier columns + row quantization of X + the int8 matmul with the fused fp16
+    outlier product.  Ops: 2MNK."""
+    M, K = 4096, 4096
+    x, _ = workloads.int8_activations(M, K, tag=1)
+    X = torch.from_numpy(x).cuda().half()
+    res = {}
+    for N in (4096, 11008):
+        W = torch.randn((N, K), device="cuda").mul_(0.02).half()
+        CB, SCB = qk.qk_int8_quantize_rows(W)
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        state = {}
+
+        def fwd():
+            _, flags, idx, count = qk.qk_int8_outlier_columns(X, 6.0)
+            Xq, SX = qk.qk_int8_quantize_rows(X, flags)
+            state["mm"] = (Xq, SX, idx, count)
+            qk.qk_int8_matmul(Xq, SX, CB, SCB, X, idx, count, Y)
+
+        fwd()
+        Xq, SX, idx, count = state["mm"]
+        for name, fn in (("forward", fwd), ("matmul", lambda: qk.qk_int8_matmul(Xq, SX, CB, SCB, X, idx, count, Y))):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / iters * 1e-3
+            res[f"N{N}_{name}_us"] = round(t * 1e6, 1)
+            res[f"N{N}_{name}_tops"] = round(2 * M * N * K / t / 1e12, 1)
+        res[f"N{N}_outlier_columns"] = int(count.item())
+    return res
+
+
 def gemv_isolated(torch, qk, workloads, reps=6, iters=20):
     """GEMV M=1 over `reps` copies of the layer set (607 MB of NF4 state at 6),
     cycled so the 256 MB last-level cache cannot hold them; HBM rate."""
@@ -482,6 +521,7 @@ def bench(args):
     extra["lora_merge"] = merge_rate(torch, qk, wl)
     extra["qlora_backward"] = backward_rate(torch, qk, wl)
     extra["quant8_adam_states"] = quant8_rate(torch, qk, workloads)
+    extra["llm_int8"] = int8_rate(torch, qk, workloads)
 
     cpu = None
     if not args.skip_cpu:
