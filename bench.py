@@ -518,10 +518,11 @@ def bench(args):
     if not args.skip_isolated:
         extra["gemv_m1_isolated_607MB"] = gemv_isolated(torch, qk, workloads)
 
-    extra["lora_merge"] = merge_rate(torch, qk, wl)
-    extra["qlora_backward"] = backward_rate(torch, qk, wl)
-    extra["quant8_adam_states"] = quant8_rate(torch, qk, workloads)
-    extra["llm_int8"] = int8_rate(torch, qk, workloads)
+    if not args.skip_rows:
+        extra["lora_merge"] = merge_rate(torch, qk, wl)
+        extra["qlora_backward"] = backward_rate(torch, qk, wl)
+        extra["quant8_adam_states"] = quant8_rate(torch, qk, workloads)
+        extra["llm_int8"] = int8_rate(torch, qk, workloads)
 
     cpu = None
     if not args.skip_cpu:
@@ -635,6 +636,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-isolated", action="store_true", help="skip the isolated GEMV HBM measurement")
+    ap.add_argument("--skip-rows", action="store_true",
+                    help="skip the timings of the merge, backward, 8-bit state and LLM.int8 calls")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB device copy")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"),
                     help="summarize a rocprofv3 --kernel-trace --stats directory into OUT")
