@@ -17,14 +17,14 @@
 // on the order), then one workgroup lists the columns over the threshold in
 // increasing order (a prefix sum, deterministic).
 //
-// Matmul: 128 x 128 output tiles, 128 k per step, 4 waves as 2 x 2, each 64 x 64
-// = 2 x 2 tiles of v_mfma_i32_32x32x32_i8 (exact int32 sums); both operands
-// staged through double-buffered LDS with 128-byte rows whose 16-byte pieces are
-// XOR-swizzled (piece c of row r in slot c ^ ((r >> 1) & 7): conflict-free
-// fragment reads); the global loads run two steps ahead; one barrier per step.  Epilogue: C = RN(RN(float(acc) * SX[m])
-// * SCB[n]) / 127^2 in fp32, then the outlier columns 16 at a time with
-// v_mfma_f32_32x32x16_f16 into the same fp32 accumulators (X's fp16 values and the
-// weight columns dequantized to fp16, CB * SCB / 127), fp16 output.
+// Matmul: 256 x 256 output tiles, 64 k per step, 8 waves as 4 x 2, each 64 x 128
+// = 2 x 4 tiles of v_mfma_i32_32x32x32_i8 (exact int32 sums; 6 fragment reads per
+// 8 MFMAs; two waves per SIMD); both operands staged through double-buffered LDS with 64-byte rows
+// whose 16-byte pieces are XOR-swizzled (conflict-free fragment reads); the global
+// loads run two steps ahead; one barrier per step.  Epilogue: C = RN(RN(float(acc) * SX[m])
+// * SCB[n]) / 127^2 in fp32, plus the outlier columns' product computed with
+// v_mfma_f32_32x32x16_f16 from X's fp16 values and the weight columns dequantized
+// to fp16 (CB * SCB / 127), gathered by the workgroup into LDS; fp16 output.
 #include "qk_internal.h"
 #include "qk_device.h"
 #include "qk_quant_io.h"
@@ -181,18 +181,29 @@ struct MmArgs {
     int64_t M, N, K;
 };
 
-constexpr int TM = 128, TN = 128, TKB = 128;
+constexpr int TM = 256, TN = 256, TKB = 64;
 constexpr int kXcds = 8;
+constexpr int kOGroup = 32;                 // outlier columns staged at a time (2 MFMA steps of 16)
+constexpr int kOPitch = kOGroup + 8;        // fp16 per staged outlier row (80 bytes: conflict-free reads)
 
-__device__ __forceinline__ int soff(int row, int chunk) { return row * 128 + 16 * (chunk ^ ((row >> 1) & 7)); }
+// byte offset of 16-byte piece c of row r in a tile of 64-byte rows: piece c sits in
+// slot c ^ ((r >> 2) & 3), so 16 consecutive rows reading one piece hit 16 bank groups
+__device__ __forceinline__ int soff(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 2) & 3)); }
 
-__global__ __launch_bounds__(kThreads) void int8mm_kernel(MmArgs a) {
-    __shared__ __attribute__((aligned(16))) int8_t xa0[TM * TKB];
-    __shared__ __attribute__((aligned(16))) int8_t xa1[TM * TKB];
-    __shared__ __attribute__((aligned(16))) int8_t wb0[TN * TKB];
-    __shared__ __attribute__((aligned(16))) int8_t wb1[TN * TKB];
+constexpr int kMmThreads = 512;            // 8 waves: two per SIMD, so one wave's MFMAs cover the other's waits
+
+template <bool kTail>
+__global__ __launch_bounds__(kMmThreads, 1) void int8mm_kernel(MmArgs a) {
+    // one pool: X tiles at 0 and 16 KB, W tiles at 32 and 48 KB; the epilogue reuses it
+    // for the staged outlier columns (X part at 0, W part at 32 KB, 20 KB each)
+    __shared__ __attribute__((aligned(16))) int8_t pool[2 * TM * TKB + 2 * TN * TKB];
+    int8_t* const xa0 = pool;
+    int8_t* const xa1 = pool + TM * TKB;
+    int8_t* const wb0 = pool + 2 * TM * TKB;
+    int8_t* const wb1 = pool + 2 * TM * TKB + TN * TKB;
+    static_assert(TM * kOPitch * 2 <= 2 * TM * TKB && TN * kOPitch * 2 <= 2 * TN * TKB, "outlier staging fits");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1;                     // wave tile: rows [64 wm, +64) x cols [128 wn, +128)
     const int fi = lane & 31, h = lane >> 5;
     const int64_t M = a.M, N = a.N, K = a.K;
     const uint32_t tiles_n = (uint32_t)((N + TN - 1) / TN);
@@ -202,50 +213,65 @@ __global__ __launch_bounds__(kThreads) void int8mm_kernel(MmArgs a) {
     const int64_t m0 = (int64_t)(lid / tiles_n) * TM, n0 = (int64_t)(lid % tiles_n) * TN;
     const int64_t nsteps = (K + TKB - 1) / TKB;
 
-    // staging: piece c = tid + 256 v of a 128 x 128-byte tile: row c >> 3, 16-byte piece c & 7;
-    // pieces at k >= K (the tail, and steps past the last) are zeros without a load
-    auto load = [&](uint4 (&ra)[4], uint4 (&rb)[4], int64_t st) {
+    // staging: piece c = tid + 512 v (v < 2) of a 256 x 64-byte tile: row c >> 2, piece c & 3
+    const int8_t* xrow[2];
+    const int8_t* wrow[2];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int c = tid + kThreads * v;
-            const int row = c >> 3, ch = c & 7;
-            const int64_t k = st * TKB + 16 * ch;
-            const int64_t gm = m0 + row < M ? m0 + row : M - 1;
-            const int64_t gn = n0 + row < N ? n0 + row : N - 1;
-            ra[v] = k < K ? *reinterpret_cast<const uint4*>(a.Xq + gm * K + k) : make_uint4(0, 0, 0, 0);
-            rb[v] = k < K ? *reinterpret_cast<const uint4*>(a.CB + gn * K + k) : make_uint4(0, 0, 0, 0);
+    for (int v = 0; v < 2; ++v) {
+        const int row = (tid + kMmThreads * v) >> 2;
+        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
+        const int64_t gn = n0 + row < N ? n0 + row : N - 1;
+        xrow[v] = a.Xq + gm * K;
+        wrow[v] = a.CB + gn * K;
+    }
+    // unconditional loads from a clamped address (a conditional load would become a
+    // branch); with K % 64 != 0 the pieces at k >= K of the last step are zeroed when
+    // they are stored.  Steps past the last are loaded (clamped) but never computed.
+    auto load = [&](uint4 (&ra)[2], uint4 (&rb)[2], int64_t st) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int64_t k = st * TKB + 16 * ((tid + kMmThreads * v) & 3);
+            const int64_t kc = k < K ? k : K - 16;
+            ra[v] = *reinterpret_cast<const uint4*>(xrow[v] + kc);
+            rb[v] = *reinterpret_cast<const uint4*>(wrow[v] + kc);
         }
     };
-    auto store = [&](const uint4 (&ra)[4], const uint4 (&rb)[4], int8_t* xa, int8_t* wb) {
+    auto store = [&](const uint4 (&ra)[2], const uint4 (&rb)[2], int64_t st, int8_t* xa, int8_t* wb) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int c = tid + kThreads * v;
-            *reinterpret_cast<uint4*>(xa + soff(c >> 3, c & 7)) = ra[v];
-            *reinterpret_cast<uint4*>(wb + soff(c >> 3, c & 7)) = rb[v];
+        for (int v = 0; v < 2; ++v) {
+            const int c = tid + kMmThreads * v;
+            uint4 va = ra[v], vb = rb[v];
+            if constexpr (kTail) {
+                const bool kin = st * TKB + 16 * (c & 3) < K;
+                va = make_uint4(kin ? va.x : 0u, kin ? va.y : 0u, kin ? va.z : 0u, kin ? va.w : 0u);
+                vb = make_uint4(kin ? vb.x : 0u, kin ? vb.y : 0u, kin ? vb.z : 0u, kin ? vb.w : 0u);
+            }
+            *reinterpret_cast<uint4*>(xa + soff(c >> 2, c & 3)) = va;
+            *reinterpret_cast<uint4*>(wb + soff(c >> 2, c & 3)) = vb;
         }
     };
-    intx16_t acc[2][2];
+    intx16_t acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
     auto compute = [&](const int8_t* xa, const int8_t* wb) {
 #pragma unroll
         for (int kk = 0; kk < TKB / 32; ++kk) {
-            v4i_t af[2], bf[2];
+            v4i_t af[2], bf[4];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 af[i] = *reinterpret_cast<const v4i_t*>(xa + soff(wm * 64 + 32 * i + fi, 2 * kk + h));
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const v4i_t*>(wb + soff(wn * 64 + 32 * j + fi, 2 * kk + h));
+            for (int j = 0; j < 4; ++j)
+                bf[j] = *reinterpret_cast<const v4i_t*>(wb + soff(wn * 128 + 32 * j + fi, 2 * kk + h));
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
     };
@@ -256,81 +282,95 @@ __global__ __launch_bounds__(kThreads) void int8mm_kernel(MmArgs a) {
         asm volatile("" ::: "memory");
     };
 
-    // two register sets: the loads of step s + 2 are issued while step s is computed
-    uint4 ra0[4], rb0[4], ra1[4], rb1[4];
+    // two register sets: the loads of step s + 2 are issued while step s is computed;
+    // the empty asm statements keep the scheduler from sinking the loads to the end of
+    // the step (next to the stores that consume the other register set)
+    uint4 ra0[2], rb0[2], ra1[2], rb1[2];
     load(ra0, rb0, 0);
-    store(ra0, rb0, xa0, wb0);
+    store(ra0, rb0, 0, xa0, wb0);
     load(ra1, rb1, 1);
     barrier();
     int64_t st = 0;
     for (; st + 1 < nsteps; st += 2) {
         load(ra0, rb0, st + 2);
+        asm volatile("" ::: "memory");
         compute(xa0, wb0);
-        store(ra1, rb1, xa1, wb1);
+        store(ra1, rb1, st + 1, xa1, wb1);
         barrier();
         load(ra1, rb1, st + 3);
+        asm volatile("" ::: "memory");
         compute(xa1, wb1);
-        store(ra0, rb0, xa0, wb0);
+        store(ra0, rb0, st + 2, xa0, wb0);
         barrier();
     }
     if (st < nsteps) compute(xa0, wb0);
+    __syncthreads();
 
-    // epilogue: lane holds C[8 b + 4 h + q][fi] in register 4 b + q
-    floatx16_t f[2][2];
-    float scb[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + wn * 64 + 32 * j + fi;
-        scb[j] = a.SCB[n < N ? n : N - 1];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t m = m0 + wm * 64 + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
-            const float sx = a.SX[m < M ? m : M - 1];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                f[i][j][e] = __fdiv_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e], sx), scb[j]), 16129.0f);
-        }
+    // epilogue.  The outlier columns are staged in groups of 32: threads 0..255 take row
+    // t of the tile's X columns (fp16), threads 256..511 row t - 256 of the weight
+    // columns (CB * SCB / 127 in fp16), in LDS freed by the main loop.  Then tile by
+    // tile: the outlier product in fp32 (v_mfma_f32_32x32x16_f16, 16 columns per MFMA),
+    // plus the int32 sums scaled by SX[m] SCB[n] / 127^2, to fp16.  With more than 32
+    // outlier columns every tile restages the groups (rare: the page's figure is 0.1%
+    // of the columns).
     const int32_t nout = a.ocount ? *a.ocount : 0;
-    for (int32_t c0 = 0; c0 < nout; c0 += 16) {
-        halfx8_t xo[2], wo[2];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int32_t oi = c0 + 8 * h + p;
+    const int ngroups = (nout + kOGroup - 1) / kOGroup;
+    _Float16* xo = reinterpret_cast<_Float16*>(xa0);              // [TM][kOPitch] over xa0, xa1
+    _Float16* wo = reinterpret_cast<_Float16*>(wb0);              // [TN][kOPitch] over wb0, wb1
+    auto stage = [&](int g) {
+        const int r = tid & 255;
+        const bool xside = tid < 256;
+        const int64_t m = m0 + r < M ? m0 + r : M - 1;
+        const int64_t n = n0 + r < N ? n0 + r : N - 1;
+        const float sn = a.SCB[n];
+#pragma unroll 4
+        for (int p = 0; p < kOGroup; ++p) {
+            const int32_t oi = kOGroup * g + p;
             const bool live = oi < nout;
             const int64_t col = live ? a.oidx[oi] : 0;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                int64_t m = m0 + wm * 64 + 32 * i + fi;
-                m = m < M ? m : M - 1;
-                xo[i][p] = live ? a.X[m * K + col] : (_Float16)0.0f;
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                int64_t n = n0 + wn * 64 + 32 * j + fi;
-                n = n < N ? n : N - 1;
-                const float wd = __fdiv_rn(__fmul_rn((float)a.CB[n * K + col], scb[j]), 127.0f);
-                wo[j][p] = live ? (_Float16)wd : (_Float16)0.0f;
-            }
+            if (xside) xo[r * kOPitch + p] = live ? a.X[m * K + col] : (_Float16)0.0f;
+            else wo[r * kOPitch + p] =
+                live ? (_Float16)__fdiv_rn(__fmul_rn((float)a.CB[n * K + col], sn), 127.0f) : (_Float16)0.0f;
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) f[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xo[i], wo[j], f[i][j], 0, 0, 0);
+    };
+    if (ngroups == 1) {
+        stage(0);
+        __syncthreads();
     }
+    const int64_t mrow = m0 + wm * 64 + 4 * h;                   // + 32 i + 8 b + q
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + wn * 64 + 32 * j + fi;
+        for (int j = 0; j < 4; ++j) {
+            floatx16_t t;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) t[e] = 0.0f;
+            for (int g = 0; g < ngroups; ++g) {
+                if (ngroups > 1) {
+                    __syncthreads();
+                    stage(g);
+                    __syncthreads();
+                }
+#pragma unroll
+                for (int c = 0; c < kOGroup / 16; ++c) {
+                    const halfx8_t xf =
+                        *reinterpret_cast<const halfx8_t*>(xo + (wm * 64 + 32 * i + fi) * kOPitch + 16 * c + 8 * h);
+                    const halfx8_t wf =
+                        *reinterpret_cast<const halfx8_t*>(wo + (wn * 128 + 32 * j + fi) * kOPitch + 16 * c + 8 * h);
+                    t = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf, wf, t, 0, 0, 0);
+                }
+            }
+            const int64_t n = n0 + wn * 128 + 32 * j + fi;
+            const float sn = a.SCB[n < N ? n : N - 1];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * 64 + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
-                if (m < M && n < N) a.Y[m * N + n] = (_Float16)f[i][j][e];
+                const int64_t m = mrow + 32 * i + 8 * (e / 4) + (e % 4);
+                const float sx = a.SX[m < M ? m : M - 1];
+                const float y = __fdiv_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e], sx), sn), 16129.0f) + t[e];
+                if (m < M && n < N) a.Y[m * N + n] = (_Float16)y;
             }
         }
+    }
 }
 
 template <typename InT>
@@ -396,7 +436,8 @@ hipError_t launch_int8_matmul(const int8_t* Xq, const float* SX, const int8_t* C
     a.M = M; a.N = N; a.K = K;
     const int64_t nt = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
     if (nt > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(int8mm_kernel, dim3((unsigned)nt), dim3(kThreads), 0, s, a);
+    if (K % TKB == 0) hipLaunchKernelGGL((int8mm_kernel<false>), dim3((unsigned)nt), dim3(kMmThreads), 0, s, a);
+    else hipLaunchKernelGGL((int8mm_kernel<true>), dim3((unsigned)nt), dim3(kMmThreads), 0, s, a);
     return hipGetLastError();
 }
 
