@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kCopies = 32;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 2;
 constexpr int kUnitElems = kWave * 8;
 
 __device__ __forceinline__ float block_scale(const DeqArgs& a, int64_t blk) {
@@ -105,7 +105,7 @@ hipError_t launch_dequantize(const DeqArgs& a, void* out, int32_t out_dtype, hip
     const int64_t nunits = (a.n + kUnitElems - 1) / kUnitElems;
     const int64_t waves_needed = (nunits + kUnroll - 1) / kUnroll;
     const int64_t wgs_needed = (waves_needed + (kThreads / kWave) - 1) / (kThreads / kWave);
-    const int64_t cap = (int64_t)device_cu_count() * 8;
+    const int64_t cap = (int64_t)device_cu_count() * 16;
     const int grid = (int)(wgs_needed < cap ? wgs_needed : cap);
     if (out_dtype == QK_BF16)
         hipLaunchKernelGGL(dequantize_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a, out);

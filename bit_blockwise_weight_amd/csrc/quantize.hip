@@ -38,8 +38,8 @@ namespace {
 
 constexpr int kQThreads = 256;
 constexpr int kLutCopies = 32;
-constexpr int kUnroll = 4;
-constexpr int kWgsPerCu = 4;
+constexpr int kUnroll = 1;
+constexpr int kWgsPerCu = 8;
 constexpr int kUnitElems = kWave * 8;
 
 constexpr float kAMin = 0x1p-36f;
