@@ -24,7 +24,8 @@
 // loads run two steps ahead; one barrier per step.  Epilogue: C = RN(RN(float(acc) * SX[m])
 // * SCB[n]) / 127^2 in fp32, plus the outlier columns' product computed with
 // v_mfma_f32_32x32x16_f16 from X's fp16 values and the weight columns dequantized
-// to fp16 (CB * SCB / 127), gathered by the workgroup into LDS; fp16 output.
+// to fp16 (CB * SCB / 127), gathered by the workgroup into LDS; fp16 output, each
+// 32 x 32 tile passed through a wave-private LDS area so it leaves in 16-byte stores.
 #include "qk_internal.h"
 #include "qk_device.h"
 #include "qk_quant_io.h"
@@ -338,6 +339,10 @@ __global__ __launch_bounds__(kMmThreads, 1) void int8mm_kernel(MmArgs a) {
         __syncthreads();
     }
     const int64_t mrow = m0 + wm * 64 + 4 * h;                   // + 32 i + 8 b + q
+    // a 2 KB LDS area per wave for the output tile, outside the staged outlier columns
+    // (X part [0, 20 KB), W part [32, 52) KB): waves 0-5 at 20 KB + 2 KB w, 6-7 at 52 KB +
+    uint16_t* yst = reinterpret_cast<uint16_t*>(pool + (wave < 6 ? 20480 + 2048 * wave : 53248 + 2048 * (wave - 6)));
+    const bool vec_ok = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -367,7 +372,24 @@ __global__ __launch_bounds__(kMmThreads, 1) void int8mm_kernel(MmArgs a) {
                 const int64_t m = mrow + 32 * i + 8 * (e / 4) + (e % 4);
                 const float sx = a.SX[m < M ? m : M - 1];
                 const float y = __fdiv_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e], sx), sn), 16129.0f) + t[e];
-                if (m < M && n < N) a.Y[m * N + n] = (_Float16)y;
+                yst[(8 * (e / 4) + 4 * h + (e % 4)) * 32 + fi] = __builtin_bit_cast(uint16_t, (_Float16)y);
+            }
+            // the 32 x 32 tile back from the wave's LDS area, 16 bytes per lane: two
+            // stores, each 16 rows x 64 contiguous bytes
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int row = 16 * half + (lane >> 2), q = lane & 3;
+                const uint4 v = *reinterpret_cast<const uint4*>(yst + row * 32 + 8 * q);
+                const int64_t gm = m0 + wm * 64 + 32 * i + row;
+                const int64_t gn = n0 + wn * 128 + 32 * j + 8 * q;
+                if (gm >= M || gn >= N) continue;
+                uint16_t* dst = reinterpret_cast<uint16_t*>(a.Y) + gm * N + gn;
+                if (vec_ok && gn + 8 <= N) {
+                    *reinterpret_cast<uint4*>(dst) = v;
+                } else {
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                    for (int t8 = 0; t8 < 8 && gn + t8 < N; ++t8) dst[t8] = (uint16_t)(w4[t8 >> 1] >> ((t8 & 1) ? 16 : 0));
+                }
             }
         }
     }
