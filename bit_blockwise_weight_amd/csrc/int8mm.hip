@@ -45,6 +45,19 @@ __device__ __forceinline__ float wave_max64(float v) {
     return fmaxf(as_float(__builtin_amdgcn_readlane(as_uint(v), 0)), as_float(__builtin_amdgcn_readlane(as_uint(v), 32)));
 }
 
+// 8 elements at element offset e (in range, 16-byte aligned): one 16-byte load for
+// 16-bit types, two for fp32, without the tail handling of load_raw
+template <typename InT>
+__device__ __forceinline__ void load8(const void* x, int64_t e, typename RawOf<InT>::type& r) {
+    if constexpr (__is_same(InT, F32In)) {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + e);
+        r[0] = p[0];
+        r[1] = p[1];
+    } else {
+        r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + e);
+    }
+}
+
 __device__ __forceinline__ int32_t quant127(float x, float a) {
     if (a == 0.0f) return 0;
     return (int32_t)__builtin_rintf(__fmul_rn(x / a, 127.0f));
@@ -63,9 +76,10 @@ __global__ __launch_bounds__(kThreads) void rowquant_kernel(const void* __restri
     for (int64_t row = wave; row < rows; row += nwaves) {
         const int64_t rbase = row * cols;
         float am = 0.0f;
+#pragma unroll 4
         for (int64_t k = 8 * lane; k < cols; k += 512) {
             Raw r;
-            load_raw<InT>(x, rbase + cols, rbase + k, r);
+            load8<InT>(x, rbase + k, r);
             float v[8];
             unpack_raw<InT>(r, v);
             uint2 sk = make_uint2(0u, 0u);
@@ -77,9 +91,10 @@ __global__ __launch_bounds__(kThreads) void rowquant_kernel(const void* __restri
             }
         }
         am = wave_max64(am);
+#pragma unroll 4
         for (int64_t k = 8 * lane; k < cols; k += 512) {
             Raw r;
-            load_raw<InT>(x, rbase + cols, rbase + k, r);
+            load8<InT>(x, rbase + k, r);
             float v[8];
             unpack_raw<InT>(r, v);
             uint2 sk = make_uint2(0u, 0u);
@@ -117,9 +132,10 @@ __global__ __launch_bounds__(kThreads) void colmax_kernel(const void* __restrict
     using Raw = typename RawOf<InT>::type;
     float mx[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     if (ok) {
+#pragma unroll 8
         for (int64_t m = r0 + wave; m < r1; m += 4) {
             Raw r;
-            load_raw<InT>(x, (m + 1) * K, m * K + k, r);
+            load8<InT>(x, m * K + k, r);
             float v[8];
             unpack_raw<InT>(r, v);
 #pragma unroll
