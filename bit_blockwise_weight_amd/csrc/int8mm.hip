@@ -117,17 +117,23 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint32_t* __restric
     if (i < n) p[i] = 0u;
 }
 
-// Column maxima of |x|: workgroup (bx, s) takes 512 columns (lane l: [512 bx + 8 l, + 8))
-// and slice s of the rows, its 4 waves every 4th row of the slice; the 4 wave maxima
-// meet in LDS and one atomicMax per column and slice goes to memory.  K % 8 == 0.
+// Column maxima of |x|: a workgroup takes 512 columns (lane l: [512 c + 8 l, + 8)) and
+// one slice of the rows, its 4 waves every 4th row of the slice; the 4 wave maxima
+// meet in LDS and one atomicMax per column and slice goes to memory.  All slices of
+// a column block run on one XCD (workgroup i runs on XCD i % 8), so the atomics on a
+// column stay in that XCD's L2.  K % 8 == 0.
 template <typename InT>
 __global__ __launch_bounds__(kThreads) void colmax_kernel(const void* __restrict__ x, int64_t M, int64_t K,
                                                           int32_t nslices, uint32_t* __restrict__ colmax_bits) {
     __shared__ float part[3][512];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t k = 512 * (int64_t)blockIdx.x + 8 * lane;
+    const int64_t ncb = (K + 511) / 512;
+    const int64_t xcd = blockIdx.x % 8, idx = blockIdx.x / 8;
+    const int64_t cb = xcd + 8 * (idx / nslices);            // column block, on XCD cb % 8
+    const int s = (int)(idx % nslices);
+    if (cb >= ncb) return;
+    const int64_t k = 512 * cb + 8 * lane;
     const bool ok = k < K;
-    const int s = blockIdx.y;
     const int64_t r0 = M * s / nslices, r1 = M * (s + 1) / nslices;
     using Raw = typename RawOf<InT>::type;
     float mx[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -425,14 +431,15 @@ template <typename InT>
 hipError_t launch_colmax_t(const void* x, int64_t M, int64_t K, uint32_t* colmax_bits, hipStream_t s) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((K + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
                        colmax_bits, K);
-    // about 512 workgroups, at least 64 rows per slice
+    // about 512 workgroups, at least 64 rows per slice; column block c on XCD c % 8
     const int64_t colblocks = (K + 511) / 512;
     int64_t slices = (512 + colblocks - 1) / colblocks;
     if (slices > M / 64) slices = M / 64;
     if (slices < 1) slices = 1;
-    if (slices > 65535) slices = 65535;
-    hipLaunchKernelGGL((colmax_kernel<InT>), dim3((unsigned)colblocks, (unsigned)slices), dim3(kThreads), 0, s, x, M, K,
-                       (int32_t)slices, colmax_bits);
+    const int64_t per_xcd = (colblocks + 7) / 8;
+    const int64_t grid = 8 * per_xcd * slices;
+    hipLaunchKernelGGL((colmax_kernel<InT>), dim3((unsigned)grid), dim3(kThreads), 0, s, x, M, K, (int32_t)slices,
+                       colmax_bits);
     return hipGetLastError();
 }
 
