@@ -267,3 +267,26 @@ def test_quantize8_argument_errors(L):
     assert d(ctypes.c_void_p(0x10004), FAKE, 10, 2048, lv, FAKE, qk.QK_F32, None) == qk.QK_ERR_INVALID_ARG
     nan = (ctypes.c_float * 256)(*([float("nan")] + [0.0] * 255))
     assert d(FAKE, FAKE, 10, 2048, nan, FAKE, qk.QK_F32, None) == qk.QK_ERR_INVALID_ARG
+
+
+def test_int8_argument_errors(L):
+    q = L.qk_int8_quantize_rows
+    assert q(None, qk.QK_F16, 4, 64, None, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert q(FAKE, 9, 4, 64, None, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert q(FAKE, qk.QK_F16, 0, 64, None, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert q(FAKE, qk.QK_F16, 4, 60, None, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG     # cols % 8
+    assert q(FAKE, qk.QK_F16, 4, 64, ctypes.c_void_p(0x10004), FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    o = L.qk_int8_outlier_columns
+    assert o(FAKE, qk.QK_F16, 4, 64, 6.0, None, FAKE, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert o(FAKE, qk.QK_F16, 4, 64, -1.0, FAKE, FAKE, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert o(FAKE, qk.QK_F16, 4, 64, float("nan"), FAKE, FAKE, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert o(FAKE, qk.QK_F16, 4, 12, 6.0, FAKE, FAKE, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG  # K % 8
+    m = L.qk_int8_matmul
+    assert m(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, None, None, None, None, None) == qk.QK_ERR_INVALID_ARG
+    assert m(FAKE, FAKE, FAKE, FAKE, 4, 4, 64, FAKE, None, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert "together" in qk.qk_last_error()
+    assert m(FAKE, FAKE, FAKE, FAKE, 4, 4, 8, None, None, None, FAKE, None) == qk.QK_ERR_INVALID_ARG   # K >= 16
+    assert m(FAKE, FAKE, FAKE, FAKE, 4, 4, 72, None, None, None, FAKE, None) == qk.QK_ERR_INVALID_ARG  # K % 16
+    assert m(ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, 4, 4, 64, None, None, None, FAKE, None) \
+        == qk.QK_ERR_INVALID_ARG
+    assert m(FAKE, FAKE, FAKE, FAKE, 0, 4, 64, None, None, None, FAKE, None) == qk.QK_ERR_INVALID_ARG
