@@ -440,7 +440,10 @@ const char* qk_backend_info(void) {
     static thread_local std::string s;
     s = std::string("quantize: wave per 512 elements, DPP block absmax, reciprocal+Markstein division, LDS bin table; ") +
         "double_quant: fp64 tree partials + int8 per 256; dequantize: LDS levels; gemv: " + g_gemv_variant +
-        "; gemm: " + g_gemm_variant;
+        "; gemm: " + g_gemm_variant +
+        "; lora_merge: fp32 adapter sum in LDS, fused dequant; qlora_backward: dX 256x128 tiles mfma 32x32x16 bf16 with "
+        "W^T dequantized into LDS, dA/dB row-slice reductions; quantize_8bit: LDS bin table built per workgroup; "
+        "int8_matmul: mfma 32x32x32 i8 256x256 tiles 8 waves, fp16 outlier mfma in the epilogue";
     return s.c_str();
 }
 
