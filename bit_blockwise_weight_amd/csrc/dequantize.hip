@@ -30,14 +30,20 @@ __device__ __forceinline__ float block_scale(const DeqArgs& a, int64_t blk) {
 template <bool kBf16Out>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(DeqArgs a, void* __restrict__ out) {
     __shared__ float lev[16 * kCopies];
-    for (int i = threadIdx.x; i < 16 * kCopies; i += kThreads) lev[i] = a.levels[i / kCopies];
+    // copy t % 32 of levels t / 32 and t / 32 + 8 (both loaded before either is written)
+    static_assert(kCopies == 32 && kThreads == 256, "the fill assumes 32 copies and 256 threads");
+    {
+        const float l0 = a.levels[threadIdx.x / kCopies], l1 = a.levels[threadIdx.x / kCopies + 8];
+        lev[threadIdx.x] = l0;
+        lev[threadIdx.x + kThreads] = l1;
+    }
     __syncthreads();
 
     const int lane = threadIdx.x & (kWave - 1);
     const int copy = lane & (kCopies - 1);
     const int64_t n = a.n;
     const int64_t nunits = (n + kUnitElems - 1) / kUnitElems;
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
 
     for (int64_t u0 = wave * kUnroll; u0 < nunits; u0 += nwaves * kUnroll) {

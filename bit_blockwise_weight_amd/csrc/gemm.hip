@@ -429,9 +429,20 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
         n0 = (int64_t)(in_group / gm) * TN;
     }
 
-    for (int i = tid; i < 256 * kCopies; i += 256) {
-        const int b = i / kCopies;
-        tab[i] = make_uint2(as_uint(a.w.levels[b >> 4]), as_uint(a.w.levels[b & 15]));
+    {
+        // entry of byte b = 16 hi + lo: (level[hi], level[lo]).  Thread t writes copy t % 32
+        // of the bytes with lo = t / 32 and t / 32 + 8, for every hi: the two lo levels are
+        // loaded once and the hi levels are uniform (scalar loads), so filling the table
+        // costs one memory round trip, not one per entry
+        static_assert(kCopies == 32, "the fill assumes 32 copies and 256 threads");
+        const int c = tid & (kCopies - 1), lo = tid / kCopies;
+        const uint32_t l0 = as_uint(a.w.levels[lo]), l1 = as_uint(a.w.levels[lo + 8]);
+#pragma unroll
+        for (int hi = 0; hi < 16; ++hi) {
+            const uint32_t h = as_uint(a.w.levels[hi]);
+            tab[(16 * hi + lo) * kCopies + c] = make_uint2(h, l0);
+            tab[(16 * hi + lo + 8) * kCopies + c] = make_uint2(h, l1);
+        }
     }
 
     int64_t wrow[2], wrow_c[2];

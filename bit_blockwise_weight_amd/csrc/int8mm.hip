@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void rowquant_kernel(const void* __restri
                                                             const uint8_t* __restrict__ skip, int8_t* __restrict__ q,
                                                             float* __restrict__ absmax) {
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
     using Raw = typename RawOf<InT>::type;
     for (int64_t row = wave; row < rows; row += nwaves) {

@@ -45,7 +45,13 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(MergeArgs a) {
     __shared__ float Bs[kRankChunk][kRows];      // 4 KB
     __shared__ float lev[16 * kCopies];          // 2 KB
     const int tid = threadIdx.x;
-    for (int i = tid; i < 16 * kCopies; i += kThreads) lev[i] = a.w.levels[i / kCopies];
+    // copy t % 32 of levels t / 32 and t / 32 + 8 (both loaded before either is written)
+    static_assert(kCopies == 32 && kThreads == 256, "the fill assumes 32 copies and 256 threads");
+    {
+        const float l0 = a.w.levels[tid / kCopies], l1 = a.w.levels[tid / kCopies + 8];
+        lev[tid] = l0;
+        lev[tid + kThreads] = l1;
+    }
 
     const int64_t k0 = (int64_t)blockIdx.x * kCols;
     const int64_t n0 = (int64_t)blockIdx.y * kRows;

@@ -49,6 +49,19 @@ __device__ __forceinline__ void load_raw(const void* x, int64_t n, int64_t base,
     }
 }
 
+// The same for a lane whose 8 elements are known to be in range: no branch, so the
+// compiler can leave the load in flight across unrelated code.
+template <typename T>
+__device__ __forceinline__ void load_raw_full(const void* x, int64_t base, typename RawOf<T>::type& r) {
+    if constexpr (__is_same(T, F32In)) {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + base);
+        r[0] = p[0];
+        r[1] = p[1];
+    } else {
+        r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ void unpack_raw(const typename RawOf<T>::type& r, float v[8]) {
     if constexpr (__is_same(T, F32In)) {
@@ -64,6 +77,43 @@ __device__ __forceinline__ void unpack_raw(const typename RawOf<T>::type& r, flo
         v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
         v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
         v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+    }
+}
+
+// Largest and smallest |x| of a lane's 8 elements, from the raw words: the bit
+// pattern of a non-negative float orders like the value, so both are integer
+// max / min of the patterns with the sign cleared (two 16-bit halves at a time for
+// bf16 / fp16).  Finite input.
+template <typename T>
+__device__ __forceinline__ void abs_range_raw(const typename RawOf<T>::type& r, float& amax, float& amin) {
+    if constexpr (__is_same(T, F32In)) {
+        const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+        uint32_t hi = w[0] & 0x7FFFFFFFu, lo = hi;
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            const uint32_t a = w[i] & 0x7FFFFFFFu;
+            hi = max(hi, a);
+            lo = min(lo, a);
+        }
+        amax = as_float(hi);
+        amin = as_float(lo);
+    } else {
+        typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+        const u16x2_t a0 = __builtin_bit_cast(u16x2_t, r.x & 0x7FFF7FFFu);
+        const u16x2_t a1 = __builtin_bit_cast(u16x2_t, r.y & 0x7FFF7FFFu);
+        const u16x2_t a2 = __builtin_bit_cast(u16x2_t, r.z & 0x7FFF7FFFu);
+        const u16x2_t a3 = __builtin_bit_cast(u16x2_t, r.w & 0x7FFF7FFFu);
+        const u16x2_t mx = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1), __builtin_elementwise_max(a2, a3));
+        const u16x2_t mn = __builtin_elementwise_min(__builtin_elementwise_min(a0, a1), __builtin_elementwise_min(a2, a3));
+        const uint32_t hi = max((uint32_t)mx.x, (uint32_t)mx.y);
+        const uint32_t lo = min((uint32_t)mn.x, (uint32_t)mn.y);
+        if constexpr (__is_same(T, F16In)) {
+            amax = h2f(hi);
+            amin = h2f(lo);
+        } else {
+            amax = as_float(hi << 16);
+            amin = as_float(lo << 16);
+        }
     }
 }
 

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void quantize8_kernel(const void* __restr
     const uint32_t bin_cap = 0x4B000000u + (uint32_t)(lut.nbins - 1);
     const int64_t nunits = (n + E - 1) / E;
     const int64_t nblocks = (n + B - 1) / B;
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + tid / kWave;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(tid / kWave);
     const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
 
     // fp32: lane l holds elements [512 u + 4 l, + 4) and [512 u + 256 + 4 l, + 4) (two
@@ -224,11 +224,21 @@ __global__ __launch_bounds__(kThreads) void dequantize8_kernel(const uint8_t* __
     constexpr int V = kBf16Out ? 8 : 4;
     constexpr int Q = 1024 / (64 * V);
     __shared__ float tab[256 * kCopies];
-    for (int i = threadIdx.x; i < 256 * kCopies; i += kThreads) tab[i] = lv.v[i / kCopies];
+    {
+        // copy t % 32 of the levels t / 32 + 8 j, j < 32: all 32 loads are issued before the
+        // first write, so the fill costs one memory round trip
+        static_assert(kCopies == 32 && kThreads == 256, "the fill assumes 32 copies and 256 threads");
+        const int c = threadIdx.x & (kCopies - 1), v0 = threadIdx.x / kCopies;
+        float lvv[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) lvv[j] = lv.v[v0 + 8 * j];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) tab[(v0 + 8 * j) * kCopies + c] = lvv[j];
+    }
     __syncthreads();
     const int lane = threadIdx.x & (kWave - 1);
     const int copy = lane & (kCopies - 1);
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
     const int64_t ngroups = (n + 1023) / 1024;
     for (int64_t g = wave; g < ngroups; g += nwaves) {
