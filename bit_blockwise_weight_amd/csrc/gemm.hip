@@ -349,8 +349,9 @@ hipError_t launch_typed(const GemmArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Fast path: 256 x 256 output tile, K step 64, 4 waves.  Wave w owns weight
-// rows [64w, 64w + 64) of the tile (two 32-column MFMA tiles) and all 256 token
+// Fast path: 256 x 256 output tile, K step 64, 8 waves (two per SIMD, so one
+// wave's dequantization runs while the other's MFMAs do).  Wave w owns weight
+// rows [32w, 32w + 32) of the tile (one 32-column MFMA tile) and all 256 token
 // rows (eight 32-row MFMA tiles), so each weight of the tile is dequantized by
 // exactly one lane of one wave, straight into MFMA B-fragment registers:
 //   lane l = (j = l % 32, g = l / 32) holds the 16 code bytes of weights
@@ -360,12 +361,16 @@ hipError_t launch_typed(const GemmArgs& a, hipStream_t s) {
 //   bf16(RN(level * a')) that qk_dequantize writes.  Quarter q of the step (8
 //   weights) is the B operand of the q-th 16-deep MFMA; the A operand is
 //   X[row][64s + 32g + 8q .. +8] from LDS, the same k order.
-// Pipeline (one barrier per step):
-//   * at the start of step s the X tile of step s + 1 is loaded straight into the
-//     other LDS buffer (global_load_lds_dwordx4, no staging registers) and the
-//     codes of step s + 2 into registers;
-//   * the B fragments of the next quarter are dequantized while the 16 MFMAs of
-//     the current quarter run.
+// Pipeline:
+//   * X tiles go into two LDS buffers by buffer loads with the LDS bit; the codes
+//     are loaded into registers two steps ahead;
+//   * in a quarter, each MFMA is followed by the read of its row tile's A fragment
+//     for the next quarter; halfway through, the next quarter's B fragment is
+//     scaled from table reads issued a quarter earlier, and the table reads for the
+//     quarter after it are issued;
+//   * one barrier per step, after its third quarter: by then every wave has read
+//     the step's X buffer (it can take X of step s + 2) and X of step s + 1 has
+//     landed (the fourth quarter reads the next step's first A fragments).
 // X rows are 128 bytes in LDS with the 16-byte chunks XOR-swizzled by the row
 // (chunk c of row r sits in slot c ^ ((r >> 1) & 7)), so the fragment reads of
 // 16 consecutive rows hit 16 different bank groups (no LDS bank conflicts).
@@ -380,7 +385,6 @@ constexpr int kSplits = 8;                // K splits of the LoRA X*A pre-pass
 constexpr int kXcds = 8;                  // MI355X: 8 XCDs, workgroups dealt round robin
 constexpr int kGroupM = 4;                // tile rows per group in the tile order
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 __device__ __forceinline__ uint32_t xoff(int row, int chunk) {   // byte offset in an X tile
@@ -388,19 +392,22 @@ __device__ __forceinline__ uint32_t xoff(int row, int chunk) {   // byte offset 
 }
 
 template <int R16, bool kNested>
-__global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const float* __restrict__ T) {
+__global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const float* __restrict__ T) {
+    constexpr int kThr = 512;                          // 8 waves, two per SIMD
     constexpr int kRp = 16 * R16;
     constexpr int kTs = 16 + 8;                        // row pitch of a staged 16-rank chunk of s X A
     // r <= 16: the one chunk of s X A is staged in the prologue; larger ranks stage
     // their chunks one after another after the K loop
     constexpr bool kTEarly = R16 == 1;
-    constexpr int kCodeLoads = kNested ? 6 : 4;     // global loads issued by load_codes
+    constexpr int kCodeLoads = kNested ? 3 : 2;     // global loads issued by load_codes
     // Separate LDS objects: the compiler then knows that reads of one X buffer, of the
-    // table or of the LoRA chunk never alias the direct-to-LDS loads into the other X
-    // buffer, and does not wait for those loads before every LDS read.
+    // table or of the LoRA chunk never alias the loads into the other X buffer, and does
+    // not wait for those loads before every LDS read.  The table has the largest
+    // alignment, so it sits at LDS address 0 and its byte addresses are the v_perm
+    // results themselves.
     __shared__ __attribute__((aligned(1024))) uint4 xsA[TM * 8];          // X tile buffer 0, 32 KB
     __shared__ __attribute__((aligned(1024))) uint4 xsB[TM * 8];          // X tile buffer 1, 32 KB
-    __shared__ __attribute__((aligned(16))) uint2 tab[256 * kCopies];     // fp32 level pairs, 64 KB
+    __shared__ __attribute__((aligned(65536))) uint2 tab[256 * kCopies];  // fp32 level pairs, 64 KB
     __shared__ __attribute__((aligned(16))) uint16_t tst[2 * TM * kTs];   // s X A chunk, bf16 hi | lo, 24 KB
 
     const int tid = threadIdx.x;
@@ -413,10 +420,6 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
     const int r = a.r;
     int64_t m0, n0;
     {
-        // Tile order.  Workgroup i runs on XCD i % 8, and each XCD has its own L2, so the
-        // tiles of an XCD are made a compact group: the 1-D id is first regrouped so that
-        // XCD x gets consecutive logical ids, then logical ids walk groups of kGroupM tile
-        // rows column by column.  The XCD's tiles then share X rows and W columns in L2.
         const uint32_t tiles_n = (uint32_t)((N + TN - 1) / TN), tiles_m = (uint32_t)((M + TM - 1) / TM);
         const uint32_t nt = tiles_n * tiles_m;
         const uint32_t bid = blockIdx.x;
@@ -428,261 +431,263 @@ __global__ __launch_bounds__(256, 1) void gemm_fast_kernel(GemmArgs a, const flo
         m0 = (int64_t)(first_m + in_group % gm) * TM;
         n0 = (int64_t)(in_group / gm) * TN;
     }
-
     {
         // entry of byte b = 16 hi + lo: (level[hi], level[lo]).  Thread t writes copy t % 32
-        // of the bytes with lo = t / 32 and t / 32 + 8, for every hi: the two lo levels are
-        // loaded once and the hi levels are uniform (scalar loads), so filling the table
-        // costs one memory round trip, not one per entry
-        static_assert(kCopies == 32, "the fill assumes 32 copies and 256 threads");
+        // of the bytes with lo = t / 32, for every hi: the lo level is loaded once and the
+        // hi levels are uniform (scalar loads), so the fill costs one memory round trip
+        static_assert(kCopies == 32, "the fill assumes 32 copies and 512 threads");
         const int c = tid & (kCopies - 1), lo = tid / kCopies;
-        const uint32_t l0 = as_uint(a.w.levels[lo]), l1 = as_uint(a.w.levels[lo + 8]);
+        const uint32_t l0 = as_uint(a.w.levels[lo]);
 #pragma unroll
-        for (int hi = 0; hi < 16; ++hi) {
-            const uint32_t h = as_uint(a.w.levels[hi]);
-            tab[(16 * hi + lo) * kCopies + c] = make_uint2(h, l0);
-            tab[(16 * hi + lo + 8) * kCopies + c] = make_uint2(h, l1);
-        }
+        for (int hi = 0; hi < 16; ++hi) tab[(16 * hi + lo) * kCopies + c] = make_uint2(as_uint(a.w.levels[hi]), l0);
     }
 
-    int64_t wrow[2], wrow_c[2];
-    bool wok[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        wrow[ct] = n0 + 64 * wave + 32 * ct + j;
-        wok[ct] = wrow[ct] < N;
-        wrow_c[ct] = wok[ct] ? wrow[ct] : N - 1;
-    }
+    // this wave's 32 weight rows (one MFMA column tile)
+    const int64_t wrow = n0 + 32 * wave + j;
+    const bool wok = wrow < N;
+    const int64_t wrow_c = wok ? wrow : N - 1;
     const uint32_t lane_sel = (uint32_t)(lane & (kCopies - 1)) * 8u;
     const char* tabb = reinterpret_cast<const char*>(tab);
     const float mean = kNested ? *a.w.dq_mean : 0.0f;
 
-    // LoRA: B fragments of a 16-rank chunk, and the chunk of s X A as bf16 hi / lo in LDS
     uint16_t* thi = tst;
     uint16_t* tlo = tst + TM * kTs;
-    auto load_lora_b = [&](int kk, bf16x8_t (&bl)[2]) {
+    auto load_lora_b = [&](int kk) {
+        uint32_t e[8];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            // unconditional loads (clamped indices); ranks >= r are zeroed afterwards
-            uint32_t e[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int jj = kk + 8 * g + t;
-                e[t] = (uint32_t)a.B[(int64_t)(jj < r ? jj : r - 1) * N + wrow_c[ct]];
-            }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) e[t] = (kk + 8 * g + t < r) ? e[t] : 0u;
-            bl[ct] = __builtin_bit_cast(bf16x8_t, make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16),
-                                                             e[4] | (e[5] << 16), e[6] | (e[7] << 16)));
+        for (int t = 0; t < 8; ++t) {
+            const int jj = kk + 8 * g + t;
+            e[t] = (uint32_t)a.B[(int64_t)(jj < r ? jj : r - 1) * N + wrow_c];
         }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) e[t] = (kk + 8 * g + t < r) ? e[t] : 0u;
+        return __builtin_bit_cast(bf16x8_t, make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16),
+                                                       e[4] | (e[5] << 16), e[6] | (e[7] << 16)));
     };
     auto stage_t = [&](int kk) {
-        // thread t: row t of the tile, ranks [kk, kk + 16)
-        const int64_t gm = m0 + tid < M ? m0 + tid : M - 1;
+        if (tid < TM) {
+            const int64_t gm = m0 + tid < M ? m0 + tid : M - 1;
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            // s X A = sum of the pre-pass K splits, added in split order
-            float4 sum = *reinterpret_cast<const float4*>(T + gm * kRp + kk + 4 * c4);
+            for (int c4 = 0; c4 < 4; ++c4) {
+                float4 sum = *reinterpret_cast<const float4*>(T + gm * kRp + kk + 4 * c4);
 #pragma unroll
-            for (int sp = 1; sp < kSplits; ++sp) {
-                const float4 t = *reinterpret_cast<const float4*>(T + (sp * M + gm) * kRp + kk + 4 * c4);
-                sum.x += t.x; sum.y += t.y; sum.z += t.z; sum.w += t.w;
+                for (int sp = 1; sp < kSplits; ++sp) {
+                    const float4 t = *reinterpret_cast<const float4*>(T + (sp * M + gm) * kRp + kk + 4 * c4);
+                    sum.x += t.x; sum.y += t.y; sum.z += t.z; sum.w += t.w;
+                }
+                const uint32_t h01 = pack_bf16x2(sum.x, sum.y), h23 = pack_bf16x2(sum.z, sum.w);
+                const uint32_t l01 = pack_bf16x2(sum.x - as_float(h01 << 16), sum.y - as_float(h01 & 0xFFFF0000u));
+                const uint32_t l23 = pack_bf16x2(sum.z - as_float(h23 << 16), sum.w - as_float(h23 & 0xFFFF0000u));
+                *reinterpret_cast<uint2*>(&thi[tid * kTs + 4 * c4]) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2*>(&tlo[tid * kTs + 4 * c4]) = make_uint2(l01, l23);
             }
-            const uint32_t h01 = pack_bf16x2(sum.x, sum.y), h23 = pack_bf16x2(sum.z, sum.w);
-            const uint32_t l01 = pack_bf16x2(sum.x - as_float(h01 << 16), sum.y - as_float(h01 & 0xFFFF0000u));
-            const uint32_t l23 = pack_bf16x2(sum.z - as_float(h23 << 16), sum.w - as_float(h23 & 0xFFFF0000u));
-            *reinterpret_cast<uint2*>(&thi[tid * kTs + 4 * c4]) = make_uint2(h01, h23);
-            *reinterpret_cast<uint2*>(&tlo[tid * kTs + 4 * c4]) = make_uint2(l01, l23);
         }
     };
-    bf16x8_t bl_early[2];
-    if constexpr (kTEarly) {
-        load_lora_b(0, bl_early);
-        stage_t(0);
-    }
+    if constexpr (kTEarly) stage_t(0);
 
-    // X tile rows loaded by this lane (clamped to the last valid row: rows past M
-    // only feed output rows that are never stored)
-    const uint16_t* xsrc[8];
+    // X tiles: buffer loads with the LDS bit, 4 pieces of 16 bytes per lane and step.
+    // Unlike the global (FLAT-encoded) form, these do not make the compiler drain every
+    // LDS-read wait to zero while they are in flight.  The resource covers the tile's
+    // rows; offsets are bytes from the tile's first row (rows past M are clamped to the
+    // last row: they only feed output rows that are never stored).
+    const uint16_t* xtile = a.X + m0 * K;
+    const int64_t xbytes = (M - m0) * K * 2;
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(xtile), (short)0, (int)(xbytes < 0x7FFFFFFFll ? xbytes : 0x7FFFFFFFll), 0x00020000);
+    uint32_t xsrc[4];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-        const int p = (v * 4 + wave) * 64 + lane;          // LDS 16-byte slot written by this lane
+    for (int v = 0; v < 4; ++v) {
+        const int p = (v * 8 + wave) * 64 + lane;          // LDS 16-byte slot written by this lane
         const int row = p >> 3, slot = p & 7;
         const int chunk = slot ^ ((row >> 1) & 7);
         const int64_t gm = m0 + row < M ? m0 + row : M - 1;
-        xsrc[v] = a.X + gm * K + chunk * 8;
+        xsrc[v] = (uint32_t)(((gm - m0) * K + chunk * 8) * 2);
     }
     auto load_x = [&](int64_t s, auto buf) {
-        const int64_t k0 = (s < nk1 ? s : nk1) * TK;
+        const int32_t kbytes = (int32_t)((s < nk1 ? s : nk1) * TK * 2);
         char* base = reinterpret_cast<char*>(decltype(buf)::value ? xsB : xsA);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            lptr_t dst = (lptr_t)((__attribute__((address_space(3))) char*)base + (v * 4 + wave) * 1024);
-            __builtin_amdgcn_global_load_lds((gptr_t)(xsrc[v] + k0), dst, 16, 0, 0);
+        for (int v = 0; v < 4; ++v) {
+            lptr_t dst = (lptr_t)((__attribute__((address_space(3))) char*)base + (v * 8 + wave) * 1024);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, (int32_t)xsrc[v], kbytes, 0, 0);
         }
     };
 
-    // codes + raw scale words of a step (c[ct] = 16 bytes; q = q8 or absmax bits; d = dq scale)
     struct Codes {
-        uint4 c[2];
-        int32_t q[2];
-        float d[2];
+        uint4 c;
+        int32_t q;
+        float d;
     };
     auto load_codes = [&](int64_t s, Codes& cs) {
         const int64_t k0 = (s < nk1 ? s : nk1) * TK;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int64_t e0 = wrow_c[ct] * K + k0 + 32 * g;
-            const int64_t blk = e0 >> a.w.blocksize_log2;
-            cs.c[ct] = *reinterpret_cast<const uint4*>(a.w.codes + e0 / 2);
-            if constexpr (kNested) {
-                cs.q[ct] = (int32_t)a.w.q8[blk];
-                cs.d[ct] = a.w.dq_scale[blk / QK_DQ_BLOCK];
-            } else {
-                cs.q[ct] = (int32_t)as_uint(a.w.absmax[blk]);
-                cs.d[ct] = 1.0f;
-            }
+        const int64_t e0 = wrow_c * K + k0 + 32 * g;
+        const int64_t blk = e0 >> a.w.blocksize_log2;
+        cs.c = *reinterpret_cast<const uint4*>(a.w.codes + e0 / 2);
+        if constexpr (kNested) {
+            cs.q = (int32_t)a.w.q8[blk];
+            cs.d = a.w.dq_scale[blk / QK_DQ_BLOCK];
+        } else {
+            cs.q = (int32_t)as_uint(a.w.absmax[blk]);
+            cs.d = 1.0f;
         }
     };
-    auto scale_of = [&](const Codes& cs, int ct) {
+    auto scale_of = [&](const Codes& cs) {
         float sc;
-        if constexpr (kNested) sc = __fadd_rn(__fmul_rn((float)cs.q[ct], cs.d[ct]), mean);
-        else sc = as_float((uint32_t)cs.q[ct]);
+        if constexpr (kNested) sc = __fadd_rn(__fmul_rn((float)cs.q, cs.d), mean);
+        else sc = as_float((uint32_t)cs.q);
         return sc;
     };
-    // B fragments of quarter q of a step: for each column tile, dword q of its codes
-    auto dequant_q = [&](const Codes& cs, int q, bf16x8_t (&dst)[2]) {
+    auto lookup_q = [&](const Codes& cs, int q, uint2 (&lv)[4]) {
+        const uint32_t cw = q == 0 ? cs.c.x : q == 1 ? cs.c.y : q == 2 ? cs.c.z : cs.c.w;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const float sc = scale_of(cs, ct);
-            const uint32_t cw = q == 0 ? cs.c[ct].x : q == 1 ? cs.c[ct].y : q == 2 ? cs.c[ct].z : cs.c[ct].w;
-            uint32_t d[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t addr = __builtin_amdgcn_perm(cw, lane_sel, 0x0C0C0400u | ((uint32_t)(4 + b) << 8));
-                const uint2 lv = *reinterpret_cast<const uint2*>(tabb + addr);
-                d[b] = pack_bf16x2(__fmul_rn(as_float(lv.x), sc), __fmul_rn(as_float(lv.y), sc));
-            }
-            dst[ct] = __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+        for (int bb = 0; bb < 4; ++bb) {
+            const uint32_t addr = __builtin_amdgcn_perm(cw, lane_sel, 0x0C0C0400u | ((uint32_t)(4 + bb) << 8));
+            lv[bb] = *reinterpret_cast<const uint2*>(tabb + addr);
         }
     };
+    auto finish_q = [&](float sc, const uint2 (&lv)[4]) {
+        uint32_t d[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) d[bb] = pack_bf16x2(__fmul_rn(as_float(lv[bb].x), sc), __fmul_rn(as_float(lv[bb].y), sc));
+        return __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+    };
 
-    floatx16_t acc[8][2];
+    floatx16_t acc[8];
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[rt][ct][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) acc[rt][e] = 0.0f;
 
     using Buf0 = std::integral_constant<int, 0>;
     using Buf1 = std::integral_constant<int, 1>;
-    Codes c0, c1, c2, c3;          // codes of steps s .. s + 3
+    Codes c0, c1, c2;              // codes of steps s .. s + 2
     load_codes(0, c0);
     load_codes(1, c1);
-    load_codes(2, c2);
     load_x(0, Buf0{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();               // table and X(0) in LDS
-    bf16x8_t bq[2];
-    dequant_q(c0, 0, bq);
-    __syncthreads();
+    load_x(1, Buf1{});
 
+    // A fragments of the current quarter; each is replaced by the next quarter's right
+    // after its MFMA is issued
+    bf16x8_t af[8];
+    uint2 lv[4];                   // table reads of the B fragment two quarters ahead
+    bf16x8_t bq;
+    {
+        const char* xbb = reinterpret_cast<const char*>(xsA);
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) af[rt] = *reinterpret_cast<const bf16x8_t*>(xbb + xoff(32 * rt + j, 4 * g));
+        lookup_q(c0, 0, lv);
+        bq = finish_q(scale_of(c0), lv);
+        lookup_q(c0, 1, lv);
+    }
+
+    // One quarter, in this order (the scheduling barriers keep it): for each row tile its
+    // MFMA and the read of its A fragment for the next quarter; after the fourth, the
+    // scaling of the next quarter's B fragment (from table reads issued half a quarter
+    // earlier) and the table reads for the quarter after it.  LDS reads return in order;
+    // with this order every MFMA's wait leaves the 11 reads issued after its A fragment
+    // outstanding, and the scaling waits only for table reads 4 MFMAs old.
+    auto quarter = [&](const uint4* xa, int qa, float sc_cur, const Codes& cs_nn, int qnn) {
+        const char* xbb = reinterpret_cast<const char*>(xa);
+        bf16x8_t bn;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rt], bq, acc[rt], 0, 0, 0);
+            af[rt] = *reinterpret_cast<const bf16x8_t*>(xbb + xoff(32 * rt + j, 4 * g + qa));
+            if (rt == 3) {
+                bn = finish_q(sc_cur, lv);
+                lookup_q(cs_nn, qnn, lv);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bq = bn;
+    };
     // One K step: ca = codes of step s, cb = codes of step s + 1, cn receives the codes
-    // of step s + 3; X of step s is in buffer s % 2.  Codes are loaded three steps ahead
-    // so that a load issued in step s is complete by the barrier of step s + 1, before
-    // anything of step s + 2 (its first user) runs.  The loop is unrolled four times so
-    // that the code buffers rotate by name (a register copy would wait for its load) and
-    // every X buffer is a fixed LDS object.
+    // of step s + 2; X of step s is in buffer s % 2, X of step s + 1 is on its way into
+    // the other buffer.
     auto step = [&](int64_t s, auto buf, const Codes& ca, const Codes& cb, Codes& cn) {
         constexpr bool kB = decltype(buf)::value;
-        // loads for later steps, issued first so they have the whole step
-        if constexpr (kB) load_x(s + 1, Buf0{});
-        else load_x(s + 1, Buf1{});
-        load_codes(s + 3, cn);
-        const char* xbb = reinterpret_cast<const char*>(kB ? xsB : xsA);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bf16x8_t bn[2];
-            if (q < 3) dequant_q(ca, q + 1, bn);
-            else dequant_q(cb, 0, bn);
-#pragma unroll
-            for (int rt = 0; rt < 8; ++rt) {
-                const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(xbb + xoff(32 * rt + j, 4 * g + q));
-                acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bq[0], acc[rt][0], 0, 0, 0);
-                acc[rt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bq[1], acc[rt][1], 0, 0, 0);
-            }
-            bq[0] = bn[0];
-            bq[1] = bn[1];
-        }
-        // X(s + 1) has landed in LDS once at most the code loads of step s + 3 (issued
-        // after it) are outstanding; those stay in flight across the barrier.  A plain
-        // s_barrier: __syncthreads() would add a release fence, which waits for every
-        // outstanding global load.  The empty asm statements keep the compiler from
-        // moving memory accesses across the barrier.
+        const uint4* xcur = kB ? xsB : xsA;
+        const uint4* xnxt = kB ? xsA : xsB;
+        load_codes(s + 2, cn);
+        const float sa = scale_of(ca);
+        __builtin_amdgcn_sched_barrier(0);
+        quarter(xcur, 1, sa, ca, 2);
+        quarter(xcur, 2, sa, ca, 3);
+        quarter(xcur, 3, sa, cb, 0);
+        // X(s + 1) has landed once at most the code loads of step s + 2 are outstanding.
+        // A plain s_barrier: __syncthreads() would add a release fence, which waits for
+        // every outstanding global load.
         __builtin_amdgcn_s_waitcnt(kCodeLoads | 0x70);   // vmcnt(kCodeLoads) expcnt(7) lgkmcnt(0)
-        asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kB) load_x(s + 2, Buf1{});
+        else load_x(s + 2, Buf0{});
+        const float sb = scale_of(cb);
+        __builtin_amdgcn_sched_barrier(0);
+        quarter(xnxt, 0, sb, cb, 1);
     };
-    for (int64_t s = 0; s < nk; s += 4) {
-        step(s, Buf0{}, c0, c1, c3);
-        if (s + 1 < nk) step(s + 1, Buf1{}, c1, c2, c0);
-        if (s + 2 < nk) step(s + 2, Buf0{}, c2, c3, c1);
-        if (s + 3 < nk) step(s + 3, Buf1{}, c3, c0, c2);
+    // whole groups of 6 steps (3 code sets x 2 X buffers) without conditions inside (a
+    // condition between steps merges the compiler's wait-count state across paths and
+    // makes its waits conservative), then the 0-5 remaining steps
+    const int64_t nk6 = nk - nk % 6;
+    int64_t s = 0;
+    for (; s < nk6; s += 6) {
+        step(s, Buf0{}, c0, c1, c2);
+        step(s + 1, Buf1{}, c1, c2, c0);
+        step(s + 2, Buf0{}, c2, c0, c1);
+        step(s + 3, Buf1{}, c0, c1, c2);
+        step(s + 4, Buf0{}, c1, c2, c0);
+        step(s + 5, Buf1{}, c2, c0, c1);
     }
+    if (s < nk) step(s, Buf0{}, c0, c1, c2);
+    if (s + 1 < nk) step(s + 1, Buf1{}, c1, c2, c0);
+    if (s + 2 < nk) step(s + 2, Buf0{}, c2, c0, c1);
+    if (s + 3 < nk) step(s + 3, Buf1{}, c0, c1, c2);
+    if (s + 4 < nk) step(s + 4, Buf0{}, c1, c2, c0);
     __builtin_amdgcn_s_waitcnt(0);   // the last (clamped, unused) prefetches
     __syncthreads();
 
     if constexpr (R16 > 0) {
-        // LoRA: acc += (s X A) B, 16 ranks at a time; s X A as bf16 hi + lo (about 16
-        // significant bits together)
 #pragma unroll
         for (int kk = 0; kk < kRp; kk += 16) {
-            bf16x8_t bl[2];
+            bf16x8_t bl;
             if constexpr (kTEarly) {
-                bl[0] = bl_early[0];
-                bl[1] = bl_early[1];
+                bl = load_lora_b(0);
             } else {
-                if (kk > 0) __syncthreads();      // the previous chunk has been read
+                if (kk > 0) __syncthreads();
                 stage_t(kk);
-                load_lora_b(kk, bl);
+                bl = load_lora_b(kk);
                 __syncthreads();
             }
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
                 const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&thi[(32 * rt + j) * kTs + 8 * g]);
                 const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&tlo[(32 * rt + j) * kTs + 8 * g]);
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[ct], acc[rt][ct], 0, 0, 0);
-                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bl[ct], acc[rt][ct], 0, 0, 0);
-                }
+                acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[rt], 0, 0, 0);
+                acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bl, acc[rt], 0, 0, 0);
             }
         }
     }
 
-    // epilogue: stage the bf16 tile in LDS 64 rows at a time (64 rows x 512 bytes = one X
-    // buffer, alternating), then write Y with 16-byte row-contiguous stores.  Register e
-    // of MFMA tile (rt, ct) holds C[32 rt + 8(e/4) + 4g + e%4][64 wave + 32 ct + j].
+    // epilogue: the bf16 tile through LDS 64 rows at a time, then 16-byte row stores.
+    // Register e of tile rt holds C[32 rt + 8(e/4) + 4g + e%4][32 wave + j].
     const bool vec_ok = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
         uint16_t* cs = reinterpret_cast<uint16_t*>((pass & 1) ? xsB : xsA);
 #pragma unroll
         for (int rt = 2 * pass; rt < 2 * pass + 2; ++rt) {
+            const int col = 32 * wave + j;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int col = 64 * wave + 32 * ct + j;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = 32 * (rt - 2 * pass) + 8 * (e / 4) + 4 * g + (e % 4);
-                    cs[row * TN + col] = (uint16_t)(pack_bf16x2(acc[rt][ct][e], 0.0f) & 0xFFFFu);
-                }
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * (rt - 2 * pass) + 8 * (e / 4) + 4 * g + (e % 4);
+                cs[row * TN + col] = (uint16_t)(pack_bf16x2(acc[rt][e], 0.0f) & 0xFFFFu);
             }
         }
         __syncthreads();
-        for (int c = tid; c < (TM / 4) * (TN / 8); c += 256) {
+        for (int c = tid; c < (TM / 4) * (TN / 8); c += kThr) {
             const int row = c / (TN / 8), ch = c % (TN / 8);
             const int64_t gm = m0 + (TM / 4) * pass + row, gn = n0 + 8 * ch;
             if (gm >= M || gn >= N) continue;
@@ -813,7 +818,7 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
 
 template <bool kNested>
 void launch_fast_r(const GemmArgs& a, const float* T, hipStream_t s, dim3 grid, int r16) {
-    const dim3 block(256);
+    const dim3 block(512);
     switch (r16) {
         case 0: hipLaunchKernelGGL((v4::gemm_fast_kernel<0, kNested>), grid, block, 0, s, a, T); break;
         case 1: hipLaunchKernelGGL((v4::gemm_fast_kernel<1, kNested>), grid, block, 0, s, a, T); break;
