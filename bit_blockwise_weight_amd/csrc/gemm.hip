@@ -490,26 +490,28 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
     // LDS-read wait to zero while they are in flight.  The resource covers the tile's
     // rows; offsets are bytes from the tile's first row (rows past M are clamped to the
     // last row: they only feed output rows that are never stored).
+    // Piece v of a lane is row 64 v + 8 wave + lane / 8 of the tile, so the pieces are a
+    // uniform 64 rows apart (the stride goes into the scalar offset).  Rows past M lie
+    // beyond the resource's range, and buffer loads return zero there.
     const uint16_t* xtile = a.X + m0 * K;
-    const int64_t xbytes = (M - m0) * K * 2;
-    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(xtile), (short)0, (int)(xbytes < 0x7FFFFFFFll ? xbytes : 0x7FFFFFFFll), 0x00020000);
-    uint32_t xsrc[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int p = (v * 8 + wave) * 64 + lane;          // LDS 16-byte slot written by this lane
+    const int64_t xrows = M - m0 < TM ? M - m0 : TM;
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xtile), (short)0, (int)(xrows * K * 2), 0x00020000);
+    uint32_t xsrc0;
+    {
+        const int p = wave * 64 + lane;                    // LDS 16-byte slot written by this lane (piece 0)
         const int row = p >> 3, slot = p & 7;
-        const int chunk = slot ^ ((row >> 1) & 7);
-        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
-        xsrc[v] = (uint32_t)(((gm - m0) * K + chunk * 8) * 2);
+        const int chunk = slot ^ ((row >> 1) & 7);         // the same for every piece: rows differ by 64
+        xsrc0 = (uint32_t)((row * K + chunk * 8) * 2);
     }
+    const int32_t xstride = (int32_t)(64 * K * 2);
     auto load_x = [&](int64_t s, auto buf) {
         const int32_t kbytes = (int32_t)((s < nk1 ? s : nk1) * TK * 2);
         char* base = reinterpret_cast<char*>(decltype(buf)::value ? xsB : xsA);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             lptr_t dst = (lptr_t)((__attribute__((address_space(3))) char*)base + (v * 8 + wave) * 1024);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, (int32_t)xsrc[v], kbytes, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, (int32_t)xsrc0, kbytes + v * xstride, 0, 0);
         }
     };
 
@@ -705,15 +707,21 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
 
 // Partial LoRA products, T_p[m][j] = s * sum_{k in split p} X[m][k] A[k][j], in
 // fp32, j < 16*R16 (columns >= r are 0).  Grid: (64-row groups, kSplits K
-// splits); a workgroup's 4 waves take 16 rows each and share the A tile of each
-// 64-deep step, transposed into LDS; the next step's X fragments are loaded
-// while the current step's MFMAs run.  The GEMM kernel adds the kSplits partials
-// of its rows in split order (deterministic) when it stages s X A.
-template <int R16>
+// splits); a workgroup's 4 waves take 16 rows each.  The split's A rows are
+// transposed into LDS in chunks of up to kChunk 64-deep steps (one barrier pair
+// per chunk), and each lane's X fragments stream from global memory into a ring
+// of 4 register sets, loaded 4 steps ahead without conditions (the kernel is
+// bound by the X stream, so the loads need depth, not compute, to hide their
+// latency).  A chunk's step count is rounded up to a multiple of 4 with zero
+// columns of A^T, whose X loads are clamped to the split's last step.  The GEMM
+// kernel adds the kSplits partials of its rows in split order (deterministic)
+// when it stages s X A.
+template <int R16, bool kVec>
 __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restrict__ T) {
     constexpr int kRp = 16 * R16;
-    constexpr int kS = TK + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t at[2][kRp * kS];
+    constexpr int kChunk = R16 == 1 ? 16 : (R16 == 2 ? 8 : 4);   // steps per A^T chunk (about 33 KB of LDS)
+    constexpr int kS = kChunk * TK + 8;                           // A^T row pitch (elements)
+    __shared__ __attribute__((aligned(16))) uint16_t at[kRp * kS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
     const int64_t M = a.M, K = a.K;
@@ -724,9 +732,10 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
     const int64_t mrow = (int64_t)blockIdx.x * 64 + 16 * wave + l16;
     const int64_t mrow_c = mrow < M ? mrow : M - 1;
     const uint16_t* xrow = a.X + mrow_c * K + 8 * q4;
-    const bool a_vec = (r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.A) % 16) == 0;
-    constexpr int cpr = kRp / 8;                       // 16-byte chunks per A row (padded)
-    constexpr int kAPer = (TK * cpr + 255) / 256;
+    // kVec: r % 8 == 0 and A 16-byte aligned (A rows load as 16-byte pieces)
+    constexpr bool a_vec = kVec;
+    constexpr int cpr = kRp / 8;                                  // 16-byte chunks per A row (padded)
+    constexpr int kAPer = kChunk * TK * cpr / 256;                // A pieces per thread and chunk
 
     floatx4_t acc[R16];
 #pragma unroll
@@ -734,14 +743,25 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[jt][e] = 0.0f;
 
-    uint4 ar[kAPer];
-    auto load_a = [&](int64_t s) {
+    // X fragments of step s (clamped to the split's last step): k = 64 s + 8 q4 + [0, 8)
+    // and + 32
+    auto load_xs = [&](int64_t s, uint4 (&d)[2]) {
+        const int64_t sc = s < s1 ? s : s1 - 1;
+        const uint4* p = reinterpret_cast<const uint4*>(xrow + sc * TK);
+        d[0] = p[0];
+        d[1] = p[4];
+    };
+    // A rows [64 c0, 64 c0 + 64 kChunk) transposed into at; rows past the chunk's
+    // nsteps steps and ranks >= r are zero
+    auto load_at = [&](int64_t c0, int nsteps) {
+        uint4 ar[kAPer];
 #pragma unroll
         for (int v = 0; v < kAPer; ++v) {
             const int c = tid + 256 * v;
-            const int row = (c / cpr) < TK ? (c / cpr) : TK - 1, cc = c % cpr;
-            const uint16_t* src = a.A + (s * TK + row) * r;
-            if (a_vec) {
+            const int row = c / cpr, cc = c % cpr;
+            const int64_t krow = c0 * TK + (row < nsteps * TK ? row : nsteps * TK - 1);
+            const uint16_t* src = a.A + krow * r;
+            if constexpr (a_vec) {
                 ar[v] = *reinterpret_cast<const uint4*>(src + (cc * 8 < r ? cc * 8 : r - 8));
             } else {
                 uint32_t e[8];
@@ -750,57 +770,61 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
                 ar[v] = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
             }
         }
-    };
-    auto store_a = [&](int buf) {
 #pragma unroll
         for (int v = 0; v < kAPer; ++v) {
             const int c = tid + 256 * v;
             const int row = c / cpr, cc = c % cpr;
-            if (row < TK) {
-                const uint32_t w4[4] = {ar[v].x, ar[v].y, ar[v].z, ar[v].w};
-                const int shift = (a_vec && cc * 8 + 8 > r) ? (cc * 8 - (r - 8)) : 0;
+            const bool live = row < nsteps * TK;
+            const uint32_t w4[4] = {ar[v].x, ar[v].y, ar[v].z, ar[v].w};
+            const int shift = (a_vec && cc * 8 + 8 > r) ? (cc * 8 - (r - 8)) : 0;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int st = t + shift;
-                    at[buf][(cc * 8 + t) * kS + row] =
-                        (cc * 8 + t < r && st < 8) ? (uint16_t)(w4[st >> 1] >> ((st & 1) ? 16 : 0)) : (uint16_t)0;
-                }
+            for (int t = 0; t < 8; ++t) {
+                const int st = t + shift;
+                at[(cc * 8 + t) * kS + row] =
+                    (live && cc * 8 + t < r && st < 8) ? (uint16_t)(w4[st >> 1] >> ((st & 1) ? 16 : 0)) : (uint16_t)0;
             }
         }
     };
+    auto bare_barrier = [] {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) (LDS), vmcnt and expcnt untouched
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
 
-    uint4 xv[2];
     if (s0 < s1) {
-        load_a(s0);
-        xv[0] = *reinterpret_cast<const uint4*>(xrow + s0 * TK);
-        xv[1] = *reinterpret_cast<const uint4*>(xrow + s0 * TK + 32);
-        store_a(0);
-    }
-    __syncthreads();
-    for (int64_t s = s0; s < s1; ++s) {
-        const int buf = (int)((s - s0) & 1);
-        const bool more = s + 1 < s1;
-        uint4 xn[2];
-        if (more) {
-            load_a(s + 1);
-            xn[0] = *reinterpret_cast<const uint4*>(xrow + (s + 1) * TK);
-            xn[1] = *reinterpret_cast<const uint4*>(xrow + (s + 1) * TK + 32);
-        }
+        uint4 x0[2], x1[2], x2[2], x3[2];     // ring: X of steps s .. s + 3 (slot = step % 4 from s0)
+        load_xs(s0, x0);
+        load_xs(s0 + 1, x1);
+        load_xs(s0 + 2, x2);
+        load_xs(s0 + 3, x3);
+        auto one = [&](int64_t s, int kloc, uint4 (&xv)[2]) {
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xv[kh]);
+            for (int kh = 0; kh < 2; ++kh) {
+                const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xv[kh]);
 #pragma unroll
-            for (int jt = 0; jt < R16; ++jt) {
-                const bf16x8_t ab = *reinterpret_cast<const bf16x8_t*>(&at[buf][(16 * jt + l16) * kS + 32 * kh + 8 * q4]);
-                acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ab, acc[jt], 0, 0, 0);
+                for (int jt = 0; jt < R16; ++jt) {
+                    const bf16x8_t ab =
+                        *reinterpret_cast<const bf16x8_t*>(&at[(16 * jt + l16) * kS + kloc + 32 * kh + 8 * q4]);
+                    acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ab, acc[jt], 0, 0, 0);
+                }
+            }
+            load_xs(s + 4, xv);
+        };
+        for (int64_t c0 = s0; c0 < s1; c0 += kChunk) {
+            const int nsteps = (int)(s1 - c0 < kChunk ? s1 - c0 : kChunk);
+            bare_barrier();                   // every wave is done with the previous chunk
+            load_at(c0, nsteps);
+            bare_barrier();
+            const int ngroups = (nsteps + 3) / 4;
+            for (int gi = 0; gi < ngroups; ++gi) {
+                const int64_t s = c0 + 4 * gi;
+                one(s, (4 * gi) * TK, x0);
+                one(s + 1, (4 * gi + 1) * TK, x1);
+                one(s + 2, (4 * gi + 2) * TK, x2);
+                one(s + 3, (4 * gi + 3) * TK, x3);
             }
         }
-        if (more) {
-            store_a(buf ^ 1);
-            xv[0] = xn[0];
-            xv[1] = xn[1];
-        }
-        __syncthreads();
     }
     // 16x16 output: lane holds C[4 q4 + e][l16]
     float* Tp = T + (int64_t)split * M * kRp;
@@ -830,12 +854,19 @@ void launch_fast_r(const GemmArgs& a, const float* T, hipStream_t s, dim3 grid, 
 
 void launch_lora_xa(const GemmArgs& a, float* T, hipStream_t s, int r16) {
     const dim3 grid((unsigned)((a.M + 63) / 64), v4::kSplits);
+    const bool vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.A) % 16) == 0;
+#define QK_LORA_XA(R)                                                                  \
+    do {                                                                               \
+        if (vec) hipLaunchKernelGGL((v4::lora_xa_kernel<R, true>), grid, dim3(256), 0, s, a, T); \
+        else hipLaunchKernelGGL((v4::lora_xa_kernel<R, false>), grid, dim3(256), 0, s, a, T);    \
+    } while (0)
     switch (r16) {
-        case 1: hipLaunchKernelGGL((v4::lora_xa_kernel<1>), grid, dim3(256), 0, s, a, T); break;
-        case 2: hipLaunchKernelGGL((v4::lora_xa_kernel<2>), grid, dim3(256), 0, s, a, T); break;
-        case 3: hipLaunchKernelGGL((v4::lora_xa_kernel<3>), grid, dim3(256), 0, s, a, T); break;
-        default: hipLaunchKernelGGL((v4::lora_xa_kernel<4>), grid, dim3(256), 0, s, a, T); break;
+        case 1: QK_LORA_XA(1); break;
+        case 2: QK_LORA_XA(2); break;
+        case 3: QK_LORA_XA(3); break;
+        default: QK_LORA_XA(4); break;
     }
+#undef QK_LORA_XA
 }
 
 hipError_t launch_fast(const GemmArgs& a, void* workspace, hipStream_t s) {
