@@ -566,9 +566,12 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
     load_codes(0, c0);
     load_codes(1, c1);
     load_x(0, Buf0{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();               // table and X(0) in LDS
     load_x(1, Buf1{});
+    // table and X(0) in LDS; X(1) (the last 4 loads) stays in flight
+    __builtin_amdgcn_s_waitcnt(4 | 0x70);   // vmcnt(4) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
     // A fragments of the current quarter; each is replaced by the next quarter's right
     // after its MFMA is issued
@@ -688,7 +691,12 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
                 cs[row * TN + col] = (uint16_t)(pack_bf16x2(acc[rt][e], 0.0f) & 0xFFFFu);
             }
         }
-        __syncthreads();
+        // a bare barrier: the Y stores of the previous passes stay in flight (their LDS
+        // reads, the only use of this buffer two passes ago, are complete)
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt untouched
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         for (int c = tid; c < (TM / 4) * (TN / 8); c += kThr) {
             const int row = c / (TN / 8), ch = c % (TN / 8);
             const int64_t gm = m0 + (TM / 4) * pass + row, gn = n0 + 8 * ch;
