@@ -718,10 +718,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
 // splits); a workgroup's 4 waves take 16 rows each.  The split's A rows are
 // transposed into LDS in chunks of up to kChunk 64-deep steps (one barrier pair
 // per chunk), and each lane's X fragments stream from global memory into a ring
-// of 4 register sets, loaded 4 steps ahead without conditions (the kernel is
-// bound by the X stream, so the loads need depth, not compute, to hide their
-// latency).  A chunk's step count is rounded up to a multiple of 4 with zero
-// columns of A^T, whose X loads are clamped to the split's last step.  The GEMM
+// of 4 register sets, loaded 4 steps ahead without conditions.  A chunk's step
+// count is rounded up to a multiple of 4 with zero columns of A^T, whose X loads
+// are clamped to the split's last step.  (An 8-deep ring measured slower.)  The GEMM
 // kernel adds the kSplits partials of its rows in split order (deterministic)
 // when it stages s X A.
 template <int R16, bool kVec>
@@ -759,10 +758,10 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
         d[0] = p[0];
         d[1] = p[4];
     };
-    // A rows [64 c0, 64 c0 + 64 kChunk) transposed into at; rows past the chunk's
+    // A rows [64 c0, 64 c0 + 64 kChunk) transposed into at, in two parts (loads, then LDS
+    // stores) so the loads can be issued before other loads; rows past the chunk's
     // nsteps steps and ranks >= r are zero
-    auto load_at = [&](int64_t c0, int nsteps) {
-        uint4 ar[kAPer];
+    auto issue_a = [&](int64_t c0, int nsteps, uint4 (&ar)[kAPer]) {
 #pragma unroll
         for (int v = 0; v < kAPer; ++v) {
             const int c = tid + 256 * v;
@@ -778,6 +777,8 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
                 ar[v] = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
             }
         }
+    };
+    auto store_at = [&](int nsteps, const uint4 (&ar)[kAPer]) {
 #pragma unroll
         for (int v = 0; v < kAPer; ++v) {
             const int c = tid + 256 * v;
@@ -801,11 +802,16 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
     };
 
     if (s0 < s1) {
-        uint4 x0[2], x1[2], x2[2], x3[2];     // ring: X of steps s .. s + 3 (slot = step % 4 from s0)
-        load_xs(s0, x0);
-        load_xs(s0 + 1, x1);
-        load_xs(s0 + 2, x2);
-        load_xs(s0 + 3, x3);
+        // the first chunk's A loads go first: the wait for them then leaves the X ring's
+        // loads (issued after) in flight
+        uint4 ar[kAPer];
+        const int nsteps0 = (int)(s1 - s0 < kChunk ? s1 - s0 : kChunk);
+        issue_a(s0, nsteps0, ar);
+        uint4 xr[4][2];                       // ring: X of steps s .. s + 3 (slot = step % 4 from s0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_xs(s0 + i, xr[i]);
+        store_at(nsteps0, ar);
+        bare_barrier();
         auto one = [&](int64_t s, int kloc, uint4 (&xv)[2]) {
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
@@ -821,16 +827,16 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
         };
         for (int64_t c0 = s0; c0 < s1; c0 += kChunk) {
             const int nsteps = (int)(s1 - c0 < kChunk ? s1 - c0 : kChunk);
-            bare_barrier();                   // every wave is done with the previous chunk
-            load_at(c0, nsteps);
-            bare_barrier();
+            if (c0 > s0) {
+                bare_barrier();               // every wave is done with the previous chunk
+                issue_a(c0, nsteps, ar);
+                store_at(nsteps, ar);
+                bare_barrier();
+            }
             const int ngroups = (nsteps + 3) / 4;
             for (int gi = 0; gi < ngroups; ++gi) {
-                const int64_t s = c0 + 4 * gi;
-                one(s, (4 * gi) * TK, x0);
-                one(s + 1, (4 * gi + 1) * TK, x1);
-                one(s + 2, (4 * gi + 2) * TK, x2);
-                one(s + 3, (4 * gi + 3) * TK, x3);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) one(c0 + 4 * gi + i, (4 * gi + i) * TK, xr[i]);
             }
         }
     }
