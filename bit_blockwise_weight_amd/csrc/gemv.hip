@@ -6,14 +6,16 @@
 // fused, or 4-bit can be slower than 16-bit).  The weight is never written out.
 //
 // Fast path (K a multiple of 64 and of the block size, 16-byte aligned codes and x):
-//   * A workgroup owns 16 weight rows; its 8 waves split K in chunks of 512
-//     (wave w takes chunks w, w + 8, ...).
+//   * A workgroup owns 16 weight rows; its S waves split K in chunks of 512
+//     (wave w takes chunks w, w + S, ...).  S = 4 (80 KB of LDS: two workgroups
+//     per CU, one loading while the other computes) when there are at least two
+//     tiles per CU and K <= 4096; S = 8 otherwise.
 //   * Codes are loaded so that one instruction fetches 256 contiguous bytes from
 //     each of 4 rows; each wave writes its chunk to its own LDS area (no barrier)
 //     and reads it back in MFMA layout.  In that area the 16-byte piece p of row r
 //     sits in slot 16 r + (p ^ r), so the 16 rows a fragment read touches fall in
 //     16 different bank groups.  The next chunk's codes, x and scales are loaded
-//     before the current chunk is computed.
+//     before the current chunk is computed, by loads outside any branch.
 //   * v_mfma_f32_16x16x32_bf16 with A = x (16 x 32, rows m >= M are zero) and
 //     B = W^T (32 x 16 rows), so the 4 output registers of lane l are y[m][n] for
 //     m = 4(l / 16) + r, n = l % 16.  Lane l holds row n = l % 16 and, in 64-k block
@@ -25,7 +27,7 @@
 //     nibble, bf16 level of the low nibble) as one dword, replicated 64 times and
 //     interleaved so that lane l reads copy l: the address (byte << 8 | 4l) is one
 //     v_perm, the read never conflicts.
-//   * The 8 waves' partial tiles are summed through LDS in a fixed order.
+//   * The S waves' partial tiles are summed through LDS in a fixed order.
 // The levels are used as bf16 and the block scale is applied in fp32 after the
 // bf16 products; the result agrees with the fp64 product on the bf16-dequantized
 // weight within the documented tolerance.
@@ -74,9 +76,8 @@ struct ChunkRegs {
     float d[kChunkBlocks];       // dq scale (nested)
 };
 
-template <bool kNested>
-__global__ __launch_bounds__(512) void gemv_lds_kernel(GemvArgs a) {
-    constexpr int S = 8;
+template <bool kNested, int S>
+__global__ __launch_bounds__(S * 64) void gemv_lds_kernel(GemvArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t tab[256 * kTabCopies];   // 64 KB byte -> bf16 pair
     __shared__ __attribute__((aligned(1024))) uint4 cb[S][256];               // codes chunk, 4 KB per wave
     const int lane = threadIdx.x & 63;
@@ -173,17 +174,19 @@ __global__ __launch_bounds__(512) void gemv_lds_kernel(GemvArgs a) {
 
     const int64_t c0 = wave;
     ChunkRegs ra, rb;
-    if (ncw > 0) load(c0, ra);
+    load(c0, ra);   // clamped: a wave without chunks reads a valid one and never uses it
     {
-        // pair table, 64 copies: entry i = 64 b + copy for byte b.  With 8 waves, wave w
-        // writes the bytes b = w + 8 j, whose nibbles are (j / 2, w + 8 (j % 2)); the level
-        // reads are uniform (scalar loads), so they do not wait for the loads in flight.
-        const int w = wave;
-        const uint32_t lo0 = as_uint(a.w.levels[w]), lo1 = as_uint(a.w.levels[w + 8]);
+        // pair table, 64 copies: entry i = 64 b + copy for byte b.  Wave w writes the bytes
+        // b = w + S j, whose nibbles are (j / (16 / S), w + S (j % (16 / S))); the level reads
+        // are uniform (scalar loads), so they do not wait for the loads in flight.
+        constexpr int kLo = 16 / S;
+        float lo[kLo];
 #pragma unroll
-        for (int jj = 0; jj < 32; ++jj) {
-            const float hi_nib = a.w.levels[jj >> 1];
-            tab[(w + 8 * jj) * kTabCopies + lane] = pack_bf16x2(hi_nib, as_float((jj & 1) ? lo1 : lo0));
+        for (int q = 0; q < kLo; ++q) lo[q] = a.w.levels[wave + S * q];
+#pragma unroll
+        for (int jj = 0; jj < 256 / S; ++jj) {
+            const float hi_nib = a.w.levels[jj / kLo];
+            tab[(wave + S * jj) * kTabCopies + lane] = pack_bf16x2(hi_nib, lo[jj % kLo]);
         }
     }
     // a bare barrier: __syncthreads() would add a fence that waits for the loads in flight
@@ -191,20 +194,30 @@ __global__ __launch_bounds__(512) void gemv_lds_kernel(GemvArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (ncw > 0) stage(ra);
-    // two chunks per iteration, the register sets alternating by name (a copy would wait
-    // for its loads): load the next chunk, compute this one from LDS, then stage the next
-    for (int64_t i = 0; i < ncw; i += 2) {
+    stage(ra);
+    // Two chunks per iteration, the register sets alternating by name (a copy would wait
+    // for its loads): load the next chunk, compute this one from LDS, then stage the next.
+    // Every load inside the loop is unconditional and the last one or two chunks are
+    // peeled: a load under a branch merges the wait counts at the join, and the compute
+    // of this chunk would then wait for the next chunk's loads.
+    int64_t i = 0;
+    for (; i + 2 < ncw; i += 2) {
         const int64_t c = c0 + (int64_t)S * i;
-        const bool has1 = i + 1 < ncw, has2 = i + 2 < ncw;
-        if (has1) load(c + S, rb);
+        load(c + S, rb);
         compute(c, ra);
-        if (has1) {
-            stage(rb);
-            if (has2) load(c + 2 * S, ra);
-            compute(c + S, rb);
-            if (has2) stage(ra);
-        }
+        stage(rb);
+        load(c + 2 * S, ra);
+        compute(c + S, rb);
+        stage(ra);
+    }
+    if (ncw - i == 2) {
+        const int64_t c = c0 + (int64_t)S * i;
+        load(c + S, rb);
+        compute(c, ra);
+        stage(rb);
+        compute(c + S, rb);
+    } else if (ncw - i == 1) {
+        compute(c0 + (int64_t)S * i, ra);
     }
 
     // reduce the S waves' tiles in a fixed order: red[wave][r][lane] (over the table)
@@ -274,10 +287,19 @@ hipError_t launch_gemv(const void* x, int32_t M, const MatArgs& w, void* y, hipS
         hipLaunchKernelGGL(gemv_generic_kernel, dim3((unsigned)((w.N + 3) / 4)), dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    *variant = "mfma 16x16x32 bf16, 16 rows per workgroup, codes staged through LDS in 512-k chunks, 8 waves split-K";
+    *variant = "mfma 16x16x32 bf16, 16 rows per workgroup, codes staged through LDS in 512-k chunks, 4 or 8 waves split-K";
     const unsigned grid = (unsigned)((a.N + 15) / 16);
-    if (w.w.nested) hipLaunchKernelGGL((gemv_lds_kernel<true>), dim3(grid), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((gemv_lds_kernel<false>), dim3(grid), dim3(512), 0, s, a);
+    // 4 waves (80 KB of LDS, two workgroups per CU, so one's loads overlap the other's
+    // compute) when there are at least two tiles per CU and K fits 8 chunks; 8 waves
+    // (one workgroup per CU, more loads in flight per tile) otherwise
+    const bool four = grid >= 2u * (unsigned)device_cu_count() && w.K <= 8 * kChunkK;
+    if (four) {
+        if (w.w.nested) hipLaunchKernelGGL((gemv_lds_kernel<true, 4>), dim3(grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((gemv_lds_kernel<false, 4>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+        if (w.w.nested) hipLaunchKernelGGL((gemv_lds_kernel<true, 8>), dim3(grid), dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((gemv_lds_kernel<false, 8>), dim3(grid), dim3(512), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -86,7 +86,9 @@ def test_gemv_edge_generic_path(B, kind):
 
 
 @pytest.mark.parametrize("N,K,B,M", [(33, 64, 64, 3), (100, 128, 128, 16), (64, 256, 256, 7), (1, 64, 64, 1),
-                                     (257, 1024, 64, 9), (31, 192, 64, 16)])
+                                     (257, 1024, 64, 9), (31, 192, 64, 16),
+                                     # at least two 16-row tiles per CU: the 4-wave kernel (one chunk, partial)
+                                     (8200, 320, 64, 5), (8193, 1536, 128, 16)])
 def test_gemv_small_and_ragged(N, K, B, M):
     say(f"case: gemv ragged N={N} K={K} B={B} M={M}")
     g = np.random.default_rng(N * 7 + K)
