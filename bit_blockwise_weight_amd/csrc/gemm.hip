@@ -773,6 +773,21 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
         }
     };
     auto store_at = [&](int nsteps, const uint4 (&ar)[kAPer]) {
+        if (a_vec && r == kRp) {
+            // every 16-byte piece holds 8 live ranks: zero the piece once if its row is
+            // past the chunk, then 8 two-byte stores with compile-time element indexes
+#pragma unroll
+            for (int v = 0; v < kAPer; ++v) {
+                const int c = tid + 256 * v;
+                const int row = c / cpr, cc = c % cpr;
+                const bool live = row < nsteps * TK;
+                const uint32_t w4[4] = {live ? ar[v].x : 0u, live ? ar[v].y : 0u, live ? ar[v].z : 0u,
+                                        live ? ar[v].w : 0u};
+#pragma unroll
+                for (int t = 0; t < 8; ++t) at[(cc * 8 + t) * kS + row] = (uint16_t)(w4[t >> 1] >> ((t & 1) ? 16 : 0));
+            }
+            return;
+        }
 #pragma unroll
         for (int v = 0; v < kAPer; ++v) {
             const int c = tid + 256 * v;

@@ -144,7 +144,9 @@ def _lora(K, N, r, seed):
 
 @pytest.mark.parametrize("M,N,K,B,r", [(128, 128, 64, 64, 16), (77, 100, 128, 128, 1), (300, 257, 256, 256, 64),
                                        (1, 33, 512, 64, 16), (256, 384, 1024, 64, 8), (129, 129, 192, 64, 17),
-                                       (200, 300, 320, 64, 40), (65, 96, 448, 64, 45)])
+                                       (200, 300, 320, 64, 40), (65, 96, 448, 64, 45),
+                                       # K = 11008: each K split of the X*A pre-pass takes several A chunks
+                                       (96, 64, 11008, 64, 16), (70, 48, 11008, 64, 64)])
 def test_gemm_small_and_ragged(M, N, K, B, r):
     say(f"case: gemm ragged M={M} N={N} K={K} B={B} r={r}")
     g = np.random.default_rng(M + N + K)
