@@ -39,7 +39,7 @@ struct MergeArgs {
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return as_float((uint32_t)b << 16); }
 
-template <bool kVec>
+template <bool kVec, bool kVecAB>
 __global__ __launch_bounds__(kThreads) void lora_merge_kernel(MergeArgs a) {
     __shared__ float At[kRankChunk][kCols];      // 16 KB
     __shared__ float Bs[kRankChunk][kRows];      // 4 KB
@@ -65,18 +65,62 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(MergeArgs a) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) p[i][q] = 0.0f;
 
+    // kVec: the epilogue's code words and block-scale inputs are loaded here, so their
+    // latency passes under the adapter product (rows or k past the edge read a valid
+    // address and are not stored)
+    const int64_t kb = k0 + 8 * kc;
+    uint32_t cwp[8];
+    int32_t qp[8];
+    float dp[8];
+    if constexpr (kVec) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t n = n0 + 8 * rg + i;
+            const int64_t e0 = (n < N ? n : N - 1) * K + (kb < K ? kb : K - 8);
+            cwp[i] = *reinterpret_cast<const uint32_t*>(a.w.codes + e0 / 2);
+            const int64_t blk = e0 >> a.w.blocksize_log2;
+            if (a.w.nested) {
+                qp[i] = a.w.q8[blk];
+                dp[i] = a.w.dq_scale[blk / QK_DQ_BLOCK];
+            } else {
+                qp[i] = (int32_t)as_uint(a.w.absmax[blk]);
+                dp[i] = 0.0f;
+            }
+        }
+    }
+
     for (int j0 = 0; j0 < r; j0 += kRankChunk) {
         const int nr = r - j0 < kRankChunk ? r - j0 : kRankChunk;
         __syncthreads();                                   // the previous chunk has been read
         {
             // A: thread t stages row k0 + t of the tile (ranks j0 .. j0 + nr)
             const int64_t k = k0 + tid;
-            for (int j = 0; j < kRankChunk; ++j)
-                At[j][tid] = (k < K && j < nr) ? bf16f(a.A[k * r + j0 + j]) : 0.0f;
-            // B: 16 ranks x 64 rows, 4 per thread
-            for (int e = tid; e < kRankChunk * kRows; e += kThreads) {
-                const int j = e / kRows, nn = e % kRows;
-                Bs[j][nn] = (j < nr && n0 + nn < N) ? bf16f(a.B[(int64_t)(j0 + j) * N + n0 + nn]) : 0.0f;
+            if constexpr (kVecAB) {
+                // r % 8 == 0 (nr is 8 or 16), A and B 16-byte aligned, N % 8 == 0
+                const uint4* ap = reinterpret_cast<const uint4*>(a.A + (k < K ? k : K - 1) * r + j0);
+                const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+                const uint4 h0 = k < K ? ap[0] : z;
+                const uint4 h1 = (k < K && nr == 16) ? ap[1] : z;
+                const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+                for (int j = 0; j < kRankChunk; ++j) At[j][tid] = as_float((j & 1) ? (hw[j >> 1] & 0xFFFF0000u) : (hw[j >> 1] << 16));
+                // B: 16 ranks x 64 rows as 8-element pieces, threads 0 .. 127
+                if (tid < kRankChunk * kRows / 8) {
+                    const int j = tid >> 3, nn = 8 * (tid & 7);
+                    uint4 bv = z;
+                    if (j < nr && n0 + nn < N) bv = *reinterpret_cast<const uint4*>(a.B + (int64_t)(j0 + j) * N + n0 + nn);
+                    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) Bs[j][nn + t] = as_float((t & 1) ? (bw[t >> 1] & 0xFFFF0000u) : (bw[t >> 1] << 16));
+                }
+            } else {
+                for (int j = 0; j < kRankChunk; ++j)
+                    At[j][tid] = (k < K && j < nr) ? bf16f(a.A[k * r + j0 + j]) : 0.0f;
+                // B: 16 ranks x 64 rows, 4 per thread
+                for (int e = tid; e < kRankChunk * kRows; e += kThreads) {
+                    const int j = e / kRows, nn = e % kRows;
+                    Bs[j][nn] = (j < nr && n0 + nn < N) ? bf16f(a.B[(int64_t)(j0 + j) * N + n0 + nn]) : 0.0f;
+                }
             }
         }
         __syncthreads();
@@ -104,14 +148,13 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t n = n0 + 8 * rg + i;
-        const int64_t kb = k0 + 8 * kc;
         if (n >= N || kb >= K) continue;
         const int64_t e0 = n * K + kb;
         float w[8];
         if constexpr (kVec) {
             // K % 8 == 0: the 8 elements are 4 aligned code bytes inside one block
-            const uint32_t cw = *reinterpret_cast<const uint32_t*>(a.w.codes + e0 / 2);
-            const float sc = scale_of(e0 >> a.w.blocksize_log2);
+            const uint32_t cw = cwp[i];
+            const float sc = a.w.nested ? __fadd_rn(__fmul_rn((float)qp[i], dp[i]), mean) : as_float((uint32_t)qp[i]);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const uint32_t code = (cw >> (8 * (q >> 1) + ((q & 1) ? 0 : 4))) & 0xFu;
@@ -152,8 +195,12 @@ hipError_t launch_lora_merge(const MatArgs& w, const void* A, const void* B, int
     if (gy > 65535) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((w.K + kCols - 1) / kCols), (unsigned)gy);
     const bool vec = (w.K % 8) == 0 && (reinterpret_cast<uintptr_t>(out) % 16) == 0;
-    if (vec) hipLaunchKernelGGL(lora_merge_kernel<true>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(lora_merge_kernel<false>, grid, dim3(kThreads), 0, s, a);
+    const bool vec_ab = (r % 8) == 0 && (w.N % 8) == 0 && (reinterpret_cast<uintptr_t>(A) % 16) == 0 &&
+                        (reinterpret_cast<uintptr_t>(B) % 16) == 0;
+    if (vec && vec_ab) hipLaunchKernelGGL((lora_merge_kernel<true, true>), grid, dim3(kThreads), 0, s, a);
+    else if (vec) hipLaunchKernelGGL((lora_merge_kernel<true, false>), grid, dim3(kThreads), 0, s, a);
+    else if (vec_ab) hipLaunchKernelGGL((lora_merge_kernel<false, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((lora_merge_kernel<false, false>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

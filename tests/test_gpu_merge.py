@@ -48,6 +48,9 @@ def _gpu_state(Wb, N, K, B, kind, nested):
     (64, 256, 1, 256, ocb.FP4, True),        # rank 1
     (37, 4099, 5, 64, ocb.FP4, False),       # K % 8 != 0: per-element path, blocks straddle rows
     (3, 7, 3, 64, ocb.NF4, True),            # smaller than one tile
+    (264, 512, 16, 64, ocb.NF4, True),       # 16-byte adapter staging (r % 8 == 0, N % 8 == 0), ragged rows
+    (136, 1024, 40, 128, ocb.NF4, False),    # 16-byte adapter staging, rank chunks of 16, 16 and 8
+    (40, 4099, 8, 64, ocb.FP4, False),       # 16-byte adapter staging with the per-element weight path
 ])
 def test_merge_bit_exact(N, K, r, B, kind, nested):
     say(f"case: merge N={N} K={K} r={r} B={B} kind={kind} nested={nested}")
