@@ -40,7 +40,7 @@ struct MergeArgs {
 __device__ __forceinline__ float bf16f(uint16_t b) { return as_float((uint32_t)b << 16); }
 
 template <bool kVec, bool kVecAB>
-__global__ __launch_bounds__(kThreads) void lora_merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void lora_merge_kernel(MergeArgs a) {
     __shared__ float At[kRankChunk][kCols];      // 16 KB
     __shared__ float Bs[kRankChunk][kRows];      // 4 KB
     __shared__ float lev[16 * kCopies];          // 2 KB
@@ -89,41 +89,49 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(MergeArgs a) {
         }
     }
 
-    for (int j0 = 0; j0 < r; j0 += kRankChunk) {
-        const int nr = r - j0 < kRankChunk ? r - j0 : kRankChunk;
-        __syncthreads();                                   // the previous chunk has been read
-        {
-            // A: thread t stages row k0 + t of the tile (ranks j0 .. j0 + nr)
-            const int64_t k = k0 + tid;
-            if constexpr (kVecAB) {
-                // r % 8 == 0 (nr is 8 or 16), A and B 16-byte aligned, N % 8 == 0
-                const uint4* ap = reinterpret_cast<const uint4*>(a.A + (k < K ? k : K - 1) * r + j0);
-                const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-                const uint4 h0 = k < K ? ap[0] : z;
-                const uint4 h1 = (k < K && nr == 16) ? ap[1] : z;
-                const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+    // the adapter product, 16 ranks per LDS chunk; the first chunk is peeled so the
+    // block scales are formed from their early loads right after its staging, where
+    // those loads have landed (the staging waits for loads issued after them)
+    const float mean = a.w.nested ? *a.w.dq_mean : 0.0f;
+    float scp[8];
+    auto make_scales = [&] {
+        if constexpr (kVec) {
 #pragma unroll
-                for (int j = 0; j < kRankChunk; ++j) At[j][tid] = as_float((j & 1) ? (hw[j >> 1] & 0xFFFF0000u) : (hw[j >> 1] << 16));
-                // B: 16 ranks x 64 rows as 8-element pieces, threads 0 .. 127
-                if (tid < kRankChunk * kRows / 8) {
-                    const int j = tid >> 3, nn = 8 * (tid & 7);
-                    uint4 bv = z;
-                    if (j < nr && n0 + nn < N) bv = *reinterpret_cast<const uint4*>(a.B + (int64_t)(j0 + j) * N + n0 + nn);
-                    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+            for (int i = 0; i < 8; ++i) scp[i] = a.w.nested ? __fadd_rn(__fmul_rn((float)qp[i], dp[i]), mean) : as_float((uint32_t)qp[i]);
+        }
+    };
+    auto stage = [&](int j0, int nr) {
+        // A: thread t stages row k0 + t of the tile (ranks j0 .. j0 + nr)
+        const int64_t k = k0 + tid;
+        if constexpr (kVecAB) {
+            // r % 8 == 0 (nr is 8 or 16), A and B 16-byte aligned, N % 8 == 0
+            const uint4* ap = reinterpret_cast<const uint4*>(a.A + (k < K ? k : K - 1) * r + j0);
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            const uint4 h0 = k < K ? ap[0] : z;
+            const uint4 h1 = (k < K && nr == 16) ? ap[1] : z;
+            const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) Bs[j][nn + t] = as_float((t & 1) ? (bw[t >> 1] & 0xFFFF0000u) : (bw[t >> 1] << 16));
-                }
-            } else {
-                for (int j = 0; j < kRankChunk; ++j)
-                    At[j][tid] = (k < K && j < nr) ? bf16f(a.A[k * r + j0 + j]) : 0.0f;
-                // B: 16 ranks x 64 rows, 4 per thread
-                for (int e = tid; e < kRankChunk * kRows; e += kThreads) {
-                    const int j = e / kRows, nn = e % kRows;
-                    Bs[j][nn] = (j < nr && n0 + nn < N) ? bf16f(a.B[(int64_t)(j0 + j) * N + n0 + nn]) : 0.0f;
-                }
+            for (int j = 0; j < kRankChunk; ++j) At[j][tid] = as_float((j & 1) ? (hw[j >> 1] & 0xFFFF0000u) : (hw[j >> 1] << 16));
+            // B: 16 ranks x 64 rows as 8-element pieces, threads 0 .. 127
+            if (tid < kRankChunk * kRows / 8) {
+                const int j = tid >> 3, nn = 8 * (tid & 7);
+                uint4 bv = z;
+                if (j < nr && n0 + nn < N) bv = *reinterpret_cast<const uint4*>(a.B + (int64_t)(j0 + j) * N + n0 + nn);
+                const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                for (int t = 0; t < 8; ++t) Bs[j][nn + t] = as_float((t & 1) ? (bw[t >> 1] & 0xFFFF0000u) : (bw[t >> 1] << 16));
+            }
+        } else {
+            for (int j = 0; j < kRankChunk; ++j)
+                At[j][tid] = (k < K && j < nr) ? bf16f(a.A[k * r + j0 + j]) : 0.0f;
+            // B: 16 ranks x 64 rows, 4 per thread
+            for (int e = tid; e < kRankChunk * kRows; e += kThreads) {
+                const int j = e / kRows, nn = e % kRows;
+                Bs[j][nn] = (j < nr && n0 + nn < N) ? bf16f(a.B[(int64_t)(j0 + j) * N + n0 + nn]) : 0.0f;
             }
         }
-        __syncthreads();
+    };
+    auto ranks = [&](int nr) {
         for (int j = 0; j < nr; ++j) {
             const float4 b0 = *reinterpret_cast<const float4*>(&Bs[j][8 * rg]);
             const float4 b1 = *reinterpret_cast<const float4*>(&Bs[j][8 * rg + 4]);
@@ -136,10 +144,25 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(MergeArgs a) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) p[i][q] = __builtin_fmaf(bv[i], av[q], p[i][q]);
         }
+    };
+    if (r > 0) {
+        const int nr0 = r < kRankChunk ? r : kRankChunk;
+        stage(0, nr0);
+        __syncthreads();
+        make_scales();
+        ranks(nr0);
+        for (int j0 = kRankChunk; j0 < r; j0 += kRankChunk) {
+            const int nr = r - j0 < kRankChunk ? r - j0 : kRankChunk;
+            __syncthreads();                               // the previous chunk has been read
+            stage(j0, nr);
+            __syncthreads();
+            ranks(nr);
+        }
+    } else {
+        __syncthreads();                                   // lev
+        make_scales();
     }
-    if (r == 0) __syncthreads();                           // lev is ready either way
 
-    const float mean = a.w.nested ? *a.w.dq_mean : 0.0f;
     const int copy = tid & (kCopies - 1);
     auto scale_of = [&](int64_t blk) {
         return a.w.nested ? __fadd_rn(__fmul_rn((float)a.w.q8[blk], a.w.dq_scale[blk / QK_DQ_BLOCK]), mean)
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void lora_merge_kernel(MergeArgs a) {
         if constexpr (kVec) {
             // K % 8 == 0: the 8 elements are 4 aligned code bytes inside one block
             const uint32_t cw = cwp[i];
-            const float sc = a.w.nested ? __fadd_rn(__fmul_rn((float)qp[i], dp[i]), mean) : as_float((uint32_t)qp[i]);
+            const float sc = scp[i];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const uint32_t code = (cw >> (8 * (q >> 1) + ((q & 1) ? 0 : 4))) & 0xFu;
