@@ -178,13 +178,13 @@ def test_gemm_lora_only_with_zero_weight():
     check_close(bf16_bits_to_f32(Y).reshape(M, N), ref, "lora only")
 
 
-@pytest.mark.parametrize("N", [4096, 11008])
-def test_gemm_qlora_prefill_full_size_sampled_rows(N):
-    """X [4096, 4096], W [N, 4096] NF4 + DQ, LoRA r=16, alpha/r=2: 256 sampled
-    output rows against the fp64 oracle."""
-    say(f"case: gemm qlora prefill N={N}")
-    X, W, A, Bm = workloads.qlora_prefill(N)
-    M, K, r = 4096, 4096, 16
+@pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_gemm_qlora_prefill_full_size_sampled_rows(N, K):
+    """X [4096, K], W [N, K] NF4 + DQ, LoRA r=16, alpha/r=2 (the layer set's three
+    GEMM shapes): 256 sampled output rows against the fp64 oracle."""
+    say(f"case: gemm qlora prefill N={N} K={K}")
+    X, W, A, Bm = workloads.qlora_prefill(N, K=K)
+    M, r = 4096, 16
     qw = _quantized(W, N, K)
     Y = host(qw.gemm(dev_bf16(X).reshape(M, K), dev_bf16(A).reshape(K, r), dev_bf16(Bm).reshape(r, N),
                      workloads.QLORA_ALPHA_OVER_R)).reshape(M, N)
