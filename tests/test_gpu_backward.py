@@ -113,18 +113,18 @@ def test_backward_deterministic_and_in_bounds():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("N", [4096, 11008])
-def test_backward_qlora_prefill_full_size(N):
-    """X [4096, 4096], W [N, 4096] NF4 + DQ, LoRA r = 16, alpha / r = 2, dY
-    [4096, N]: every element of dX, dA and dB."""
-    say(f"case: backward qlora prefill N={N}")
-    X, W, A, Bm = workloads.qlora_prefill(N)
+@pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_backward_qlora_prefill_full_size(N, K):
+    """X [4096, K], W [N, K] NF4 + DQ, LoRA r = 16, alpha / r = 2, dY [4096, N]
+    (the layer set's three shapes): every element of dX, dA and dB."""
+    say(f"case: backward qlora prefill N={N} K={K}")
+    X, W, A, Bm = workloads.qlora_prefill(N, K=K)
     dY = workloads.qlora_upstream_grad(N)
-    M, K, r = 4096, 4096, 16
+    M, r = 4096, 16
     s = workloads.QLORA_ALPHA_OVER_R
     dX, dA, dB, _ = _run(dY, X, W, A, Bm, M, N, K, r, 64, ocb.NF4, True, s)
     wd = oracle_wd(W, N, K, 64, ocb.NF4, True)
     rX, rA, rB = obw_.qlora_backward_f64(_f(dY, M, N), _f(X, M, K), wd, _f(A, K, r), _f(Bm, r, N), s)
-    check_close(_f(dX, M, K), rX, f"dX N={N}")
-    check_close(dA, rA, f"dA N={N}")
-    check_close(dB, rB, f"dB N={N}")
+    check_close(_f(dX, M, K), rX, f"dX N={N} K={K}")
+    check_close(dA, rA, f"dA N={N} K={K}")
+    check_close(dB, rB, f"dB N={N} K={K}")
