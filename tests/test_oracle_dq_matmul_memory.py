@@ -53,6 +53,34 @@ def test_mean_is_fp64_sum_over_count_then_fp32():
     assert dq.mean_f32(a) == floats.fraction_to_f32(Fraction(4, 3))
 
 
+def _half_even(x: Fraction) -> int:
+    fl = x.numerator // x.denominator
+    rem = x - fl
+    if rem != Fraction(1, 2):
+        return fl + (1 if rem > Fraction(1, 2) else 0)
+    return fl + (fl % 2)
+
+
+def test_mean_keeps_the_sum_bits_beyond_fp32():
+    """The sum 1 + 2^-24 needs 25 significant bits: kept in fp64 and divided by
+    nb = 5 in fp64, the mean rounds once to fp32 and lands one ulp above 0.2.
+    Rounding the sum to fp32 first (a tie, to even: 1.0) or summing in fp32
+    gives fp32(0.2), so a mean divided in fp32 fails here."""
+    a = np.float32([1.0, 2.0 ** -24, 0.0, 0.0, 0.0])
+    exact = (Fraction(1) + Fraction(1, 2 ** 24)) / 5
+    want = floats.fraction_to_f32(Fraction(float(exact)))     # fp64 quotient, then fp32
+    got = dq.mean_f32(a)
+    assert got == want and got.view(np.uint32) == np.float32(0.2).view(np.uint32) + 1
+    # the same value as one rounding of the exact quotient (no double rounding here)
+    assert want == floats.fraction_to_f32(exact)
+    # the readings this case rules out
+    seq32 = np.float32(0.0)
+    for v in a:
+        seq32 = np.float32(seq32 + v)
+    assert np.float32(seq32 / np.float32(a.size)) != got
+    assert np.float32(np.float32(1.0 + 2.0 ** -24) / np.float32(5.0)) != got
+
+
 # ---------------------------------------------------------------- double quant
 
 def test_hand_worked_double_quant():
@@ -62,6 +90,33 @@ def test_hand_worked_double_quant():
     assert mu == np.float32(2.5)
     assert q.tolist() == [-127, -42, 42, 127]
     assert sigma.tolist() == [np.float32(1.5) / np.float32(127)]
+
+
+def test_double_quant_ties_round_half_even():
+    """absmax = 200 + [127, -127, .5, -.5, 2.5, -2.5, 1.5, -1.5]: the mean is 200
+    exactly, the block maximum |c| is 127 and RN(RN(c/127)*127) gives back
+    +-0.5, +-2.5, +-1.5, which are ties.  Half-even rounding sends them to
+    0, 0, 2, -2, 2, -2; half-away-from-zero (floor(x + 1/2) for positives, C
+    roundf) would give 1, -1, 3, -3, 2, -2."""
+    offs = [127.0, -127.0, 0.5, -0.5, 2.5, -2.5, 1.5, -1.5]
+    a = np.float32(200.0) + np.float32(offs)
+    q, sigma, mu = dq.double_quant(a)
+    assert mu == np.float32(200.0)
+    s = Fraction(127)
+    want, scaled = [], []
+    for j in range(a.size):
+        c = floats.fraction_to_f32(Fraction(float(a[j])) - Fraction(float(mu)))
+        ratio = floats.fraction_to_f32(Fraction(float(c)) / s)
+        u = Fraction(float(floats.fraction_to_f32(Fraction(float(ratio)) * 127)))
+        scaled.append(u)
+        want.append(_half_even(u))
+    assert scaled[2:] == [Fraction(v) for v in offs[2:]]      # the ties are reached exactly
+    assert want == [127, -127, 0, 0, 2, -2, 2, -2]
+    assert q.tolist() == want
+    assert sigma.tolist() == [np.float32(1.0)]
+    # the rule this case rules out
+    away = [int(np.sign(float(u))) * int(np.floor(abs(float(u)) + 0.5)) for u in scaled]
+    assert away != want
 
 
 def test_constant_absmax_round_trips_exactly():
