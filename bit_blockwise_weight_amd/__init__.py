@@ -366,15 +366,30 @@ def qk_dequantize(state: QuantState, out_dtype=torch.bfloat16, out=None, device=
     return out
 
 
+def _rows_of(t: torch.Tensor, cols: int, name: str) -> torch.Tensor:
+    """t viewed as [M, cols]; a ValueError when its size is not a multiple of cols."""
+    if t.numel() % cols != 0 or (t.dim() > 0 and t.shape[-1] != cols):
+        raise ValueError(f"{name} {tuple(t.shape)} does not end in the weight's {cols} columns")
+    return t.reshape(-1, cols)
+
+
+def _check_out(t: torch.Tensor, shape, dtype, name: str):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != shape[0] * shape[1] or (t.dim() == 2 and tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{name} {tuple(t.shape)} does not hold [{shape[0]}, {shape[1]}]")
+
+
 def qk_gemv_nf4(x: torch.Tensor, state: QuantState, y=None) -> torch.Tensor:
-    _require_cuda(x)
     if x.dtype != torch.bfloat16:
         raise ValueError("qk_gemv_nf4 takes bf16 activations")
-    x2 = x.reshape(-1, state.cols)
+    x2 = _rows_of(x, state.cols, "x")
     M = x2.shape[0]
+    if y is not None:
+        _check_out(y, (M, state.rows), torch.bfloat16, "y")
+    _require_cuda(x, y)
     if y is None:
         y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=x.device)
-    _require_cuda(y)
     with _on(x.device):
         _check(lib().qk_gemv_nf4(_ptr(x2), M, ctypes.byref(state), _ptr(y), ctypes.c_void_p(_stream(x))))
     return y
@@ -388,10 +403,19 @@ def qk_gemm_nf4_workspace_size(M: int, r: int) -> int:
 
 def qk_gemm_nf4(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: float = 0.0, Y=None,
                 workspace=None) -> torch.Tensor:
-    _require_cuda(X, A, B)
-    X2 = X.reshape(-1, state.cols)
+    if (A is None) != (B is None):
+        raise ValueError("give both LoRA A and B, or neither")
+    for name, t in (("X", X), ("A", A), ("B", B)):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16, got {t.dtype}")
+    X2 = _rows_of(X, state.cols, "X")
     M = X2.shape[0]
-    r = 0 if A is None else A.shape[1]
+    r = 0 if A is None else A.shape[-1]
+    if A is not None and (tuple(A.shape) != (state.cols, r) or tuple(B.shape) != (r, state.rows)):
+        raise ValueError(f"shapes A {tuple(A.shape)}, B {tuple(B.shape)} do not match W [{state.rows}, {state.cols}]")
+    if Y is not None:
+        _check_out(Y, (M, state.rows), torch.bfloat16, "Y")
+    _require_cuda(X, A, B, Y)
     if Y is None:
         Y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=X.device)
     wsb = qk_gemm_nf4_workspace_size(M, r)

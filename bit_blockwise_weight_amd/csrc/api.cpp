@@ -66,7 +66,9 @@ qk_status validate_state(const qk_quant_state* st) {
         return fail(QK_ERR_BAD_STATE, "quant state: struct_bytes %u != %zu", st->struct_bytes, sizeof(qk_quant_state));
     if (st->rows < 1 || st->cols < 1 || st->n < 1)
         return fail(QK_ERR_BAD_STATE, "quant state: rows, cols and n must be >= 1");
-    if (st->rows > (int64_t)1 << 40 || st->cols > (int64_t)1 << 40 || st->n != st->rows * st->cols)
+    int64_t rc = 0;
+    if (st->rows > (int64_t)1 << 40 || st->cols > (int64_t)1 << 40 || st->n > (int64_t)1 << 40 ||
+        __builtin_mul_overflow(st->rows, st->cols, &rc) || st->n != rc)
         return fail(QK_ERR_BAD_STATE, "quant state: n (%lld) != rows (%lld) * cols (%lld)", (long long)st->n,
                     (long long)st->rows, (long long)st->cols);
     if (!valid_blocksize(st->blocksize))

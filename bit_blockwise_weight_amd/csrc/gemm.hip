@@ -490,8 +490,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
     // rows; offsets are bytes from the tile's first row (rows past M are clamped to the
     // last row: they only feed output rows that are never stored).
     // Piece v of a lane is row 64 v + 8 wave + lane / 8 of the tile, so the pieces are a
-    // uniform 64 rows apart (the stride goes into the scalar offset).  Rows past M lie
-    // beyond the resource's range, and buffer loads return zero there.
+    // uniform 64 rows apart.  The row part of the offset (row and piece) is in the vector
+    // offset, which the range check covers, and only the step's k offset is in the scalar
+    // offset, which it does not cover: a row past M has a vector offset at or beyond the
+    // resource's size, so its load returns zero and touches no memory, and a row inside
+    // the tile stays inside its own row for every k.
     const uint16_t* xtile = a.X + m0 * K;
     const int64_t xrows = M - m0 < TM ? M - m0 : TM;
     const __amdgpu_buffer_rsrc_t xrsrc =
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             lptr_t dst = (lptr_t)((__attribute__((address_space(3))) char*)base + (v * 8 + wave) * 1024);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, (int32_t)xsrc0, kbytes + v * xstride, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, (int32_t)(xsrc0 + (uint32_t)(v * xstride)), kbytes, 0, 0);
         }
     };
 
@@ -951,8 +954,9 @@ hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A
     a.r = A ? r : 0;
     a.lora_scale = lora_scale;
     if (a.M > 65535LL * BM || a.N > 65535LL * BN) return hipErrorInvalidValue;   // grid limits of both paths
+    // the fast path's buffer offsets of a 256-row X tile are 32-bit: 256 * K * 2 < 2^31
     const bool fast = (w.K % BK) == 0 && (w.K % w.w.blocksize) == 0 && (reinterpret_cast<uintptr_t>(X) % 16) == 0 &&
-                      (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0;
+                      (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0 && w.K < ((int64_t)1 << 22);
     if (fast) {
         *variant = "mfma 32x32x16 bf16, 256x256x64 tiles, W dequantized into B fragments, LoRA X*A pre-pass + epilogue";
         return launch_fast(a, workspace, s);

@@ -290,3 +290,42 @@ def test_int8_argument_errors(L):
     assert m(ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, 4, 4, 64, None, None, None, FAKE, None) \
         == qk.QK_ERR_INVALID_ARG
     assert m(FAKE, FAKE, FAKE, FAKE, 0, 4, 64, None, None, None, FAKE, None) == qk.QK_ERR_INVALID_ARG
+
+
+def test_binding_checks_gemv_gemm_operands(L):
+    """The binding refuses operands whose dtype or shape does not match the
+    descriptor before anything reaches the device (W here is [4, 64])."""
+    import torch
+    st = _state()
+    bf = torch.bfloat16
+    x = torch.zeros(2, 64, dtype=bf)
+    with pytest.raises(ValueError, match="bf16"):
+        qk.qk_gemv_nf4(x.float(), st)
+    with pytest.raises(ValueError, match="columns"):
+        qk.qk_gemv_nf4(torch.zeros(2, 48, dtype=bf), st)
+    with pytest.raises(ValueError, match="does not hold"):
+        qk.qk_gemv_nf4(x, st, torch.zeros(2, 3, dtype=bf))
+    with pytest.raises(ValueError, match="must be"):
+        qk.qk_gemv_nf4(x, st, torch.zeros(2, 4, dtype=torch.float32))
+    A, B = torch.zeros(64, 16, dtype=bf), torch.zeros(16, 4, dtype=bf)
+    with pytest.raises(ValueError, match="X must be bf16"):
+        qk.qk_gemm_nf4(x.half(), st, A, B, 2.0)
+    with pytest.raises(ValueError, match="A must be bf16"):
+        qk.qk_gemm_nf4(x, st, A.float(), B, 2.0)
+    with pytest.raises(ValueError, match="B must be bf16"):
+        qk.qk_gemm_nf4(x, st, A, B.half(), 2.0)
+    with pytest.raises(ValueError, match="do not match"):
+        qk.qk_gemm_nf4(x, st, torch.zeros(32, 16, dtype=bf), B, 2.0)
+    with pytest.raises(ValueError, match="do not match"):
+        qk.qk_gemm_nf4(x, st, A, torch.zeros(16, 3, dtype=bf), 2.0)
+    with pytest.raises(ValueError, match="do not match"):
+        qk.qk_gemm_nf4(x, st, A, torch.zeros(8, 4, dtype=bf), 2.0)
+    with pytest.raises(ValueError, match="neither"):
+        qk.qk_gemm_nf4(x, st, A, None, 2.0)
+    with pytest.raises(ValueError, match="does not hold"):
+        qk.qk_gemm_nf4(x, st, A, B, 2.0, Y=torch.zeros(3, 4, dtype=bf))
+    with pytest.raises(ValueError, match="must be"):
+        qk.qk_gemm_nf4(x, st, Y=torch.zeros(2, 4, dtype=torch.float16))
+    # well-formed host tensors get as far as the device check
+    with pytest.raises(ValueError, match="HIP device"):
+        qk.qk_gemm_nf4(x, st, A, B, 2.0)

@@ -61,6 +61,25 @@ def test_single_1024_quantize_dq_dequant():
         assert_bits_equal(y, want, f"dequant {dt}")
 
 
+def test_double_quant_ties_and_wide_mean_sum():
+    """The absmax arrays that pin the oracle's double quantization: ties of
+    RN(RN(c/s)*127) at +-0.5, +-2.5, +-1.5 (half-even: 0, 0, 2, -2, 2, -2) and a
+    mean whose fp64 sum 1 + 2^-24 needs 25 bits (one fp32 ulp above 0.2).  Each
+    is also repeated past one DQ block and past one tree-partial chunk."""
+    ties = np.float32(200.0) + np.float32([127.0, -127.0, 0.5, -0.5, 2.5, -2.5, 1.5, -1.5])
+    wide = np.float32([1.0, 2.0 ** -24, 0.0, 0.0, 0.0])
+    for name, a in (("ties", ties), ("wide-sum mean", wide), ("ties x 700", np.tile(ties, 700)),
+                    ("ties x 1200", np.tile(ties, 1200))):
+        say(f"case: double quant {name}, nb={a.size}")
+        q8, scale, mean = qk.qk_double_quant(dev_f32(a))
+        torch.cuda.synchronize()
+        oq, osig, omu = odd.double_quant(a)
+        assert_bits_equal(host(mean), np.float32([omu]), f"{name} mean")
+        assert_bits_equal(host(scale), osig, f"{name} scale")
+        assert_bits_equal(host(q8), oq, f"{name} q8")
+    assert oq[:8].tolist() == [127, -127, 0, 0, 2, -2, 2, -2]
+
+
 def dev_u8(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
 
