@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "QKError", "QuantState", "QuantizedWeight", "NF4", "FP4", "CUSTOM", "lib",
     "qk_make_codebook", "qk_quantize_blockwise", "qk_double_quant_workspace_size", "qk_double_quant",
-    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_last_error", "qk_version",
+    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemv_nf4_grouped", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_last_error", "qk_version",
     "qk_backend_info", "quantize",
 ]
 
@@ -68,6 +68,11 @@ class QuantState(ctypes.Structure):
     ]
 
 
+class GemvTask(ctypes.Structure):
+    """Mirror of qk_gemv_task (include/qk.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("st", ctypes.POINTER(QuantState)), ("y", ctypes.c_void_p)]
+
+
 _lib = None
 _load_error = None
 
@@ -98,6 +103,7 @@ def lib():
         "qk_state_init": [st_p, i32, ctypes.POINTER(ctypes.c_float), i64, i64, i32, vp, vp, vp, vp, vp],
         "qk_dequantize": [st_p, vp, i32, vp],
         "qk_gemv_nf4": [vp, i32, st_p, vp, vp],
+        "qk_gemv_nf4_grouped": [ctypes.POINTER(GemvTask), i32, i32, vp],
         "qk_gemm_nf4_workspace_size": [i64, i32, ctypes.POINTER(ctypes.c_size_t)],
         "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp, ctypes.c_size_t, vp],
         "qk_lora_merge": [st_p, vp, vp, i32, f32, vp, vp],
@@ -393,6 +399,41 @@ def qk_gemv_nf4(x: torch.Tensor, state: QuantState, y=None) -> torch.Tensor:
     with _on(x.device):
         _check(lib().qk_gemv_nf4(_ptr(x2), M, ctypes.byref(state), _ptr(y), ctypes.c_void_p(_stream(x))))
     return y
+
+
+def qk_gemv_nf4_grouped(tasks, ys=None):
+    """y_i = x_i deq(W_i)^T for a list of (x_i, state_i) with the same M, in as few
+    launches as the states allow.  Returns the list of y_i (bf16 [M, N_i])."""
+    tasks = list(tasks)
+    if not tasks:
+        raise ValueError("qk_gemv_nf4_grouped needs at least one (x, state)")
+    M = None
+    xs, outs = [], []
+    for i, (x, state) in enumerate(tasks):
+        if x.dtype != torch.bfloat16:
+            raise ValueError(f"task {i}: x must be bf16")
+        x2 = _rows_of(x, state.cols, f"task {i}: x")
+        if M is None:
+            M = x2.shape[0]
+        elif x2.shape[0] != M:
+            raise ValueError(f"task {i}: every x needs the same number of rows ({M}), got {x2.shape[0]}")
+        y = None if ys is None else ys[i]
+        if y is not None:
+            _check_out(y, (M, state.rows), torch.bfloat16, f"task {i}: y")
+        _require_cuda(x, y)
+        if y is None:
+            y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=x.device)
+        xs.append(x2)
+        outs.append(y)
+    arr = (GemvTask * len(tasks))()
+    for i, ((_, state), x2, y) in enumerate(zip(tasks, xs, outs)):
+        arr[i].x = x2.data_ptr()
+        arr[i].st = ctypes.pointer(state)
+        arr[i].y = y.data_ptr()
+    dev = xs[0].device
+    with _on(dev):
+        _check(lib().qk_gemv_nf4_grouped(arr, len(tasks), int(M), ctypes.c_void_p(_stream(xs[0]))))
+    return outs
 
 
 def qk_gemm_nf4_workspace_size(M: int, r: int) -> int:

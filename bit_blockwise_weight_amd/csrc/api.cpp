@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "qk_internal.h"
 
@@ -390,12 +391,50 @@ qk_status qk_qlora_backward(const void* dY, int64_t M, const qk_quant_state* st,
                     "qk_qlora_backward");
 }
 
+qk_status qk_gemv_nf4_grouped(const qk_gemv_task* tasks, int32_t ntasks, int32_t M, void* stream) {
+    if (!tasks) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4_grouped: tasks is NULL");
+    if (ntasks < 1 || ntasks > 256)
+        return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4_grouped: ntasks must be in 1..256 (got %d)", ntasks);
+    if (M < 1 || M > 16) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4_grouped: M must be in 1..16 (got %d)", M);
+    std::vector<qk::GemvItem> items((size_t)ntasks);
+    for (int32_t i = 0; i < ntasks; ++i) {
+        const qk_gemv_task& t = tasks[i];
+        const qk_status v = validate_state(t.st);
+        if (v != QK_OK) return v;
+        if (!t.x || !t.y) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4_grouped: task %d: NULL x or y", i);
+        if (!aligned(t.x, 16) || !aligned(t.y, 2))
+            return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4_grouped: task %d: x must be 16-byte aligned, y 2-byte", i);
+        items[i] = qk::GemvItem{t.x, t.y, qk::MatArgs{deq_args(t.st), t.st->rows, t.st->cols}};
+    }
+    // every y must be disjoint from the other ys and from every x
+    for (int32_t i = 0; i < ntasks; ++i) {
+        const uintptr_t y0 = reinterpret_cast<uintptr_t>(tasks[i].y);
+        const uintptr_t y1 = y0 + (uintptr_t)M * (uintptr_t)tasks[i].st->rows * 2;
+        for (int32_t j = 0; j < ntasks; ++j) {
+            const uintptr_t x0 = reinterpret_cast<uintptr_t>(tasks[j].x);
+            const uintptr_t x1 = x0 + (uintptr_t)M * (uintptr_t)tasks[j].st->cols * 2;
+            if (x0 < y1 && y0 < x1)
+                return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4_grouped: y of task %d overlaps x of task %d", i, j);
+            if (j == i) continue;
+            const uintptr_t z0 = reinterpret_cast<uintptr_t>(tasks[j].y);
+            const uintptr_t z1 = z0 + (uintptr_t)M * (uintptr_t)tasks[j].st->rows * 2;
+            if (z0 < y1 && y0 < z1)
+                return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4_grouped: y of task %d overlaps y of task %d", i, j);
+        }
+    }
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_gemv_group(items.data(), ntasks, M, reinterpret_cast<hipStream_t>(stream),
+                                          &g_gemv_variant),
+                    "qk_gemv_nf4_grouped");
+}
+
 qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* y, void* stream) {
     const qk_status v = validate_state(st);
     if (v != QK_OK) return v;
     if (!x || !y) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4: NULL x or y");
     if (M < 1 || M > 16) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4: M must be in 1..16 (got %d)", M);
-    if (!aligned(x, 16) || !aligned(y, 4)) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4: x must be 16-byte aligned, y 4-byte");
+    if (!aligned(x, 16) || !aligned(y, 2)) return fail(QK_ERR_INVALID_ARG, "qk_gemv_nf4: x must be 16-byte aligned, y 2-byte");
     const qk_status dev = ensure_device();
     if (dev != QK_OK) return dev;
     qk::MatArgs w{deq_args(st), st->rows, st->cols};
@@ -410,17 +449,26 @@ qk_status qk_gemm_nf4_workspace_size(int64_t M, int32_t r, size_t* bytes) {
     return ok();
 }
 
-qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const void* A, const void* B, int32_t r,
-                      float lora_scale, void* Y, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+qk_status check_gemm_args(const char* fn, const void* X, int64_t M, const qk_quant_state* st, const void* A,
+                          const void* B, int32_t r, float lora_scale, const void* Y) {
     const qk_status v = validate_state(st);
     if (v != QK_OK) return v;
-    if (!X || !Y) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: NULL X or Y");
-    if (M < 1 || M > ((int64_t)1 << 31)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: M must be in 1..2^31");
-    if ((A == nullptr) != (B == nullptr)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: give both LoRA A and B, or neither");
-    if (A && (r < 1 || r > 64)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: LoRA rank must be in 1..64 (got %d)", r);
-    if (A && !std::isfinite(lora_scale)) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: lora_scale is not finite");
+    if (!X || !Y) return fail(QK_ERR_INVALID_ARG, "%s: NULL X or Y", fn);
+    if (M < 1 || M > ((int64_t)1 << 31)) return fail(QK_ERR_INVALID_ARG, "%s: M must be in 1..2^31", fn);
+    if ((A == nullptr) != (B == nullptr)) return fail(QK_ERR_INVALID_ARG, "%s: give both LoRA A and B, or neither", fn);
+    if (A && (r < 1 || r > 64)) return fail(QK_ERR_INVALID_ARG, "%s: LoRA rank must be in 1..64 (got %d)", fn, r);
+    if (A && !std::isfinite(lora_scale)) return fail(QK_ERR_INVALID_ARG, "%s: lora_scale is not finite", fn);
     if (!aligned(X, 2) || !aligned(Y, 2) || (A && (!aligned(A, 2) || !aligned(B, 2))))
-        return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4: bf16 buffers must be 2-byte aligned");
+        return fail(QK_ERR_INVALID_ARG, "%s: bf16 buffers must be 2-byte aligned", fn);
+    return QK_OK;
+}
+}  // namespace
+
+qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const void* A, const void* B, int32_t r,
+                      float lora_scale, void* Y, void* workspace, size_t workspace_bytes, void* stream) {
+    const qk_status v = check_gemm_args("qk_gemm_nf4", X, M, st, A, B, r, lora_scale, Y);
+    if (v != QK_OK) return v;
     const size_t need = qk::gemm_workspace_bytes(M, A ? r : 0);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(QK_ERR_WORKSPACE, "qk_gemm_nf4: workspace of %zu bytes needed, %zu given", need,

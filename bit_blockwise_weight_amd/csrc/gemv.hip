@@ -35,7 +35,10 @@
 // Generic path (any K, blocks straddling rows): one wave per row, each lane walks
 // k = lane, lane + 64, ... and dequantizes each weight exactly as the dequantize
 // kernel does (bf16 of level * a'), with fp32 accumulation.
+#include <algorithm>
+#include <cstring>
 #include <type_traits>
+#include <vector>
 
 #include "qk_internal.h"
 #include "qk_device.h"
@@ -64,89 +67,243 @@ __device__ __forceinline__ float row_scale(const DeqArgs& a, int64_t blk) {
 }
 
 // Fast path kernel (see the top of the file).
-constexpr int kChunkK = 512;                   // k per chunk (8 blocks of 64)
-constexpr int kChunkBlocks = kChunkK / 64;
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-struct ChunkRegs {
-    u32x4_t c[4];                // 16-byte code pieces of this lane (4 rows x 256 bytes per wave load)
-    uint4 x[kChunkBlocks][2];    // x[m][c0 + 64 b + 16 h + 8 t .. +8], t = 0, 1
-    int32_t q[kChunkBlocks];     // q8 (nested) or absmax bits
-    float d[kChunkBlocks];       // dq scale (nested)
+// A slice of rows of one weight (a whole weight unless it is very tall).
+struct GemvTask {
+    const uint16_t* x;       // [M, K] bf16 bits
+    uint16_t* y;             // y of the slice's first row: y[m * ystride + row]
+    const uint8_t* codes;    // codes of the slice's first row
+    const void* sc;          // the weight's q8 (int8, nested) or absmax (fp32), from its first block
+    const float* dq_scale;   // nested
+    const float* dq_mean;    // nested
+    int64_t N;               // rows of the slice
+    int64_t ystride;         // rows of the weight
+    int64_t qbase;           // quantization block of the slice's first element
+    int32_t K;
+    int32_t nchunk;          // ceil(K / 512)
+    int32_t jobs;            // jobs per wave per tile: ceil(nchunk / S)
+    int32_t item0;           // first tile of the slice in the launch
+    int32_t code_bytes;      // N * K / 2 of the slice (< 2^31)
+    int32_t sc_bytes;        // bytes of the weight's q8 (rounded up to dwords) or absmax (< 2^31)
+    int32_t dq_bytes;        // bytes of the weight's dq_scale (nested)
+    int32_t pad;
 };
 
-template <bool kNested, int S>
-__global__ __launch_bounds__(S * 64) void gemv_lds_kernel(GemvArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t tab[256 * kTabCopies];   // 64 KB byte -> bf16 pair
-    __shared__ __attribute__((aligned(1024))) uint4 cb[S][256];               // codes chunk, 4 KB per wave
+struct GemvGroup {
+    GemvTask t[kMaxGemvTasks];
+    float levels[16];
+    int32_t ntasks;
+    int32_t nitems;          // tiles of 16 rows over all slices (<= kOutSlots * grid)
+    int32_t M;
+    int32_t qs;              // log2(block size) - 6
+};
+
+constexpr int kChunkK = 512;                   // k per job (8 blocks of 64)
+constexpr int kChunkBlocks = kChunkK / 64;
+constexpr int kOutSlots = 32;                  // tiles per workgroup whose outputs LDS holds until the end
+constexpr int kXPitch = 80;                    // 16-byte units per staged x row (64 used)
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Rotation of staged x row m: unit u of the row sits in slot m * kXPitch + u + xrot(m).  A
+// fragment read of one (block, half) touches unit 8 b + 2 h + t of rows m < M in lanes
+// (h, m); with this rotation those 16-byte reads of rows 0..3 fall in 16 distinct groups
+// of 4 banks, and the writes of one row (unit = lane) are consecutive.
+__device__ __forceinline__ int xrot(int m) { return 8 * (m & 1) + (m >> 1); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One job's registers: the scale inputs (the codes and x rows of a job go to LDS directly).
+struct JobRegs {
+    u32x3_t q;                   // nested: 12 bytes from the aligned start of the job's q8 run
+    u32x4_t f0, f1;              // plain: absmax of the job's quantization blocks (up to 8)
+    u32x2_t d;                   // nested: dq scales of the first block's dq block and the next
+    uint32_t qinfo;              // nested: (qf & 3) | (blocks left in the first dq block) << 2
+};
+
+// S waves per workgroup, MX rows of x staged per job (M <= MX), C copies of the code table,
+// QS = log2(block size) - 6 (a job's 8 blocks of 64 fall in 8 >> QS quantization blocks).
+//
+// A job is 16 rows x 512 k: its codes (4 KB) and x rows (M x 1 KB) are copied from memory
+// straight into one of the wave's two LDS slots by buffer loads with the LDS bit, 16 bytes
+// per lane and instruction (so 4 + M vector memory instructions carry a job's bulk, with no
+// registers and no LDS writes of the wave's own); the scales come with two more.  The two
+// slots are separate LDS objects, so the wait before reading one leaves the other's copies
+// in flight.
+template <int S, int MX, int C, bool kNested, int QS>
+__global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
+    constexpr int kR = MX < 4 ? MX : 4;        // output registers of a lane that can hold a row m < M
+    constexpr int kSlotX = MX * kXPitch;       // 16-byte units of a staged x slot
+    __shared__ __attribute__((aligned(16))) uint32_t tab[256 * C];            // byte -> bf16 pair, C copies
+    __shared__ __attribute__((aligned(1024))) uint4 cb0[S * 256];             // codes, slot 0 (4 KB per wave)
+    __shared__ __attribute__((aligned(1024))) uint4 cb1[S * 256];             // codes, slot 1
+    __shared__ __attribute__((aligned(16))) uint4 xs0[S * kSlotX];            // x rows, slot 0
+    __shared__ __attribute__((aligned(16))) uint4 xs1[S * kSlotX];            // x rows, slot 1
+    __shared__ __attribute__((aligned(16))) float red[2][S][kR][64];          // per-wave partial tiles
+    __shared__ __attribute__((aligned(16))) uint16_t outb[kOutSlots][16 * MX]; // finished outputs, bf16
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;                   // weight row of the tile (and x row m of the A operand)
     const int h = lane >> 4;                   // 16-weight group of a 64-k block
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t K = a.K;
-    const int64_t nblk = K / 64;
-    const int64_t nchunk = (K + kChunkK - 1) / kChunkK;
-    const int64_t ncw = (nchunk - wave + S - 1) / S;       // chunks of this wave
-    const int M = a.M;
-    const bool x_ok = n < M;
-    const uint16_t* xrow = a.x + (int64_t)(x_ok ? n : 0) * K + 16 * h;
-    const int64_t rowc = n0 + n < a.N ? n0 + n : a.N - 1;
-    const int64_t qb0 = (rowc * K) >> a.w.blocksize_log2;  // first quantization block of the row
-    const int bshift = a.w.blocksize_log2 - 6;
-    const float mean = kNested ? *a.w.dq_mean : 0.0f;
-    const int64_t row_bytes = K / 2;
+    const int M = g.M;
+    constexpr int qs = QS;
+    const int32_t G = (int32_t)gridDim.x;
+    const int32_t wg = (int32_t)blockIdx.x;
 
-    // code loads: load i, lane L fetches piece (L % 16) ^ r of row r = 4 i + L / 16
-    const uint8_t* csrc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * i + (lane >> 4);
-        const int64_t gr = n0 + r < a.N ? n0 + r : a.N - 1;
-        csrc[i] = a.w.codes + gr * row_bytes + 16 * ((lane & 15) ^ r);
-    }
-    auto load = [&](int64_t c, ChunkRegs& cr) {
-        const int64_t cc = c < nchunk ? c : nchunk - 1;
-        const int64_t cbase = cc * (kChunkK / 2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // pieces past the end of a row (last, partial chunk) are clamped and never used
-            const int64_t off = cbase + 16 * ((lane & 15) ^ (4 * i + (lane >> 4)));
-            const int64_t adj = off + 16 <= row_bytes ? 0 : row_bytes - 16 - off;
-            cr.c[i] = *reinterpret_cast<const u32x4_t*>(csrc[i] + cbase + adj);
-        }
-#pragma unroll
-        for (int b = 0; b < kChunkBlocks; ++b) {
-            int64_t blk = cc * kChunkBlocks + b;
-            blk = blk < nblk ? blk : nblk - 1;
-            const uint4* xp = reinterpret_cast<const uint4*>(xrow + 64 * blk);
-            cr.x[b][0] = xp[0];     // rows m >= M read row 0 and are zeroed at use
-            cr.x[b][1] = xp[1];
-            const int64_t qb = qb0 + (blk >> bshift);
-            if constexpr (kNested) {
-                cr.q[b] = (int32_t)a.w.q8[qb];
-                cr.d[b] = a.w.dq_scale[qb / QK_DQ_BLOCK];
-            } else {
-                cr.q[b] = (int32_t)as_uint(a.w.absmax[qb]);
-                cr.d[b] = 0.0f;
-            }
+    // This workgroup takes the tiles wg, wg + G, ...; in each, wave w takes the jobs
+    // (chunks of 512 k) w, w + S, ...  Every wave of the workgroup sees the same tiles and
+    // job counts, so the tile ends are uniform in the workgroup.  The load cursor copies
+    // its slice's fields when it moves to another slice; the compute cursor only needs
+    // the job count, the row length and the mean (a scalar load when it changes slice).
+    struct LoadCur {
+        int32_t item, task, j, jobs, nchunk, K, item0, code_bytes, sc_bytes, dq_bytes;
+        int64_t N, qbase;
+        const uint16_t* x;
+        const uint8_t* codes;
+        const void* sc;
+        const float* dq_scale;
+    };
+    struct CompCur {
+        int32_t item, task, j, jobs, nblk;
+        float mu;
+    };
+    auto task_from = [&](int32_t item, int32_t t) {
+        while (t + 1 < g.ntasks && item >= g.t[t + 1].item0) ++t;
+        return t;
+    };
+    auto set_load_task = [&](LoadCur& c, int32_t t) {
+        const GemvTask& T = g.t[t];
+        c.task = t;
+        c.jobs = T.jobs;
+        c.nchunk = T.nchunk;
+        c.K = T.K;
+        c.item0 = T.item0;
+        c.code_bytes = T.code_bytes;
+        c.sc_bytes = T.sc_bytes;
+        c.dq_bytes = T.dq_bytes;
+        c.N = T.N;
+        c.qbase = T.qbase;
+        c.x = T.x;
+        c.codes = T.codes;
+        c.sc = T.sc;
+        c.dq_scale = T.dq_scale;
+    };
+    auto set_comp_task = [&](CompCur& c, int32_t t) {
+        c.task = t;
+        c.jobs = g.t[t].jobs;
+        c.nblk = g.t[t].K / 64;
+        // a scalar load (constant address space: the mean does not change during the
+        // kernel): no vector memory operation under the task-switch condition
+        c.mu = kNested ? *(const __attribute__((address_space(4))) float*)(uintptr_t)g.t[t].dq_mean : 0.0f;
+    };
+    auto advance_load = [&](LoadCur& c) {
+        if (++c.j == c.jobs) {
+            c.j = 0;
+            c.item += G;
+            if (c.item < g.nitems && c.task + 1 < g.ntasks && c.item >= g.t[c.task + 1].item0)
+                set_load_task(c, task_from(c.item, c.task + 1));
         }
     };
-    u32x4_t* mine = reinterpret_cast<u32x4_t*>(cb[wave]);
-    auto stage = [&](const ChunkRegs& cr) {
+    auto advance_comp = [&](CompCur& c) {
+        if (++c.j == c.jobs) {
+            c.j = 0;
+            c.item += G;
+            if (c.item < g.nitems && c.task + 1 < g.ntasks && c.item >= g.t[c.task + 1].item0)
+                set_comp_task(c, task_from(c.item, c.task + 1));
+        }
+    };
+    LoadCur lc;
+    lc.item = wg;
+    lc.j = 0;
+    set_load_task(lc, task_from(wg, 0));
+    CompCur cc;
+    cc.item = wg;
+    cc.j = 0;
+    set_comp_task(cc, lc.task);
+
+    auto load = [&](const LoadCur& c, JobRegs& jr, auto slot) {
+        constexpr bool kB = decltype(slot)::value;
+        // a job past the end (after the last one) clamps its rows to the last row of its
+        // slice: it reads valid memory, mostly from the cache, and is never used
+        const int64_t N = c.N;
+        const int64_t K = c.K;
+        const int64_t row_bytes = K / 2;
+        const int64_t n0 = (int64_t)(c.item - c.item0) * 16;
+        const int32_t chunk = c.j * S + wave;
+        const int32_t ch = chunk < c.nchunk ? chunk : c.nchunk - 1;
+        // codes: load i, lane L fetches piece (L % 16) ^ r of row r = 4 i + L / 16 (rows past
+        // N clamped to the last; pieces past the end of a row, in a partial chunk, clamped
+        // to its last 16 bytes and never used), which lands in slot unit 64 i + L
+        const __amdgpu_buffer_rsrc_t cr = buf_rsrc(c.codes, c.code_bytes);
+        __attribute__((address_space(3))) char* cdst =
+            (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? cb1 : cb0) + wave * 4096;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mine[i * 64 + lane] = cr.c[i];    // slot 64 i + L = 16 r + (piece ^ r)
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const int64_t gr = n0 + r < N ? n0 + r : N - 1;
+            int64_t off = (int64_t)ch * (kChunkK / 2) + 16 * ((lane & 15) ^ r);
+            off = off + 16 <= row_bytes ? off : row_bytes - 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr_t)(cdst + i * 1024), 16,
+                                                     (uint32_t)(gr * row_bytes + off), 0, 0, 0);
+        }
+        // x rows m < MX of the job's k, 16 bytes per lane: unit L of row m lands in slot unit
+        // m * kXPitch + xrot(m) + L (rows past M, and k past the row in a partial chunk, read
+        // zero or the next row: never used)
+        const __amdgpu_buffer_rsrc_t xr = buf_rsrc(c.x, (int32_t)(M * K * 2));
+        __attribute__((address_space(3))) char* xdst =
+            (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? xs1 : xs0) + wave * (kSlotX * 16);
+        const uint32_t xo = (uint32_t)(((int64_t)ch * kChunkK + 8 * lane) * 2);
+#pragma unroll
+        for (int m = 0; m < MX; ++m)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xdst + (m * kXPitch + xrot(m)) * 16), 16,
+                                                     xo + (uint32_t)(m * K * 2), 0, 0, 0);
+        // the job's quantization blocks of row n are consecutive, from qf on (a partial
+        // chunk's blocks past the row are read from the next row or as zero, never used)
+        const int64_t rowc = n0 + n < N ? n0 + n : N - 1;
+        const int64_t qf = c.qbase + ((rowc * K) >> (qs + 6)) + ((int64_t)(ch * kChunkBlocks) >> qs);
+        const __amdgpu_buffer_rsrc_t sr = buf_rsrc(c.sc, c.sc_bytes);
+        if constexpr (kNested) {
+            jr.q = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(sr, (uint32_t)(qf & ~(int64_t)3), 0, 0));
+            const __amdgpu_buffer_rsrc_t dr = buf_rsrc(c.dq_scale, c.dq_bytes);
+            jr.d = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   dr, (uint32_t)((qf / QK_DQ_BLOCK) * 4), 0, 0));
+            jr.qinfo = (uint32_t)(qf & 3) | ((uint32_t)(QK_DQ_BLOCK - qf % QK_DQ_BLOCK) << 2);
+        } else {
+            jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)(qf * 4), 0, 0));
+            if constexpr (QS == 0)
+                jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)(qf * 4 + 16), 0, 0));
+        }
     };
 
     floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t lane_sel = (uint32_t)lane * 4u;
+    const uint32_t lane_sel = C == 64 ? (uint32_t)lane * 4u : (uint32_t)(lane & 31) * 8u;
     const char* tabb = reinterpret_cast<const char*>(tab);
-    const char* mb = reinterpret_cast<const char*>(mine);
-    auto compute = [&](int64_t c, const ChunkRegs& cr) {
+    // A operand rows m >= M are another row's data: they only feed output rows that are
+    // never stored
+    const int xrow = n < M ? n : M - 1;
+    const int xunit = xrow * kXPitch + xrot(xrow) + 2 * h;
+    auto compute = [&](const CompCur& c, const JobRegs& jr, auto slot) {
+        constexpr bool kB = decltype(slot)::value;
+        const char* mb = reinterpret_cast<const char*>(kB ? cb1 : cb0) + wave * 4096;
+        const u32x4_t* xf = reinterpret_cast<const u32x4_t*>(kB ? xs1 : xs0) + wave * kSlotX + xunit;
+        // blocks past the row's end, and every block of a job past the end, add nothing
+        const int32_t nblk = c.item < g.nitems ? c.nblk : 0;
+        const int32_t b0 = (c.j * S + wave) * kChunkBlocks;
+        uint32_t qlo = 0, qhi = 0, split = 0;
+        if constexpr (kNested) {
+            const uint32_t sh = jr.qinfo & 3u;
+            qlo = __builtin_amdgcn_alignbyte(jr.q[1], jr.q[0], sh);
+            qhi = __builtin_amdgcn_alignbyte(jr.q[2], jr.q[1], sh);
+            split = jr.qinfo >> 2;
+        }
 #pragma unroll
-        for (int b = 0; b < kChunkBlocks; ++b) {
-            const int piece = 2 * b + (h >> 1);
+        for (int bb = 0; bb < kChunkBlocks; ++bb) {
+            const int piece = 2 * bb + (h >> 1);
             const uint2 cw = *reinterpret_cast<const uint2*>(mb + (16 * n + (piece ^ n)) * 16 + 8 * (h & 1));
             const uint32_t cws[2] = {cw.x, cw.y};
             floatx4_t part = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -154,86 +311,139 @@ __global__ __launch_bounds__(S * 64) void gemv_lds_kernel(GemvArgs a) {
             for (int t = 0; t < 2; ++t) {
                 uint32_t wv[4];
 #pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    const uint32_t addr = __builtin_amdgcn_perm(cws[t], lane_sel, 0x0C0C0400u | ((uint32_t)(4 + bb) << 8));
-                    wv[bb] = *reinterpret_cast<const uint32_t*>(tabb + addr);
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    uint32_t addr = __builtin_amdgcn_perm(cws[t], lane_sel, 0x0C0C0400u | ((uint32_t)(4 + k4) << 8));
+                    if constexpr (C == 32) addr >>= 1;
+                    wv[k4] = *reinterpret_cast<const uint32_t*>(tabb + addr);
                 }
-                const uint4 z = make_uint4(0, 0, 0, 0);
-                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x_ok ? cr.x[b][t] : z),
+                const u32x4_t xv = xf[8 * bb + t];
+                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
                                                                __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3])),
                                                                part, 0, 0, 0);
             }
-            float sc;
-            if constexpr (kNested) sc = __fadd_rn(__fmul_rn((float)cr.q[b], cr.d[b]), mean);
-            else sc = as_float((uint32_t)cr.q[b]);
-            const bool live = c * kChunkBlocks + b < nblk;
+            // the block's scale: quantization block bb >> qs of the job
+            const uint32_t qq = (uint32_t)bb >> qs;
+            float a;
+            if constexpr (kNested) {
+                const uint32_t word = qq < 4 ? qlo : qhi;
+                const int32_t q8 = __builtin_amdgcn_sbfe((int32_t)word, 8 * (qq & 3), 8);
+                const float dsc = __builtin_bit_cast(float, qq < split ? jr.d[0] : jr.d[1]);
+                a = __fadd_rn(__fmul_rn((float)q8, dsc), c.mu);
+            } else {
+                const uint32_t fsel[8] = {jr.f0[0], jr.f0[1], jr.f0[2], jr.f0[3], jr.f1[0], jr.f1[1], jr.f1[2], jr.f1[3]};
+                a = __builtin_bit_cast(float, fsel[qq]);
+            }
+            // a block past the row's end weighs 0 (its products are finite: the codes, x and
+            // scales it read are valid data or zero); a select of the weight, not of the
+            // accumulation, keeps the block loop free of branches
+            const float aw = b0 + bb < nblk ? a : 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = live ? __builtin_fmaf(part[r], sc, acc[r]) : acc[r];
+            for (int r = 0; r < kR; ++r) acc[r] = __builtin_fmaf(part[r], aw, acc[r]);
         }
     };
 
-    const int64_t c0 = wave;
-    ChunkRegs ra, rb;
-    load(c0, ra);   // clamped: a wave without chunks reads a valid one and never uses it
+    // bare barrier: __syncthreads() would add a fence that waits for the loads in flight
+    auto bare_barrier = [] {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS accesses are done; vmcnt untouched
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    int32_t done = 0;          // tiles finished by this workgroup
+    int p = 0;                 // reduction buffer parity
+    // the end of a tile: the S waves' partial tiles are added in wave order and the
+    // outputs kept in LDS; the buffer of one parity is written again two tiles later,
+    // after a barrier that every reader of it has passed
+    auto tile_end = [&]() {
+#pragma unroll
+        for (int r = 0; r < kR; ++r) red[p][wave][r][lane] = acc[r];
+        bare_barrier();
+        const int e = threadIdx.x;             // M * 16 <= 256 <= S * 64 outputs per tile
+        if (e < M * 16) {
+            // output (m, nn): register r = m % 4 of lane nn + 16 (m / 4)
+            const int m = e >> 4, nn = e & 15;
+            const int r = m & 3, ln = nn + 16 * (m >> 2);
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < S; ++w) v += red[p][w][r][ln];
+            outb[done][e] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+        }
+        acc = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        p ^= 1;
+        ++done;
+    };
+    auto end_job = [&]() {
+        if (cc.item < g.nitems && cc.j == cc.jobs - 1) tile_end();
+        advance_comp(cc);
+    };
+
+    // jobs of each wave: the workgroup's tiles of each slice times its jobs per tile
+    int32_t njobs = 0;
+    for (int32_t t = 0; t < g.ntasks; ++t) {
+        const int32_t lo = g.t[t].item0, hi = t + 1 < g.ntasks ? g.t[t + 1].item0 : g.nitems;
+        const int32_t k0 = lo <= wg ? 0 : (lo - wg + G - 1) / G;   // first k with wg + k G >= lo
+        const int32_t k1 = hi <= wg ? 0 : (hi - wg + G - 1) / G;   // first k with wg + k G >= hi
+        njobs += (k1 - k0) * g.t[t].jobs;
+    }
+
+    using SlotA = std::integral_constant<bool, false>;
+    using SlotB = std::integral_constant<bool, true>;
+    JobRegs ra, rb;
+    load(lc, ra, SlotA{});
+    advance_load(lc);
+    load(lc, rb, SlotB{});
+    advance_load(lc);
     {
-        // pair table, 64 copies: entry i = 64 b + copy for byte b.  Wave w writes the bytes
-        // b = w + S j, whose nibbles are (j / (16 / S), w + S (j % (16 / S))); the level reads
-        // are uniform (scalar loads), so they do not wait for the loads in flight.
+        // pair table: entry C b + copy for byte b.  Wave w writes the bytes b = w + S j,
+        // whose nibbles are (j / (16 / S), w + S (j % (16 / S))); the level reads are
+        // uniform (scalar loads), so they do not wait for the copies in flight
         constexpr int kLo = 16 / S;
         float lo[kLo];
 #pragma unroll
-        for (int q = 0; q < kLo; ++q) lo[q] = a.w.levels[wave + S * q];
+        for (int q = 0; q < kLo; ++q) lo[q] = g.levels[wave + S * q];
+        if (lane < C) {
 #pragma unroll
-        for (int jj = 0; jj < 256 / S; ++jj) {
-            const float hi_nib = a.w.levels[jj / kLo];
-            tab[(wave + S * jj) * kTabCopies + lane] = pack_bf16x2(hi_nib, lo[jj % kLo]);
+            for (int jj = 0; jj < 256 / S; ++jj) {
+                const float hi_nib = g.levels[jj / kLo];
+                tab[(wave + S * jj) * C + lane] = pack_bf16x2(hi_nib, lo[jj % kLo]);
+            }
         }
     }
-    // a bare barrier: __syncthreads() would add a fence that waits for the loads in flight
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) (the table writes), vmcnt and expcnt untouched
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    stage(ra);
-    // Two chunks per iteration, the register sets alternating by name (a copy would wait
-    // for its loads): load the next chunk, compute this one from LDS, then stage the next.
-    // Every load inside the loop is unconditional and the last one or two chunks are
-    // peeled: a load under a branch merges the wait counts at the join, and the compute
-    // of this chunk would then wait for the next chunk's loads.
-    int64_t i = 0;
-    for (; i + 2 < ncw; i += 2) {
-        const int64_t c = c0 + (int64_t)S * i;
-        load(c + S, rb);
-        compute(c, ra);
-        stage(rb);
-        load(c + 2 * S, ra);
-        compute(c + S, rb);
-        stage(ra);
-    }
-    if (ncw - i == 2) {
-        const int64_t c = c0 + (int64_t)S * i;
-        load(c + S, rb);
-        compute(c, ra);
-        stage(rb);
-        compute(c + S, rb);
-    } else if (ncw - i == 1) {
-        compute(c0 + (int64_t)S * i, ra);
-    }
+    bare_barrier();
+    // Two jobs in flight: each job is computed from its LDS slot (the wait is for its own
+    // copies, issued before the other slot's), then its slot is refilled with the job two
+    // ahead before the tile end's barrier.  The loop runs whole pairs of jobs with no
+    // condition around a load (the last pair may end with a job past the end, which adds
+    // nothing) and writes no global memory, so the compiler's wait before each compute
+    // leaves the other slot's copies outstanding.  A slot is refilled only after every LDS
+    // read of it has returned: the compute consumes all of them.
+    const int32_t npairs = (njobs + 1) / 2;
+    int32_t it = 0;
+    do {
+        compute(cc, ra, SlotA{});
+        load(lc, ra, SlotA{});
+        advance_load(lc);
+        end_job();
+        compute(cc, rb, SlotB{});
+        load(lc, rb, SlotB{});
+        advance_load(lc);
+        end_job();
+    } while (++it < npairs);
 
-    // reduce the S waves' tiles in a fixed order: red[wave][r][lane] (over the table)
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(tab);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
-    __syncthreads();
-    // output (m, nn): register r = m % 4 of lane nn + 16 (m / 4)
-    for (int e = threadIdx.x; e < M * 16; e += S * 64) {
-        const int m = e >> 4, nn = e & 15;
-        const int r = m & 3, ln = nn + 16 * (m >> 2);
-        float v = 0.0f;
-        for (int w = 0; w < S; ++w) v += red[(w * 4 + r) * 64 + ln];
-        const int64_t on = n0 + nn;
-        if (on < a.N) a.y[(int64_t)m * a.N + on] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    // outputs of the workgroup's tiles, from LDS to y
+    bare_barrier();
+    int32_t t = 0;
+    for (int32_t k = 0; k < done; ++k) {
+        const int32_t item = wg + k * G;
+        t = task_from(item, t);
+        const GemvTask& T = g.t[t];
+        const int64_t n0 = (int64_t)(item - T.item0) * 16;
+        const int e = threadIdx.x;
+        if (e < M * 16) {
+            const int m = e >> 4, nn = e & 15;
+            if (n0 + nn < T.N) T.y[(int64_t)m * T.ystride + n0 + nn] = outb[k][e];
+        }
     }
 }
 
@@ -272,35 +482,141 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
 
 }  // namespace
 
+hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hipStream_t s,
+                             const char** variant) {
+    // more than 4 rows of x: groups of at most 4 rows (each a launch that reads the weights)
+    if (M > 4) {
+        std::vector<GemvItem> part(items, items + count);
+        for (int32_t m0 = 0; m0 < M; m0 += 4) {
+            const int32_t mr = M - m0 < 4 ? M - m0 : 4;
+            for (int32_t i = 0; i < count; ++i) {
+                part[i].x = reinterpret_cast<const uint16_t*>(items[i].x) + (int64_t)m0 * items[i].w.K;
+                part[i].y = reinterpret_cast<uint16_t*>(items[i].y) + (int64_t)m0 * items[i].w.N;
+            }
+            const hipError_t e = launch_gemv_group(part.data(), count, mr, s, variant);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    // waves per workgroup: 8 for M = 1, else 4 (LDS holds two staged jobs of every wave)
+    const int S = M == 1 ? 8 : 4;
+    const int64_t cus = device_cu_count();
+    const int64_t max_tiles = kOutSlots * cus;     // tiles per launch: LDS holds each workgroup's outputs
+    // weights the fast kernel cannot take go one by one through the generic kernel; the
+    // others are cut into slices of rows whose codes fit a 31-bit buffer offset and whose
+    // tiles fit one launch
+    std::vector<GemvTask> slices;
+    std::vector<const DeqArgs*> slice_w;
+    for (int32_t i = 0; i < count; ++i) {
+        const MatArgs& w = items[i].w;
+        const int64_t nb = (w.N * w.K) >> w.w.blocksize_log2;
+        const bool ok = (w.K % kStep) == 0 && (w.K % w.w.blocksize) == 0 &&
+                        (reinterpret_cast<uintptr_t>(items[i].x) % 16) == 0 &&
+                        (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0 && (int64_t)M * w.K * 2 < ((int64_t)1 << 31) &&
+                        w.K / 2 * 16 < ((int64_t)1 << 31) && (w.w.nested ? nb : 4 * nb) < ((int64_t)1 << 31);
+        if (!ok) {
+            GemvArgs a;
+            a.x = reinterpret_cast<const uint16_t*>(items[i].x);
+            a.y = reinterpret_cast<uint16_t*>(items[i].y);
+            a.w = w.w;
+            a.N = w.N;
+            a.K = w.K;
+            a.M = M;
+            *variant = "generic (per-element dequantization, one wave per row)";
+            hipLaunchKernelGGL(gemv_generic_kernel, dim3((unsigned)((w.N + 3) / 4)), dim3(256), 0, s, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        int64_t rows = (((int64_t)1 << 31) - 1) / (w.K / 2);
+        rows = rows < max_tiles * 16 ? rows : max_tiles * 16;
+        rows -= rows % 16;
+        for (int64_t r0 = 0; r0 < w.N; r0 += rows) {
+            GemvTask t{};
+            const int64_t nr = w.N - r0 < rows ? w.N - r0 : rows;
+            t.x = reinterpret_cast<const uint16_t*>(items[i].x);
+            t.y = reinterpret_cast<uint16_t*>(items[i].y) + r0;
+            t.codes = w.w.codes + r0 * (w.K / 2);
+            t.sc = w.w.nested ? static_cast<const void*>(w.w.q8) : static_cast<const void*>(w.w.absmax);
+            t.dq_scale = w.w.dq_scale;
+            t.dq_mean = w.w.dq_mean;
+            t.N = nr;
+            t.ystride = w.N;
+            t.qbase = (r0 * w.K) >> w.w.blocksize_log2;
+            t.K = (int32_t)w.K;
+            t.nchunk = (int32_t)((w.K + kChunkK - 1) / kChunkK);
+            t.jobs = (t.nchunk + S - 1) / S;
+            t.code_bytes = (int32_t)(nr * (w.K / 2));
+            // buffer loads check their range per dword and return zero for a dword that ends
+            // past it: the q8 range is rounded up to whole dwords so the last q8 bytes read
+            // back (the up to 3 bytes after the array share its last dword, and so its page;
+            // they are never used)
+            t.sc_bytes = (int32_t)(w.w.nested ? (nb + 3) / 4 * 4 : 4 * nb);
+            t.dq_bytes = (int32_t)(w.w.nested ? 4 * ((nb + QK_DQ_BLOCK - 1) / QK_DQ_BLOCK) : 0);
+            slices.push_back(t);
+            slice_w.push_back(&w.w);
+        }
+    }
+    // launches of slices that share the code table, block size and nesting, longest rows
+    // first (a workgroup takes tiles blockIdx.x, + grid, ...: the long tiles are spread
+    // over the workgroups before the short ones)
+    std::vector<size_t> order(slices.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) { return slices[a].K > slices[b].K; });
+    std::vector<bool> used(slices.size(), false);
+    for (size_t f = 0; f < order.size(); ++f) {
+        if (used[order[f]]) continue;
+        const DeqArgs& w0 = *slice_w[order[f]];
+        GemvGroup gg;
+        std::memset(&gg, 0, sizeof(gg));
+        std::memcpy(gg.levels, w0.levels, sizeof(gg.levels));
+        gg.M = M;
+        int64_t nitems = 0;
+        for (size_t f2 = f; f2 < order.size() && gg.ntasks < kMaxGemvTasks; ++f2) {
+            const size_t k = order[f2];
+            if (used[k]) continue;
+            const DeqArgs& w = *slice_w[k];
+            if (w.nested != w0.nested || w.blocksize != w0.blocksize ||
+                std::memcmp(w.levels, w0.levels, sizeof(w.levels)) != 0)
+                continue;
+            const int64_t tiles = (slices[k].N + 15) / 16;
+            if (nitems + tiles > max_tiles) continue;
+            GemvTask& t = gg.t[gg.ntasks++];
+            t = slices[k];
+            t.item0 = (int32_t)nitems;
+            nitems += tiles;
+            used[k] = true;
+        }
+        gg.nitems = (int32_t)nitems;
+        gg.qs = w0.blocksize_log2 - 6;
+        const unsigned grid = (unsigned)(nitems < cus ? nitems : cus);
+        *variant = "mfma 16x16x32 bf16, persistent grouped launch: 16-row tiles, 8 (M <= 4) or 4 waves split K "
+                   "in 512-k jobs, three in flight per wave, codes loaded in MFMA layout, x rows staged through LDS";
+#define QK_GEMV_LAUNCH_Q(SS, MXX, CC, QQ)                                                                    \
+    do {                                                                                                     \
+        if (w0.nested) hipLaunchKernelGGL((gemv_group_kernel<SS, MXX, CC, true, QQ>), dim3(grid), dim3(SS * 64), 0, s, gg); \
+        else hipLaunchKernelGGL((gemv_group_kernel<SS, MXX, CC, false, QQ>), dim3(grid), dim3(SS * 64), 0, s, gg); \
+    } while (0)
+#define QK_GEMV_LAUNCH(SS, MXX, CC)                       \
+    do {                                                  \
+        if (gg.qs == 0) QK_GEMV_LAUNCH_Q(SS, MXX, CC, 0); \
+        else if (gg.qs == 1) QK_GEMV_LAUNCH_Q(SS, MXX, CC, 1); \
+        else QK_GEMV_LAUNCH_Q(SS, MXX, CC, 2);            \
+    } while (0)
+        if (M == 1) QK_GEMV_LAUNCH(8, 1, 64);
+        else if (M == 2) QK_GEMV_LAUNCH(4, 2, 64);
+        else QK_GEMV_LAUNCH(4, 4, 64);
+#undef QK_GEMV_LAUNCH
+#undef QK_GEMV_LAUNCH_Q
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_gemv(const void* x, int32_t M, const MatArgs& w, void* y, hipStream_t s, const char** variant) {
-    GemvArgs a;
-    a.x = reinterpret_cast<const uint16_t*>(x);
-    a.y = reinterpret_cast<uint16_t*>(y);
-    a.w = w.w;
-    a.N = w.N;
-    a.K = w.K;
-    a.M = M;
-    const bool fast = (w.K % kStep) == 0 && (w.K % w.w.blocksize) == 0 &&
-                      (reinterpret_cast<uintptr_t>(x) % 16) == 0 && (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0;
-    if (!fast) {
-        *variant = "generic (per-element dequantization, one wave per row)";
-        hipLaunchKernelGGL(gemv_generic_kernel, dim3((unsigned)((w.N + 3) / 4)), dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
-    *variant = "mfma 16x16x32 bf16, 16 rows per workgroup, codes staged through LDS in 512-k chunks, 4 or 8 waves split-K";
-    const unsigned grid = (unsigned)((a.N + 15) / 16);
-    // 4 waves (80 KB of LDS, two workgroups per CU, so one's loads overlap the other's
-    // compute) when there are at least two tiles per CU and K fits 8 chunks; 8 waves
-    // (one workgroup per CU, more loads in flight per tile) otherwise
-    const bool four = grid >= 2u * (unsigned)device_cu_count() && w.K <= 8 * kChunkK;
-    if (four) {
-        if (w.w.nested) hipLaunchKernelGGL((gemv_lds_kernel<true, 4>), dim3(grid), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((gemv_lds_kernel<false, 4>), dim3(grid), dim3(256), 0, s, a);
-    } else {
-        if (w.w.nested) hipLaunchKernelGGL((gemv_lds_kernel<true, 8>), dim3(grid), dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((gemv_lds_kernel<false, 8>), dim3(grid), dim3(512), 0, s, a);
-    }
-    return hipGetLastError();
+    const GemvItem it{x, y, w};
+    return launch_gemv_group(&it, 1, M, s, variant);
 }
 
 }  // namespace qk

@@ -120,6 +120,16 @@ struct MatArgs {
 };
 hipError_t launch_gemv(const void* x, int32_t M, const MatArgs& w, void* y, hipStream_t s,
                        const char** variant);
+// Several weights with their own x and y (the same M) in as few launches as their
+// code tables, block sizes and nesting allow (at most kMaxGemvTasks weights each).
+constexpr int kMaxGemvTasks = 16;
+struct GemvItem {
+    const void* x;
+    void* y;
+    MatArgs w;
+};
+hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hipStream_t s,
+                             const char** variant);
 size_t gemm_workspace_bytes(int64_t M, int32_t r);
 hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B,
                        int32_t r, float lora_scale, void* Y, void* workspace, hipStream_t s,

@@ -228,11 +228,33 @@ qk_status qk_dequantize(const qk_quant_state* st, void* out, int32_t out_dtype, 
  *   x:  device, [M, K] bf16 row-major (K = st->cols), 16-byte aligned.
  *   M:  1..16.
  *   st: host pointer to a valid descriptor of W [N, K] (N = st->rows).
- *   y:  device, [M, N] bf16 row-major, written.
+ *   y:  device, [M, N] bf16 row-major, written; 2-byte aligned.
  *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG (M outside 1..16, null or
  *   misaligned pointers), QK_ERR_HIP.
  */
 qk_status qk_gemv_nf4(const void* x, int32_t M, const qk_quant_state* st, void* y, void* stream);
+
+/*
+ * qk_gemv_nf4_grouped — device.  qk_gemv_nf4 of several weights, each with its own
+ * x and y and the same M, in as few launches as possible: one per run of up to 16
+ * weights that share the level table, block size and nesting (a decode step's
+ * q / k / v, or gate / up, or a whole layer when their inputs are ready together).
+ * Each y is bit-for-bit what qk_gemv_nf4 of that weight alone writes.
+ *   tasks: host array of ntasks entries
+ *     x:  device, [M, K] bf16 row-major (K = st->cols), 16-byte aligned;
+ *     st: host pointer to a valid descriptor of W [N, K];
+ *     y:  device, [M, N] bf16 row-major, written; 2-byte aligned.
+ *   ntasks: 1..256.   M: 1..16.
+ *   No y may overlap another task's y or any task's x (else QK_ERR_INVALID_ARG).
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_HIP.
+ */
+typedef struct qk_gemv_task {
+    const void* x;
+    const qk_quant_state* st;
+    void* y;
+} qk_gemv_task;
+
+qk_status qk_gemv_nf4_grouped(const qk_gemv_task* tasks, int32_t ntasks, int32_t M, void* stream);
 
 /*
  * qk_gemm_nf4_workspace_size — host.  Bytes of device workspace qk_gemm_nf4

@@ -329,3 +329,37 @@ def test_binding_checks_gemv_gemm_operands(L):
     # well-formed host tensors get as far as the device check
     with pytest.raises(ValueError, match="HIP device"):
         qk.qk_gemm_nf4(x, st, A, B, 2.0)
+
+
+def test_gemv_grouped_argument_errors(L):
+    st = _state()                        # W [4, 64]
+    T = qk.GemvTask
+
+    def arr(*entries):
+        a = (T * len(entries))()
+        for i, (x, s, y) in enumerate(entries):
+            a[i].x = x
+            a[i].st = None if s is None else ctypes.pointer(s)
+            a[i].y = y
+        return a
+
+    X0, Y0, Y1 = 0x100000, 0x200000, 0x300000
+    ok = arr((X0, st, Y0))
+    call = L.qk_gemv_nf4_grouped
+    assert call(None, 1, 1, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 0, 1, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 257, 1, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 1, 0, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 1, 17, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((X0, None, Y0)), 1, 1, None) == qk.QK_ERR_INVALID_ARG
+    bad = _state()
+    bad.version = 7
+    assert call(arr((X0, st, Y0), (X0, bad, Y1)), 2, 1, None) == qk.QK_ERR_BAD_STATE
+    assert call(arr((None, st, Y0)), 1, 1, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((X0 + 8, st, Y0)), 1, 1, None) == qk.QK_ERR_INVALID_ARG      # x not 16-byte aligned
+    assert call(arr((X0, st, Y0 + 1)), 1, 1, None) == qk.QK_ERR_INVALID_ARG      # y not 2-byte aligned
+    # y [M, 4] bf16 = 8 bytes per row: overlapping outputs, an output over an input
+    assert call(arr((X0, st, Y0), (X0, st, Y0 + 6)), 2, 1, None) == qk.QK_ERR_INVALID_ARG
+    assert "overlaps y" in qk.qk_last_error()
+    assert call(arr((X0, st, Y0), (X0, st, X0 + 64)), 2, 1, None) == qk.QK_ERR_INVALID_ARG
+    assert "overlaps x" in qk.qk_last_error()

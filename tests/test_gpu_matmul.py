@@ -196,7 +196,7 @@ def test_gemm_qlora_prefill_full_size_sampled_rows(N, K):
     check_close(bf16_bits_to_f32(Y[rows]), ref, f"gemm prefill N={N}")
 
 
-@pytest.mark.parametrize("B", [64, 256])
+@pytest.mark.parametrize("B", [64, 128, 256])
 @pytest.mark.parametrize("kind", [ocb.NF4, ocb.FP4])
 def test_gemm_edge_generic_path(B, kind):
     say(f"case: gemm edge 512x3000x4099 B={B} kind={kind}")
