@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "QKError", "QuantState", "QuantizedWeight", "NF4", "FP4", "CUSTOM", "lib",
     "qk_make_codebook", "qk_quantize_blockwise", "qk_double_quant_workspace_size", "qk_double_quant",
-    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemv_nf4_grouped", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_last_error", "qk_version",
+    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemv_nf4_grouped", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_gemm_nf4_noalloc", "qk_last_error", "qk_version",
     "qk_backend_info", "quantize",
 ]
 
@@ -106,6 +106,7 @@ def lib():
         "qk_gemv_nf4_grouped": [ctypes.POINTER(GemvTask), i32, i32, vp],
         "qk_gemm_nf4_workspace_size": [i64, i32, ctypes.POINTER(ctypes.c_size_t)],
         "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp, ctypes.c_size_t, vp],
+        "qk_gemm_nf4_noalloc": [vp, i64, st_p, vp, vp, i32, f32, vp, vp],
         "qk_lora_merge": [st_p, vp, vp, i32, f32, vp, vp],
         "qk_qlora_backward_workspace_size": [i64, st_p, i32, ctypes.POINTER(ctypes.c_size_t)],
         "qk_qlora_backward": [vp, i64, st_p, vp, vp, vp, i32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp],
@@ -467,6 +468,32 @@ def qk_gemm_nf4(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: 
         _check(lib().qk_gemm_nf4(_ptr(X2), M, ctypes.byref(state), _ptr(A), _ptr(B), int(r), float(lora_scale),
                                  _ptr(Y), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                  ctypes.c_void_p(_stream(X))))
+    return Y
+
+
+def qk_gemm_nf4_noalloc(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: float = 0.0,
+                        Y=None) -> torch.Tensor:
+    """qk_gemm_nf4 without a workspace: the LoRA partials use the library's static
+    device scratch (M * 16 * ceil(r / 16) <= 262144).  Calls that overlap on one
+    device race."""
+    if (A is None) != (B is None):
+        raise ValueError("give both LoRA A and B, or neither")
+    for name, t in (("X", X), ("A", A), ("B", B)):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16, got {t.dtype}")
+    X2 = _rows_of(X, state.cols, "X")
+    M = X2.shape[0]
+    r = 0 if A is None else A.shape[-1]
+    if A is not None and (tuple(A.shape) != (state.cols, r) or tuple(B.shape) != (r, state.rows)):
+        raise ValueError(f"shapes A {tuple(A.shape)}, B {tuple(B.shape)} do not match W [{state.rows}, {state.cols}]")
+    if Y is not None:
+        _check_out(Y, (M, state.rows), torch.bfloat16, "Y")
+    _require_cuda(X, A, B, Y)
+    if Y is None:
+        Y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=X.device)
+    with _on(X.device):
+        _check(lib().qk_gemm_nf4_noalloc(_ptr(X2), M, ctypes.byref(state), _ptr(A), _ptr(B), int(r),
+                                         float(lora_scale), _ptr(Y), ctypes.c_void_p(_stream(X))))
     return Y
 
 

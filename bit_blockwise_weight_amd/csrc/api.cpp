@@ -482,6 +482,31 @@ qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const 
                     "qk_gemm_nf4");
 }
 
+qk_status qk_gemm_nf4_noalloc(const void* X, int64_t M, const qk_quant_state* st, const void* A, const void* B,
+                              int32_t r, float lora_scale, void* Y, void* stream) {
+    const qk_status v = check_gemm_args("qk_gemm_nf4_noalloc", X, M, st, A, B, r, lora_scale, Y);
+    if (v != QK_OK) return v;
+    const size_t need = qk::gemm_workspace_bytes(M, A ? r : 0);
+    const size_t cap = qk::gemm_noalloc_scratch_bytes();
+    if (need > cap)
+        return fail(QK_ERR_WORKSPACE,
+                    "qk_gemm_nf4_noalloc: the LoRA partials of M = %lld, r = %d need %zu bytes; the static scratch "
+                    "holds %zu (M * 16 * ceil(r / 16) <= %zu); use qk_gemm_nf4 with a workspace",
+                    (long long)M, r, need, cap, cap / (8 * sizeof(float)));
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    void* scratch = nullptr;
+    if (need > 0) {
+        const hipError_t e = qk::gemm_noalloc_scratch(&scratch);
+        if (e != hipSuccess)
+            return fail(QK_ERR_HIP, "qk_gemm_nf4_noalloc: address of the static scratch: %s", hipGetErrorString(e));
+    }
+    qk::MatArgs w{deq_args(st), st->rows, st->cols};
+    return launched(qk::launch_gemm(X, M, w, A, B, A ? r : 0, lora_scale, Y, scratch,
+                                    reinterpret_cast<hipStream_t>(stream), &g_gemm_variant),
+                    "qk_gemm_nf4_noalloc");
+}
+
 const char* qk_last_error(void) { return g_last_error.c_str(); }
 
 const char* qk_version(void) { return "qk 0.1.0 gfx950"; }

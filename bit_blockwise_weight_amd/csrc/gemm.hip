@@ -25,6 +25,7 @@
 // A generic variant (template flag) loads X element by element and dequantizes
 // W with flat indexing, for K that is not a multiple of 64 or of the block size
 // (blocks straddling rows) and unaligned X.
+#include <mutex>
 #include <type_traits>
 
 #include "qk_internal.h"
@@ -934,6 +935,42 @@ hipError_t launch_lora_xa_sum(const void* X, int64_t M, int64_t K, const void* A
     const int64_t n = M * 16 * r16;
     hipLaunchKernelGGL(lora_split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T_splits, n, Ts);
     return hipGetLastError();
+}
+
+// Scratch of qk_gemm_nf4_noalloc: the LoRA pre-pass partials live in this
+// file-scope device array instead of a caller workspace.  Each device holds its
+// own copy (at its own address) until the process ends; every call on a device
+// shares it, so calls that overlap on one device race.  The pre-pass writes every
+// partial it leaves for the GEMM, so nothing has to be cleared between calls.
+// Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): it passes the device address that hipGetSymbolAddress
+// returns, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+size_t gemm_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t gemm_noalloc_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 size_t gemm_workspace_bytes(int64_t M, int32_t r) {

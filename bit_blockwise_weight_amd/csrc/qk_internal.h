@@ -131,6 +131,11 @@ struct GemvItem {
 hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hipStream_t s,
                              const char** variant);
 size_t gemm_workspace_bytes(int64_t M, int32_t r);
+// The static device scratch of the no-allocation GEMM: its size, and its address
+// on the current device (looked up with hipGetSymbolAddress on the first call per
+// device, then cached).
+size_t gemm_noalloc_scratch_bytes();
+hipError_t gemm_noalloc_scratch(void** ptr);
 hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B,
                        int32_t r, float lora_scale, void* Y, void* workspace, hipStream_t s,
                        const char** variant);

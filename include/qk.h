@@ -288,6 +288,27 @@ qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const 
                       size_t workspace_bytes, void* stream);
 
 /*
+ * qk_gemm_nf4_noalloc — device.  qk_gemm_nf4 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and the same result, bit for bit, as
+ * qk_gemm_nf4 with a workspace, but the LoRA partials live in a static device
+ * array of the library (8 MiB per device, held until the process ends), so the
+ * call takes no workspace and allocates nothing.
+ *   X, M, st, A, B, r, lora_scale, Y: as for qk_gemm_nf4.
+ *   Limit: with an adapter, M * 16 * ceil(r / 16) <= 262144 (for instance
+ *   M <= 16384 at r <= 16, M <= 4096 at r <= 64); larger calls are refused
+ *   with QK_ERR_WORKSPACE and launch nothing.
+ *   Every call on one device shares its array: calls that overlap on one device
+ *   (on different streams, or from different threads) race and give undefined
+ *   results; calls in one stream order are safe.  The first call on a device
+ *   looks up the array's address (hipGetSymbolAddress), so make it once before
+ *   graph capture.
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_WORKSPACE, QK_ERR_HIP.
+ */
+qk_status qk_gemm_nf4_noalloc(const void* X, int64_t M, const qk_quant_state* st, const void* A,
+                              const void* B, int32_t r, float lora_scale, void* Y, void* stream);
+
+/*
  * qk_lora_merge — device.  Merges a LoRA adapter into the dequantized weight,
  * [DEQ] section 8 (merge: dequantize the 4-bit weight to BF16, add the LoRA
  * product, W_new is BF16; requantize it with qk_quantize_blockwise when a

@@ -331,6 +331,26 @@ def test_binding_checks_gemv_gemm_operands(L):
         qk.qk_gemm_nf4(x, st, A, B, 2.0)
 
 
+def test_gemm_noalloc_argument_errors(L):
+    """qk_gemm_nf4_noalloc validates like qk_gemm_nf4 and refuses LoRA partials
+    beyond its static scratch (M * 16 * ceil(r / 16) <= 262144) before any device
+    work."""
+    st = _state()
+    call = L.qk_gemm_nf4_noalloc
+    assert call(None, 8, ctypes.byref(st), None, None, 0, 0.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert call(FAKE, 0, ctypes.byref(st), None, None, 0, 0.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert call(FAKE, 8, ctypes.byref(st), FAKE, None, 16, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert call(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 65, 2.0, FAKE, None) == qk.QK_ERR_INVALID_ARG
+    assert call(FAKE, 8, ctypes.byref(st), FAKE, FAKE, 16, float("nan"), FAKE, None) == qk.QK_ERR_INVALID_ARG
+    bad = _state()
+    bad.magic = 0
+    assert call(FAKE, 8, ctypes.byref(bad), None, None, 0, 0.0, FAKE, None) == qk.QK_ERR_BAD_STATE
+    assert call(FAKE, 16385, ctypes.byref(st), FAKE, FAKE, 16, 2.0, FAKE, None) == qk.QK_ERR_WORKSPACE
+    assert "static scratch" in qk.qk_last_error()
+    assert call(FAKE, 4097, ctypes.byref(st), FAKE, FAKE, 64, 2.0, FAKE, None) == qk.QK_ERR_WORKSPACE
+    assert call(FAKE, 8193, ctypes.byref(st), FAKE, FAKE, 17, 2.0, FAKE, None) == qk.QK_ERR_WORKSPACE
+
+
 def test_gemv_grouped_argument_errors(L):
     st = _state()                        # W [4, 64]
     T = qk.GemvTask
