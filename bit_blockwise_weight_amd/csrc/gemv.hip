@@ -92,15 +92,17 @@ struct GemvGroup {
     GemvTask t[kMaxGemvTasks];
     float levels[16];
     int32_t ntasks;
-    int32_t nitems;          // tiles of 16 rows over all slices (<= kOutSlots * grid)
+    int32_t nitems;          // tiles of 16 rows over all slices (<= out_slots * grid)
     int32_t M;
     int32_t qs;              // log2(block size) - 6
 };
 
 constexpr int kChunkK = 512;                   // k per job (8 blocks of 64)
 constexpr int kChunkBlocks = kChunkK / 64;
-constexpr int kOutSlots = 32;                  // tiles per workgroup whose outputs LDS holds until the end
-constexpr int kXPitch = 80;                    // 16-byte units per staged x row (64 used)
+// tiles per workgroup whose partial sums LDS holds until the end of the kernel
+__host__ __device__ constexpr int out_slots(int S, int MX) { return S * MX <= 8 ? 32 : 16; }
+// 16-byte units per staged x row (64 used, the rest pads the rotation of rows m > 0)
+__host__ __device__ constexpr int x_pitch(int MX) { return MX == 1 ? 64 : 80; }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
@@ -120,56 +122,66 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // One job's registers: the scale inputs (the codes and x rows of a job go to LDS directly).
 struct JobRegs {
-    u32x3_t q;                   // nested: 12 bytes from the aligned start of the job's q8 run
+    u32x3_t q;                   // nested: q8 bytes of the job (aligned: the first 8; else 12 from qf & ~3)
     u32x4_t f0, f1;              // plain: absmax of the job's quantization blocks (up to 8)
-    u32x2_t d;                   // nested: dq scales of the first block's dq block and the next
-    uint32_t qinfo;              // nested: (qf & 3) | (blocks left in the first dq block) << 2
+    u32x2_t d;                   // nested: dq scale of the job (aligned), or of its first dq block and the next
+    uint32_t qinfo;              // nested, not aligned: (qf & 3) | (blocks left in the first dq block) << 2
 };
 
 // S waves per workgroup, MX rows of x staged per job (M <= MX), C copies of the code table,
-// QS = log2(block size) - 6 (a job's 8 blocks of 64 fall in 8 >> QS quantization blocks).
+// QS = log2(block size) - 6 (a job's 8 blocks of 64 fall in 8 >> QS quantization blocks),
+// kAligned: every row length of the launch is a multiple of 512, so a job's quantization
+// blocks are one aligned run inside one double-quantization block.
 //
 // A job is 16 rows x 512 k: its codes (4 KB) and x rows (M x 1 KB) are copied from memory
 // straight into one of the wave's two LDS slots by buffer loads with the LDS bit, 16 bytes
 // per lane and instruction (so 4 + M vector memory instructions carry a job's bulk, with no
 // registers and no LDS writes of the wave's own); the scales come with two more.  The two
 // slots are separate LDS objects, so the wait before reading one leaves the other's copies
-// in flight.
-template <int S, int MX, int C, bool kNested, int QS>
+// in flight.  The lane offsets of a tile's rows are computed once per tile; the job's chunk
+// enters the loads as their scalar offset where the chunk cannot run past the row.
+template <int S, int MX, int C, bool kNested, int QS, bool kAligned>
 __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     constexpr int kR = MX < 4 ? MX : 4;        // output registers of a lane that can hold a row m < M
+    constexpr int kXPitch = x_pitch(MX);
     constexpr int kSlotX = MX * kXPitch;       // 16-byte units of a staged x slot
-    __shared__ __attribute__((aligned(16))) uint32_t tab[256 * C];            // byte -> bf16 pair, C copies
+    constexpr int kSlots = out_slots(S, MX);
+    constexpr int kJobQ = kChunkBlocks >> QS;  // quantization blocks per job
+    // vector memory instructions per job: the scales (two, or one absmax load when a job
+    // has at most 4 blocks), the 4 code copies and the MX x copies
+    constexpr int kLoads = (kNested || QS == 0 ? 2 : 1) + 4 + MX;
+    // byte -> bf16 pair, C copies; the highest alignment puts it at LDS offset 0, so the
+    // table base fits the read instructions' immediate offset (no add per lookup)
+    __shared__ __attribute__((aligned(4096))) uint32_t tab[256 * C];
     __shared__ __attribute__((aligned(1024))) uint4 cb0[S * 256];             // codes, slot 0 (4 KB per wave)
     __shared__ __attribute__((aligned(1024))) uint4 cb1[S * 256];             // codes, slot 1
     __shared__ __attribute__((aligned(16))) uint4 xs0[S * kSlotX];            // x rows, slot 0
     __shared__ __attribute__((aligned(16))) uint4 xs1[S * kSlotX];            // x rows, slot 1
-    __shared__ __attribute__((aligned(16))) float red[2][S][kR][64];          // per-wave partial tiles
-    __shared__ __attribute__((aligned(16))) uint16_t outb[kOutSlots][16 * MX]; // finished outputs, bf16
+    __shared__ __attribute__((aligned(16))) float part[kSlots][S][kR][16];    // each wave's partial tiles
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;                   // weight row of the tile (and x row m of the A operand)
     const int h = lane >> 4;                   // 16-weight group of a 64-k block
     const int M = g.M;
-    constexpr int qs = QS;
     const int32_t G = (int32_t)gridDim.x;
     const int32_t wg = (int32_t)blockIdx.x;
 
     // This workgroup takes the tiles wg, wg + G, ...; in each, wave w takes the jobs
     // (chunks of 512 k) w, w + S, ...  Every wave of the workgroup sees the same tiles and
-    // job counts, so the tile ends are uniform in the workgroup.  The load cursor copies
-    // its slice's fields when it moves to another slice; the compute cursor only needs
-    // the job count, the row length and the mean (a scalar load when it changes slice).
+    // job counts.  The load cursor holds its slice's buffers and, for its tile, this lane's
+    // offsets of the code rows and of its row's first scale; the compute cursor only needs
+    // the job count and the mean (a scalar load when it changes slice).
     struct LoadCur {
         int32_t item, task, j, jobs, nchunk, K, item0, code_bytes, sc_bytes, dq_bytes;
-        int64_t N, qbase;
-        const uint16_t* x;
-        const uint8_t* codes;
+        const void* codes;
+        const void* x;
         const void* sc;
-        const float* dq_scale;
+        const void* dq_scale;
+        uint32_t crow[4];          // code offset of row 4 i + lane / 16 and this lane's piece
+        uint32_t qrow;             // scale index of the first block of row n
     };
     struct CompCur {
-        int32_t item, task, j, jobs, nblk;
+        int32_t item, task, j, jobs;
         float mu;
     };
     auto task_from = [&](int32_t item, int32_t t) {
@@ -186,17 +198,29 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
         c.code_bytes = T.code_bytes;
         c.sc_bytes = T.sc_bytes;
         c.dq_bytes = T.dq_bytes;
-        c.N = T.N;
-        c.qbase = T.qbase;
-        c.x = T.x;
         c.codes = T.codes;
+        c.x = T.x;
         c.sc = T.sc;
         c.dq_scale = T.dq_scale;
+    };
+    // rows past the slice's end are clamped to its last row (valid memory, never stored)
+    auto enter_tile = [&](LoadCur& c) {
+        const GemvTask& T = g.t[c.task];
+        const int32_t N = (int32_t)T.N;
+        const int32_t n0 = (c.item - c.item0) * 16;
+        const uint32_t row_bytes = (uint32_t)(c.K / 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const int32_t gr = n0 + r < N ? n0 + r : N - 1;
+            c.crow[i] = (uint32_t)gr * row_bytes + 16u * (uint32_t)((lane & 15) ^ r);
+        }
+        const int32_t rowc = n0 + n < N ? n0 + n : N - 1;
+        c.qrow = (uint32_t)T.qbase + (uint32_t)rowc * (uint32_t)(c.K >> (QS + 6));
     };
     auto set_comp_task = [&](CompCur& c, int32_t t) {
         c.task = t;
         c.jobs = g.t[t].jobs;
-        c.nblk = g.t[t].K / 64;
         // a scalar load (constant address space: the mean does not change during the
         // kernel): no vector memory operation under the task-switch condition
         c.mu = kNested ? *(const __attribute__((address_space(4))) float*)(uintptr_t)g.t[t].dq_mean : 0.0f;
@@ -205,8 +229,11 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
         if (++c.j == c.jobs) {
             c.j = 0;
             c.item += G;
-            if (c.item < g.nitems && c.task + 1 < g.ntasks && c.item >= g.t[c.task + 1].item0)
-                set_load_task(c, task_from(c.item, c.task + 1));
+            if (c.item < g.nitems) {
+                if (c.task + 1 < g.ntasks && c.item >= g.t[c.task + 1].item0)
+                    set_load_task(c, task_from(c.item, c.task + 1));
+                enter_tile(c);
+            }
         }
     };
     auto advance_comp = [&](CompCur& c) {
@@ -221,6 +248,7 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     lc.item = wg;
     lc.j = 0;
     set_load_task(lc, task_from(wg, 0));
+    enter_tile(lc);
     CompCur cc;
     cc.item = wg;
     cc.j = 0;
@@ -228,56 +256,82 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
 
     auto load = [&](const LoadCur& c, JobRegs& jr, auto slot) {
         constexpr bool kB = decltype(slot)::value;
-        // a job past the end (after the last one) clamps its rows to the last row of its
-        // slice: it reads valid memory, mostly from the cache, and is never used
-        const int64_t N = c.N;
-        const int64_t K = c.K;
-        const int64_t row_bytes = K / 2;
-        const int64_t n0 = (int64_t)(c.item - c.item0) * 16;
-        const int32_t chunk = c.j * S + wave;
-        const int32_t ch = chunk < c.nchunk ? chunk : c.nchunk - 1;
-        // codes: load i, lane L fetches piece (L % 16) ^ r of row r = 4 i + L / 16 (rows past
-        // N clamped to the last; pieces past the end of a row, in a partial chunk, clamped
-        // to its last 16 bytes and never used), which lands in slot unit 64 i + L
-        const __amdgpu_buffer_rsrc_t cr = buf_rsrc(c.codes, c.code_bytes);
+        // a job past the end of the work (after the last one) reloads its last tile's rows
+        // (valid memory, mostly from the cache); it is never stored
+        const __amdgpu_buffer_rsrc_t lcr = buf_rsrc(c.codes, c.code_bytes);
+        const __amdgpu_buffer_rsrc_t lxr = buf_rsrc(c.x, M * c.K * 2);
+        const __amdgpu_buffer_rsrc_t lsr = buf_rsrc(c.sc, c.sc_bytes);
+        const __amdgpu_buffer_rsrc_t ldr = buf_rsrc(c.dq_scale, c.dq_bytes);
+        // (the builtins below take plainly typed locals: a member of the cursor, whose type
+        // depends on the template, makes host compilation drop the kernel's launch stub)
+        const int32_t K = c.K;
+        const uint32_t qrow = c.qrow;
+        const uint32_t crow[4] = {c.crow[0], c.crow[1], c.crow[2], c.crow[3]};
+        const int32_t ch = c.j * S + wave;
+        const bool live = ch < c.nchunk;                 // an idle wave's chunk: x reads zero
+        const int32_t chc = live ? ch : c.nchunk - 1;
+        // the job's quantization blocks of row n are consecutive from qf on
+        const uint32_t qf = qrow + (uint32_t)(chc * kJobQ);
+        if constexpr (kNested) {
+            if constexpr (kAligned) {
+                // the job's kJobQ q8 bytes start at a multiple of kJobQ (8, 4 or 2)
+                if constexpr (QS == 0)
+                    jr.q.xy = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(lsr, qrow, (uint32_t)(chc * kJobQ), 0));
+                else
+                    jr.q.x = __builtin_amdgcn_raw_buffer_load_b32(lsr, qf & ~3u, 0, 0);
+                if constexpr (QS == 2) jr.qinfo = qf & 3u;
+                jr.d.x = __builtin_amdgcn_raw_buffer_load_b32(ldr, (qf / QK_DQ_BLOCK) * 4u, 0, 0);
+            } else {
+                jr.q = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(lsr, qf & ~3u, 0, 0));
+                jr.d = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ldr, (qf / QK_DQ_BLOCK) * 4u, 0, 0));
+                jr.qinfo = (qf & 3u) | ((QK_DQ_BLOCK - qf % QK_DQ_BLOCK) << 2);
+            }
+        } else {
+            if constexpr (kAligned) {
+                jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, (uint32_t)(chc * kJobQ * 4), 0));
+                if constexpr (QS == 0)
+                    jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, (uint32_t)(chc * kJobQ * 4 + 16), 0));
+            } else {
+                jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qf * 4u, 0, 0));
+                if constexpr (QS == 0)
+                    jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qf * 4u + 16u, 0, 0));
+            }
+        }
         __attribute__((address_space(3))) char* cdst =
             (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? cb1 : cb0) + wave * 4096;
+        // codes: load i, lane L fetches piece (L % 16) ^ r of row r = 4 i + L / 16, which lands
+        // in slot unit 64 i + L
+        if constexpr (kAligned) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * i + (lane >> 4);
-            const int64_t gr = n0 + r < N ? n0 + r : N - 1;
-            int64_t off = (int64_t)ch * (kChunkK / 2) + 16 * ((lane & 15) ^ r);
-            off = off + 16 <= row_bytes ? off : row_bytes - 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr_t)(cdst + i * 1024), 16,
-                                                     (uint32_t)(gr * row_bytes + off), 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(lcr, (lds_ptr_t)(cdst + i * 1024), 16, crow[i],
+                                                         (uint32_t)chc * (kChunkK / 2), 0, 0);
+        } else {
+            // pieces past the end of a row, in a partial chunk, are clamped to the row's last
+            // 16 bytes (their x is zero); the offset stays in the range-checked vector part
+            const uint32_t row_bytes = (uint32_t)(K / 2);
+            const uint32_t cofs = (uint32_t)chc * (kChunkK / 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                const uint32_t piece = 16u * (uint32_t)((lane & 15) ^ r);
+                const uint32_t within = cofs + piece + 16u <= row_bytes ? cofs : row_bytes - 16u - piece;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(lcr, (lds_ptr_t)(cdst + i * 1024), 16, crow[i] + within,
+                                                         0, 0, 0);
+            }
         }
         // x rows m < MX of the job's k, 16 bytes per lane: unit L of row m lands in slot unit
-        // m * kXPitch + xrot(m) + L (rows past M, and k past the row in a partial chunk, read
-        // zero or the next row: never used)
-        const __amdgpu_buffer_rsrc_t xr = buf_rsrc(c.x, (int32_t)(M * K * 2));
+        // m * kXPitch + xrot(m) + L.  An idle wave's chunk and the k past the row in a partial
+        // chunk take an offset beyond the buffer and read zero, so those products vanish
+        // whatever codes and scales the job holds; rows past M are never stored.
         __attribute__((address_space(3))) char* xdst =
             (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? xs1 : xs0) + wave * (kSlotX * 16);
-        const uint32_t xo = (uint32_t)(((int64_t)ch * kChunkK + 8 * lane) * 2);
+        const bool xin = live && ch * kChunkK + 8 * lane < K;
+        const uint32_t xo = xin ? (uint32_t)(ch * (kChunkK * 2) + 16 * lane) : 0x80000000u;
 #pragma unroll
         for (int m = 0; m < MX; ++m)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xdst + (m * kXPitch + xrot(m)) * 16), 16,
-                                                     xo + (uint32_t)(m * K * 2), 0, 0, 0);
-        // the job's quantization blocks of row n are consecutive, from qf on (a partial
-        // chunk's blocks past the row are read from the next row or as zero, never used)
-        const int64_t rowc = n0 + n < N ? n0 + n : N - 1;
-        const int64_t qf = c.qbase + ((rowc * K) >> (qs + 6)) + ((int64_t)(ch * kChunkBlocks) >> qs);
-        const __amdgpu_buffer_rsrc_t sr = buf_rsrc(c.sc, c.sc_bytes);
-        if constexpr (kNested) {
-            jr.q = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(sr, (uint32_t)(qf & ~(int64_t)3), 0, 0));
-            const __amdgpu_buffer_rsrc_t dr = buf_rsrc(c.dq_scale, c.dq_bytes);
-            jr.d = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                   dr, (uint32_t)((qf / QK_DQ_BLOCK) * 4), 0, 0));
-            jr.qinfo = (uint32_t)(qf & 3) | ((uint32_t)(QK_DQ_BLOCK - qf % QK_DQ_BLOCK) << 2);
-        } else {
-            jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)(qf * 4), 0, 0));
-            if constexpr (QS == 0)
-                jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)(qf * 4 + 16), 0, 0));
-        }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(lxr, (lds_ptr_t)(xdst + (m * kXPitch + xrot(m)) * 16), 16,
+                                                     xo, (uint32_t)(m * K * 2), 0, 0);
     };
 
     floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -291,22 +345,38 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
         constexpr bool kB = decltype(slot)::value;
         const char* mb = reinterpret_cast<const char*>(kB ? cb1 : cb0) + wave * 4096;
         const u32x4_t* xf = reinterpret_cast<const u32x4_t*>(kB ? xs1 : xs0) + wave * kSlotX + xunit;
-        // blocks past the row's end, and every block of a job past the end, add nothing
-        const int32_t nblk = c.item < g.nitems ? c.nblk : 0;
-        const int32_t b0 = (c.j * S + wave) * kChunkBlocks;
-        uint32_t qlo = 0, qhi = 0, split = 0;
+        uint32_t qlo = 0, qhi = 0, split = 8;
+        float dsc0 = 0.0f, dsc1 = 0.0f;
         if constexpr (kNested) {
-            const uint32_t sh = jr.qinfo & 3u;
-            qlo = __builtin_amdgcn_alignbyte(jr.q[1], jr.q[0], sh);
-            qhi = __builtin_amdgcn_alignbyte(jr.q[2], jr.q[1], sh);
-            split = jr.qinfo >> 2;
+            if constexpr (kAligned) {
+                if constexpr (QS == 2) {
+                    qlo = jr.q.x >> (8u * jr.qinfo);     // the job's 2 bytes start at byte qf & 3
+                } else {
+                    qlo = jr.q.x;
+                    qhi = jr.q.y;
+                }
+                const uint32_t d0 = jr.d[0];
+                dsc0 = dsc1 = __builtin_bit_cast(float, d0);
+            } else {
+                const uint32_t sh = jr.qinfo & 3u;
+                qlo = __builtin_amdgcn_alignbyte(jr.q[1], jr.q[0], sh);
+                qhi = __builtin_amdgcn_alignbyte(jr.q[2], jr.q[1], sh);
+                split = jr.qinfo >> 2;
+                // (the elements go through plain locals: a bit cast of a vector element
+                // lvalue reads the vector's first element)
+                const uint32_t d0 = jr.d[0], d1 = jr.d[1];
+                dsc0 = __builtin_bit_cast(float, d0);
+                dsc1 = __builtin_bit_cast(float, d1);
+            }
         }
 #pragma unroll
         for (int bb = 0; bb < kChunkBlocks; ++bb) {
             const int piece = 2 * bb + (h >> 1);
-            const uint2 cw = *reinterpret_cast<const uint2*>(mb + (16 * n + (piece ^ n)) * 16 + 8 * (h & 1));
-            const uint32_t cws[2] = {cw.x, cw.y};
-            floatx4_t part = {0.0f, 0.0f, 0.0f, 0.0f};
+            // a plain vector load (a copy of a HIP vector struct becomes a memcpy that
+            // loses the LDS object's identity, and then every copy in flight is waited for)
+            const u32x2_t cw = *reinterpret_cast<const u32x2_t*>(mb + (16 * n + (piece ^ n)) * 16 + 8 * (h & 1));
+            const uint32_t cws[2] = {cw[0], cw[1]};
+            floatx4_t pp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 uint32_t wv[4];
@@ -317,60 +387,37 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
                     wv[k4] = *reinterpret_cast<const uint32_t*>(tabb + addr);
                 }
                 const u32x4_t xv = xf[8 * bb + t];
-                part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
-                                                               __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3])),
-                                                               part, 0, 0, 0);
+                pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
+                                                             __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3])),
+                                                             pp, 0, 0, 0);
             }
-            // the block's scale: quantization block bb >> qs of the job
-            const uint32_t qq = (uint32_t)bb >> qs;
+            // the block's scale: quantization block bb >> QS of the job
+            const uint32_t qq = (uint32_t)bb >> QS;
             float a;
             if constexpr (kNested) {
                 const uint32_t word = qq < 4 ? qlo : qhi;
                 const int32_t q8 = __builtin_amdgcn_sbfe((int32_t)word, 8 * (qq & 3), 8);
-                const float dsc = __builtin_bit_cast(float, qq < split ? jr.d[0] : jr.d[1]);
+                const float dsc = qq < split ? dsc0 : dsc1;
                 a = __fadd_rn(__fmul_rn((float)q8, dsc), c.mu);
             } else {
                 const uint32_t fsel[8] = {jr.f0[0], jr.f0[1], jr.f0[2], jr.f0[3], jr.f1[0], jr.f1[1], jr.f1[2], jr.f1[3]};
                 a = __builtin_bit_cast(float, fsel[qq]);
             }
-            // a block past the row's end weighs 0 (its products are finite: the codes, x and
-            // scales it read are valid data or zero); a select of the weight, not of the
-            // accumulation, keeps the block loop free of branches
-            const float aw = b0 + bb < nblk ? a : 0.0f;
 #pragma unroll
-            for (int r = 0; r < kR; ++r) acc[r] = __builtin_fmaf(part[r], aw, acc[r]);
+            for (int r = 0; r < kR; ++r) acc[r] = __builtin_fmaf(pp[r], a, acc[r]);
         }
-    };
-
-    // bare barrier: __syncthreads() would add a fence that waits for the loads in flight
-    auto bare_barrier = [] {
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS accesses are done; vmcnt untouched
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
     };
 
     int32_t done = 0;          // tiles finished by this workgroup
-    int p = 0;                 // reduction buffer parity
-    // the end of a tile: the S waves' partial tiles are added in wave order and the
-    // outputs kept in LDS; the buffer of one parity is written again two tiles later,
-    // after a barrier that every reader of it has passed
+    // the end of a tile: the wave's partial sums of the outputs m < M (registers r < M of
+    // lanes 0..15) go to LDS; the S waves' partials are added after the last job, so the
+    // waves never wait for each other inside the loop
     auto tile_end = [&]() {
+        if (lane < 16) {
 #pragma unroll
-        for (int r = 0; r < kR; ++r) red[p][wave][r][lane] = acc[r];
-        bare_barrier();
-        const int e = threadIdx.x;             // M * 16 <= 256 <= S * 64 outputs per tile
-        if (e < M * 16) {
-            // output (m, nn): register r = m % 4 of lane nn + 16 (m / 4)
-            const int m = e >> 4, nn = e & 15;
-            const int r = m & 3, ln = nn + 16 * (m >> 2);
-            float v = 0.0f;
-#pragma unroll
-            for (int w = 0; w < S; ++w) v += red[p][w][r][ln];
-            outb[done][e] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+            for (int r = 0; r < kR; ++r) part[done][wave][r][lane] = acc[r];
         }
         acc = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        p ^= 1;
         ++done;
     };
     auto end_job = [&]() {
@@ -410,39 +457,68 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
             }
         }
     }
-    bare_barrier();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the table is written; vmcnt untouched
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     // Two jobs in flight: each job is computed from its LDS slot (the wait is for its own
     // copies, issued before the other slot's), then its slot is refilled with the job two
-    // ahead before the tile end's barrier.  The loop runs whole pairs of jobs with no
-    // condition around a load (the last pair may end with a job past the end, which adds
-    // nothing) and writes no global memory, so the compiler's wait before each compute
-    // leaves the other slot's copies outstanding.  A slot is refilled only after every LDS
-    // read of it has returned: the compute consumes all of them.
+    // ahead.  The loop runs whole pairs of jobs with no condition around a load (the last
+    // pair may end with a job past the end, whose sums are never stored), has no barrier and
+    // writes no global memory, so the compiler's wait before each compute leaves the other
+    // slot's copies outstanding.  A slot is refilled only after every LDS read of it has
+    // returned: the compute consumes all of them.
+    //
+    // The waits are explicit: before a job is computed, at most the other job's kLoads
+    // loads may still be in flight (so every copy into this job's slot has landed), and
+    // before a slot is refilled every LDS read of it has returned.  (The compiler's own
+    // tracking of copies into LDS is not relied on: it can miss the copies issued before
+    // the loop.)
+    auto wait_job = [] {
+        __builtin_amdgcn_s_waitcnt((kLoads & 15) | ((kLoads >> 4) << 14) | (7 << 4) | (15 << 8));
+        asm volatile("" ::: "memory");
+    };
+    auto wait_lds = [] {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt untouched
+        asm volatile("" ::: "memory");
+    };
     const int32_t npairs = (njobs + 1) / 2;
     int32_t it = 0;
     do {
+        wait_job();
         compute(cc, ra, SlotA{});
+        wait_lds();
         load(lc, ra, SlotA{});
         advance_load(lc);
         end_job();
+        wait_job();
         compute(cc, rb, SlotB{});
+        wait_lds();
         load(lc, rb, SlotB{});
         advance_load(lc);
         end_job();
     } while (++it < npairs);
 
-    // outputs of the workgroup's tiles, from LDS to y
-    bare_barrier();
+    // the last pair may have loaded jobs past the end: their copies into LDS land before
+    // the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    // outputs of the workgroup's tiles: the S partials added in wave order, to y
     int32_t t = 0;
-    for (int32_t k = 0; k < done; ++k) {
-        const int32_t item = wg + k * G;
-        t = task_from(item, t);
-        const GemvTask& T = g.t[t];
-        const int64_t n0 = (int64_t)(item - T.item0) * 16;
-        const int e = threadIdx.x;
-        if (e < M * 16) {
+    const int32_t per_pass = (S * 64) / (M * 16);   // tiles summed per pass of the workgroup
+    for (int32_t k0 = 0; k0 < done; k0 += per_pass) {
+        const int32_t k = k0 + (int32_t)threadIdx.x / (M * 16);
+        const int e = (int)threadIdx.x % (M * 16);
+        if ((int32_t)threadIdx.x < per_pass * M * 16 && k < done) {
+            const int32_t item = wg + k * G;
+            t = task_from(item, t);
+            const GemvTask& T = g.t[t];
+            const int64_t n0 = (int64_t)(item - T.item0) * 16;
             const int m = e >> 4, nn = e & 15;
-            if (n0 + nn < T.N) T.y[(int64_t)m * T.ystride + n0 + nn] = outb[k][e];
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < S; ++w) v += part[k][w][m][nn];
+            if (n0 + nn < T.N) T.y[(int64_t)m * T.ystride + n0 + nn] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
         }
     }
 }
@@ -500,8 +576,9 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
     }
     // waves per workgroup: 8 for M = 1, else 4 (LDS holds two staged jobs of every wave)
     const int S = M == 1 ? 8 : 4;
+    const int MX = M == 1 ? 1 : M == 2 ? 2 : 4;
     const int64_t cus = device_cu_count();
-    const int64_t max_tiles = kOutSlots * cus;     // tiles per launch: LDS holds each workgroup's outputs
+    const int64_t max_tiles = (int64_t)out_slots(S, MX) * cus;   // tiles per launch: LDS holds each workgroup's partials
     // weights the fast kernel cannot take go one by one through the generic kernel; the
     // others are cut into slices of rows whose codes fit a 31-bit buffer offset and whose
     // tiles fit one launch
@@ -567,6 +644,8 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
     for (size_t f = 0; f < order.size(); ++f) {
         if (used[order[f]]) continue;
         const DeqArgs& w0 = *slice_w[order[f]];
+        // rows that are whole jobs take the kernel whose scales are one aligned run per job
+        const bool aligned = slices[order[f]].K % kChunkK == 0;
         GemvGroup gg;
         std::memset(&gg, 0, sizeof(gg));
         std::memcpy(gg.levels, w0.levels, sizeof(gg.levels));
@@ -576,7 +655,7 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
             const size_t k = order[f2];
             if (used[k]) continue;
             const DeqArgs& w = *slice_w[k];
-            if (w.nested != w0.nested || w.blocksize != w0.blocksize ||
+            if (w.nested != w0.nested || w.blocksize != w0.blocksize || (slices[k].K % kChunkK == 0) != aligned ||
                 std::memcmp(w.levels, w0.levels, sizeof(w.levels)) != 0)
                 continue;
             const int64_t tiles = (slices[k].N + 15) / 16;
@@ -592,10 +671,15 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
         const unsigned grid = (unsigned)(nitems < cus ? nitems : cus);
         *variant = "mfma 16x16x32 bf16, persistent grouped launch: 16-row tiles, 8 (M <= 4) or 4 waves split K "
                    "in 512-k jobs, three in flight per wave, codes loaded in MFMA layout, x rows staged through LDS";
-#define QK_GEMV_LAUNCH_Q(SS, MXX, CC, QQ)                                                                    \
-    do {                                                                                                     \
-        if (w0.nested) hipLaunchKernelGGL((gemv_group_kernel<SS, MXX, CC, true, QQ>), dim3(grid), dim3(SS * 64), 0, s, gg); \
-        else hipLaunchKernelGGL((gemv_group_kernel<SS, MXX, CC, false, QQ>), dim3(grid), dim3(SS * 64), 0, s, gg); \
+#define QK_GEMV_LAUNCH_A(SS, MXX, CC, NN, QQ)                                                                      \
+    do {                                                                                                           \
+        if (aligned) hipLaunchKernelGGL((gemv_group_kernel<SS, MXX, CC, NN, QQ, true>), dim3(grid), dim3(SS * 64), 0, s, gg); \
+        else hipLaunchKernelGGL((gemv_group_kernel<SS, MXX, CC, NN, QQ, false>), dim3(grid), dim3(SS * 64), 0, s, gg); \
+    } while (0)
+#define QK_GEMV_LAUNCH_Q(SS, MXX, CC, QQ)                                \
+    do {                                                                 \
+        if (w0.nested) QK_GEMV_LAUNCH_A(SS, MXX, CC, true, QQ);          \
+        else QK_GEMV_LAUNCH_A(SS, MXX, CC, false, QQ);                   \
     } while (0)
 #define QK_GEMV_LAUNCH(SS, MXX, CC)                       \
     do {                                                  \
@@ -608,6 +692,7 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
         else QK_GEMV_LAUNCH(4, 4, 64);
 #undef QK_GEMV_LAUNCH
 #undef QK_GEMV_LAUNCH_Q
+#undef QK_GEMV_LAUNCH_A
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -54,6 +54,23 @@ def test_grouped_llama7b_layer(M):
     _check_group(weights, M, g, oracle_every=3)
 
 
+@pytest.mark.parametrize("B", [64, 128])
+@pytest.mark.parametrize("M", [1, 4])
+def test_double_quant_block_boundaries_inside_jobs(M, B):
+    """Rows of K = 4160 or 4224 (not a multiple of 512) whose magnitude jumps by 40x every 8
+    rows (about two double-quantization blocks of 256 absmax values), so
+    neighbouring dq blocks get different scales, each absmax is the mean plus a
+    large correction, and the dq-block boundaries fall inside the kernel's 512-k
+    jobs at many offsets: a block that took its neighbour's dq scale would be off
+    by far more than the tolerance."""
+    say(f"case: gemv dq-block boundaries inside jobs M={M} B={B}")
+    g = np.random.default_rng(7 + M + B)
+    N, K = 96, (4160 if B == 64 else 4224)      # K % 512 != 0, K % B == 0
+    mag = np.where((np.arange(N) // 8) % 2 == 0, 0.02, 0.8).astype(np.float32)[:, None]
+    W = ofl.f32_to_bf16_bits((g.standard_normal((N, K)).astype(np.float32) * mag).astype(np.float32))
+    _check_group([(W, B, ocb.NF4, True)], M, g)
+
+
 def test_grouped_mixed_tables_blocks_nesting_and_ragged():
     """NF4 / FP4, blocks 64 / 128 / 256, nested or not, ragged rows, K not a multiple
     of 512, and one weight on the generic path (K % 64 != 0): several launches."""
