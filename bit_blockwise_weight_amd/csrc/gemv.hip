@@ -51,6 +51,8 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kStep = 64;          // k per step
 constexpr int kTabCopies = 64;
+// rows of x from which the row-split kernel (shared x chunk) replaces the K-split one
+constexpr int kRowsMinM = 2;
 
 struct GemvArgs {
     const uint16_t* x;   // [M, K] bf16 bits
@@ -523,6 +525,265 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     }
 }
 
+// Row-split kernel for M >= 2 rows of x: each wave owns whole 16-row tiles and walks the
+// row from k = 0 to K in 512-k jobs; the S waves of a workgroup own S consecutive tiles of
+// one slice (a "group", one workgroup each, launched longest rows first so the hardware
+// dispatcher balances them) and take the same job at the same time, so the x chunk of a
+// job (M rows x 1 KB) is copied to LDS once per workgroup and shared.  Each wave's sums
+// cover its whole rows, so the outputs go straight from registers to y.
+//
+// The codes and scales of a job are loaded two jobs ahead into the wave's own LDS slot
+// and registers (as in the K-split kernel); the x chunk one job ahead into the shared
+// slot, after the barrier that ends every wave's use of that slot.  x row m sits in its
+// slot with its 16-byte units XOR-swizzled by m (unit u at u ^ m, the swizzle applied to
+// the global offsets of the copy), so the fragment reads of 16 rows fall in 16 distinct
+// bank groups without padding.
+template <int S, int MX, bool kNested, int QS, bool kAligned>
+__global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
+    constexpr int C = kTabCopies;
+    constexpr int kJobQ = kChunkBlocks >> QS;
+    constexpr int kLc = (kNested || QS == 0 ? 2 : 1) + 4;   // a job's scale loads and code copies
+    constexpr int kXL = (MX + S - 1) / S;                     // x rows a wave copies per job
+    constexpr int kXR = kXL * S;                              // rows of an x slot (rows >= MX are never read)
+    __shared__ __attribute__((aligned(4096))) uint32_t tab[256 * C];
+    __shared__ __attribute__((aligned(1024))) uint4 cb0[S * 256];
+    __shared__ __attribute__((aligned(1024))) uint4 cb1[S * 256];
+    __shared__ __attribute__((aligned(1024))) uint4 xs0[kXR * 64];
+    __shared__ __attribute__((aligned(1024))) uint4 xs1[kXR * 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int h = lane >> 4;
+    const int M = g.M;
+
+    // this workgroup's group: slice t, tiles S (item - item0) + w
+    const int32_t item = (int32_t)blockIdx.x;
+    int32_t t = 0;
+    while (t + 1 < g.ntasks && item >= g.t[t + 1].item0) ++t;
+    const GemvTask& T = g.t[t];
+    const int32_t N = (int32_t)T.N;
+    const int32_t K = T.K;
+    const int32_t nchunk = T.nchunk;
+    const uint32_t row_bytes = (uint32_t)(K / 2);
+    const int32_t n0 = ((item - T.item0) * S + wave) * 16;   // may be past N: rows clamped, never stored
+    const float mu = kNested ? *(const __attribute__((address_space(4))) float*)(uintptr_t)T.dq_mean : 0.0f;
+    const __amdgpu_buffer_rsrc_t cr = buf_rsrc(T.codes, T.code_bytes);
+    const __amdgpu_buffer_rsrc_t xr = buf_rsrc(T.x, M * K * 2);
+    const __amdgpu_buffer_rsrc_t sr = buf_rsrc(T.sc, T.sc_bytes);
+    const __amdgpu_buffer_rsrc_t dr = buf_rsrc(T.dq_scale, T.dq_bytes);
+    uint32_t crow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int32_t gr = n0 + r < N ? n0 + r : N - 1;
+        crow[i] = (uint32_t)gr * row_bytes + 16u * (uint32_t)((lane & 15) ^ r);
+    }
+    const int32_t rowc = n0 + n < N ? n0 + n : N - 1;
+    const uint32_t qrow = (uint32_t)T.qbase + (uint32_t)rowc * (uint32_t)(K >> (QS + 6));
+
+    // codes and scales of job j (chunk clamped to the last: a job past the end reloads
+    // valid memory and is never computed)
+    auto load_codes = [&](int32_t j, JobRegs& jr, auto slot) {
+        constexpr bool kB = decltype(slot)::value;
+        const int32_t chc = j < nchunk ? j : nchunk - 1;
+        const uint32_t qf = qrow + (uint32_t)(chc * kJobQ);
+        if constexpr (kNested) {
+            if constexpr (kAligned) {
+                if constexpr (QS == 0)
+                    jr.q.xy = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(sr, qrow, (uint32_t)(chc * kJobQ), 0));
+                else
+                    jr.q.x = __builtin_amdgcn_raw_buffer_load_b32(sr, qf & ~3u, 0, 0);
+                if constexpr (QS == 2) jr.qinfo = qf & 3u;
+                jr.d.x = __builtin_amdgcn_raw_buffer_load_b32(dr, (qf / QK_DQ_BLOCK) * 4u, 0, 0);
+            } else {
+                jr.q = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(sr, qf & ~3u, 0, 0));
+                jr.d = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(dr, (qf / QK_DQ_BLOCK) * 4u, 0, 0));
+                jr.qinfo = (qf & 3u) | ((QK_DQ_BLOCK - qf % QK_DQ_BLOCK) << 2);
+            }
+        } else {
+            jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, qf * 4u, 0, 0));
+            if constexpr (QS == 0)
+                jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr, qf * 4u + 16u, 0, 0));
+        }
+        __attribute__((address_space(3))) char* cdst =
+            (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? cb1 : cb0) + wave * 4096;
+        const uint32_t cofs = (uint32_t)chc * (kChunkK / 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t off = crow[i] + cofs;
+            if constexpr (!kAligned) {
+                // pieces past the end of a row (partial chunk) are clamped to its last 16 bytes
+                const int r = 4 * i + (lane >> 4);
+                const uint32_t piece = 16u * (uint32_t)((lane & 15) ^ r);
+                off = cofs + piece + 16u <= row_bytes ? off : crow[i] + row_bytes - 16u - piece;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr_t)(cdst + i * 1024), 16, off, 0, 0, 0);
+        }
+    };
+    // x rows m = wave + S i of job j, unit L of the row from global unit L ^ m (k past the
+    // row in a partial chunk reads zero).  Rows m >= M copy row M - 1 (they feed only
+    // outputs that are never stored): every wave issues the same copies, with no branch.
+    uint32_t xo_live[kXL];
+    auto load_x = [&](int32_t j, auto slot) {
+        constexpr bool kB = decltype(slot)::value;
+        __attribute__((address_space(3))) char* xdst =
+            (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? xs1 : xs0);
+#pragma unroll
+        for (int i = 0; i < kXL; ++i) {
+            const int m = wave + S * i;
+            const int ms = m < M ? m : M - 1;
+            const int u = lane ^ (m & 15);
+            const uint32_t xo = j * kChunkK + 8 * u < K ? (uint32_t)(j * (kChunkK * 2) + 16 * u + ms * K * 2) : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xdst + m * 1024), 16, xo, 0, 0, 0);
+            xo_live[i] = xo;
+        }
+    };
+    // the offset registers of the x copies stay allocated until the job's reads are issued
+    // (the compiler otherwise reuses one for an LDS read's result and waits for the copy)
+    auto keep_x = [&] {
+#pragma unroll
+        for (int i = 0; i < kXL; ++i) asm volatile("" ::"v"(xo_live[i]));
+    };
+
+    floatx4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t lane_sel = (uint32_t)lane * 4u;
+    const char* tabb = reinterpret_cast<const char*>(tab);
+    const int xrow = n < M ? n : M - 1;        // A operand rows m >= M: another row's data, never stored
+    auto compute = [&](const JobRegs& jr, auto slot) {
+        constexpr bool kB = decltype(slot)::value;
+        const char* mb = reinterpret_cast<const char*>(kB ? cb1 : cb0) + wave * 4096;
+        const u32x4_t* xf = reinterpret_cast<const u32x4_t*>(kB ? xs1 : xs0) + xrow * 64;
+        uint32_t qlo = 0, qhi = 0, split = 8;
+        float dsc0 = 0.0f, dsc1 = 0.0f;
+        if constexpr (kNested) {
+            if constexpr (kAligned) {
+                if constexpr (QS == 2) {
+                    qlo = jr.q.x >> (8u * jr.qinfo);
+                } else {
+                    qlo = jr.q.x;
+                    qhi = jr.q.y;
+                }
+                const uint32_t d0 = jr.d[0];
+                dsc0 = dsc1 = __builtin_bit_cast(float, d0);
+            } else {
+                const uint32_t sh = jr.qinfo & 3u;
+                qlo = __builtin_amdgcn_alignbyte(jr.q[1], jr.q[0], sh);
+                qhi = __builtin_amdgcn_alignbyte(jr.q[2], jr.q[1], sh);
+                split = jr.qinfo >> 2;
+                const uint32_t d0 = jr.d[0], d1 = jr.d[1];
+                dsc0 = __builtin_bit_cast(float, d0);
+                dsc1 = __builtin_bit_cast(float, d1);
+            }
+        }
+#pragma unroll
+        for (int bb = 0; bb < kChunkBlocks; ++bb) {
+            const int piece = 2 * bb + (h >> 1);
+            const u32x2_t cw = *reinterpret_cast<const u32x2_t*>(mb + (16 * n + (piece ^ n)) * 16 + 8 * (h & 1));
+            const uint32_t cws[2] = {cw[0], cw[1]};
+            floatx4_t pp = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const uint32_t addr = __builtin_amdgcn_perm(cws[tt], lane_sel, 0x0C0C0400u | ((uint32_t)(4 + k4) << 8));
+                    wv[k4] = *reinterpret_cast<const uint32_t*>(tabb + addr);
+                }
+                const u32x4_t xv = xf[(8 * bb + 2 * h + tt) ^ (xrow & 15)];
+                pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
+                                                             __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3])),
+                                                             pp, 0, 0, 0);
+            }
+            const uint32_t qq = (uint32_t)bb >> QS;
+            float a;
+            if constexpr (kNested) {
+                const uint32_t word = qq < 4 ? qlo : qhi;
+                const int32_t q8 = __builtin_amdgcn_sbfe((int32_t)word, 8 * (qq & 3), 8);
+                const float dsc = qq < split ? dsc0 : dsc1;
+                a = __fadd_rn(__fmul_rn((float)q8, dsc), mu);
+            } else {
+                const uint32_t fsel[8] = {jr.f0[0], jr.f0[1], jr.f0[2], jr.f0[3], jr.f1[0], jr.f1[1], jr.f1[2], jr.f1[3]};
+                a = __builtin_bit_cast(float, fsel[qq]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(pp[r], a, acc[r]);
+        }
+    };
+
+    using SlotA = std::integral_constant<bool, false>;
+    using SlotB = std::integral_constant<bool, true>;
+    JobRegs ra, rb;
+    // issue order codes(0), x(0), codes(1): the wait before job j allows only the codes of
+    // job j + 1 in flight
+    load_codes(0, ra, SlotA{});
+    load_x(0, SlotA{});
+    load_codes(1, rb, SlotB{});
+    {
+        constexpr int kLo = 16 / S;
+        float lo[kLo];
+#pragma unroll
+        for (int q = 0; q < kLo; ++q) lo[q] = g.levels[wave + S * q];
+        if (lane < C) {
+#pragma unroll
+            for (int jj = 0; jj < 256 / S; ++jj) {
+                const float hi_nib = g.levels[jj / kLo];
+                tab[(wave + S * jj) * C + lane] = pack_bf16x2(hi_nib, lo[jj % kLo]);
+            }
+        }
+    }
+    // (each wait is also a scheduling barrier: the compiler would otherwise hoist the next
+    // job's scale arithmetic above it and wait for that job's loads)
+    auto wait_job = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((kLc & 15) | ((kLc >> 4) << 14) | (7 << 4) | (15 << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto wait_lds = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt untouched
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto barrier = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Job j: wait until this wave's codes and x part of job j have landed (only the codes of
+    // job j + 1 may be in flight), and the table is written; the barrier then makes every
+    // wave's x part visible and ends every wave's reads of the other x slot, which takes
+    // job j + 1's x; after the job, its code slot takes job j + 2.  The loop runs whole pairs
+    // of jobs with no condition around a load or a read (a condition makes the compiler
+    // wait for every copy in flight): a job past the end reads x as zero and adds nothing.
+    for (int32_t j = 0; j < nchunk; j += 2) {
+        wait_job();
+        wait_lds();
+        barrier();
+        load_x(j + 1, SlotB{});
+        compute(ra, SlotA{});
+        keep_x();
+        wait_lds();
+        load_codes(j + 2, ra, SlotA{});
+        wait_job();
+        barrier();
+        load_x(j + 2, SlotA{});
+        compute(rb, SlotB{});
+        keep_x();
+        wait_lds();
+        load_codes(j + 3, rb, SlotB{});
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no copy into LDS outlives the workgroup
+    // outputs: register r of lane l is y[4 (l / 16) + r][n0 + l % 16]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * h + r;
+        if (m < M && n0 + n < N)
+            T.y[(int64_t)m * T.ystride + n0 + n] = (uint16_t)(pack_bf16x2(acc[r], 0.0f) & 0xFFFFu);
+    }
+}
+
 // Generic path: one wave per weight row, per-element dequantization.
 __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
     __shared__ float lev[16];
@@ -560,25 +821,16 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
 
 hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hipStream_t s,
                              const char** variant) {
-    // more than 4 rows of x: groups of at most 4 rows (each a launch that reads the weights)
-    if (M > 4) {
-        std::vector<GemvItem> part(items, items + count);
-        for (int32_t m0 = 0; m0 < M; m0 += 4) {
-            const int32_t mr = M - m0 < 4 ? M - m0 : 4;
-            for (int32_t i = 0; i < count; ++i) {
-                part[i].x = reinterpret_cast<const uint16_t*>(items[i].x) + (int64_t)m0 * items[i].w.K;
-                part[i].y = reinterpret_cast<uint16_t*>(items[i].y) + (int64_t)m0 * items[i].w.N;
-            }
-            const hipError_t e = launch_gemv_group(part.data(), count, mr, s, variant);
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
-    }
-    // waves per workgroup: 8 for M = 1, else 4 (LDS holds two staged jobs of every wave)
-    const int S = M == 1 ? 8 : 4;
-    const int MX = M == 1 ? 1 : M == 2 ? 2 : 4;
+    // M = 1: the K-split kernel (8 waves share each 16-row tile, persistent); M >= 2: the
+    // row-split kernel (8 waves, one 16-row tile each, sharing the x chunk; one workgroup
+    // per group of 8 tiles)
+    const bool rows = M >= kRowsMinM;
+    const int S = 8;
+    const int MX = rows ? (M <= 4 ? 4 : M <= 8 ? 8 : 16) : 1;
     const int64_t cus = device_cu_count();
-    const int64_t max_tiles = (int64_t)out_slots(S, MX) * cus;   // tiles per launch: LDS holds each workgroup's partials
+    // tiles per launch: the K-split kernel's LDS holds each workgroup's partials; the
+    // row-split kernel's groups are only bounded by the grid
+    const int64_t max_tiles = rows ? ((int64_t)1 << 30) : (int64_t)out_slots(S, MX) * cus;
     // weights the fast kernel cannot take go one by one through the generic kernel; the
     // others are cut into slices of rows whose codes fit a 31-bit buffer offset and whose
     // tiles fit one launch
@@ -659,18 +911,48 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
                 std::memcmp(w.levels, w0.levels, sizeof(w.levels)) != 0)
                 continue;
             const int64_t tiles = (slices[k].N + 15) / 16;
-            if (nitems + tiles > max_tiles) continue;
+            const int64_t units = rows ? (tiles + S - 1) / S : tiles;   // row-split: groups of S tiles
+            if (nitems + units > max_tiles) continue;
             GemvTask& t = gg.t[gg.ntasks++];
             t = slices[k];
             t.item0 = (int32_t)nitems;
-            nitems += tiles;
+            nitems += units;
             used[k] = true;
         }
         gg.nitems = (int32_t)nitems;
         gg.qs = w0.blocksize_log2 - 6;
-        const unsigned grid = (unsigned)(nitems < cus ? nitems : cus);
-        *variant = "mfma 16x16x32 bf16, persistent grouped launch: 16-row tiles, 8 (M <= 4) or 4 waves split K "
-                   "in 512-k jobs, three in flight per wave, codes loaded in MFMA layout, x rows staged through LDS";
+        const unsigned grid = rows ? (unsigned)nitems : (unsigned)(nitems < cus ? nitems : cus);
+        *variant = rows ? "mfma 16x16x32 bf16, row-split grouped launch: one workgroup per 8 tiles of 16 rows, each wave "
+                          "a whole tile, the x chunk shared through LDS, codes and scales two 512-k jobs ahead"
+                        : "mfma 16x16x32 bf16, persistent grouped launch: 16-row tiles split over 8 waves in 512-k jobs, "
+                          "two jobs in flight per wave, codes and x copied to LDS";
+        if (rows) {
+#define QK_GEMV_ROWS_A(MXX, NN, QQ)                                                                                    \
+    do {                                                                                                               \
+        if (aligned) hipLaunchKernelGGL((gemv_rows_kernel<8, MXX, NN, QQ, true>), dim3(grid), dim3(8 * 64), 0, s, gg); \
+        else hipLaunchKernelGGL((gemv_rows_kernel<8, MXX, NN, QQ, false>), dim3(grid), dim3(8 * 64), 0, s, gg);        \
+    } while (0)
+#define QK_GEMV_ROWS_Q(MXX, QQ)                                  \
+    do {                                                         \
+        if (w0.nested) QK_GEMV_ROWS_A(MXX, true, QQ);            \
+        else QK_GEMV_ROWS_A(MXX, false, QQ);                     \
+    } while (0)
+#define QK_GEMV_ROWS(MXX)                                        \
+    do {                                                         \
+        if (gg.qs == 0) QK_GEMV_ROWS_Q(MXX, 0);                  \
+        else if (gg.qs == 1) QK_GEMV_ROWS_Q(MXX, 1);             \
+        else QK_GEMV_ROWS_Q(MXX, 2);                             \
+    } while (0)
+            if (MX == 4) QK_GEMV_ROWS(4);
+            else if (MX == 8) QK_GEMV_ROWS(8);
+            else QK_GEMV_ROWS(16);
+#undef QK_GEMV_ROWS
+#undef QK_GEMV_ROWS_Q
+#undef QK_GEMV_ROWS_A
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            continue;
+        }
 #define QK_GEMV_LAUNCH_A(SS, MXX, CC, NN, QQ)                                                                      \
     do {                                                                                                           \
         if (aligned) hipLaunchKernelGGL((gemv_group_kernel<SS, MXX, CC, NN, QQ, true>), dim3(grid), dim3(SS * 64), 0, s, gg); \
@@ -687,9 +969,7 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
         else if (gg.qs == 1) QK_GEMV_LAUNCH_Q(SS, MXX, CC, 1); \
         else QK_GEMV_LAUNCH_Q(SS, MXX, CC, 2);            \
     } while (0)
-        if (M == 1) QK_GEMV_LAUNCH(8, 1, 64);
-        else if (M == 2) QK_GEMV_LAUNCH(4, 2, 64);
-        else QK_GEMV_LAUNCH(4, 4, 64);
+        QK_GEMV_LAUNCH(8, 1, 64);
 #undef QK_GEMV_LAUNCH
 #undef QK_GEMV_LAUNCH_Q
 #undef QK_GEMV_LAUNCH_A
