@@ -21,6 +21,14 @@ absolute rate from a second pass of K steps with an event after every launch
 (kept out of the timed region: recording 43 events a step costs about 5% of
 it).  `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 
+`extra` also times the other workloads (skip with --skip-configs): a plain 1 GiB
+device copy (the practical HBM ceiling), the 1024 x 1024 weight (microseconds per
+call), GEMV over six replicas of the 7B layer set (624 MB, M = 1 and 16, one
+grouped call per layer, eager and replayed from a HIP graph), the 70B-shaped
+8-layer stack (bulk quantize + double quant of 56 weights, then grouped GEMV at
+M = 1, 4, 8), the edge set (3000 x 4099, blocks 64/128/256, NF4 and FP4, GEMM at
+M = 512) and the shader clock under load.
+
 Other modes:
   --copy-calibration          run a plain 1 GiB device copy (for HBM counter scaling)
   --summarize-pmc DIR KERNEL  summarize rocprofv3 --pmc output of FETCH_SIZE / WRITE_SIZE
@@ -362,38 +370,261 @@ def int8_rate(torch, qk, workloads, iters=10):
     return res
 
 
-def gemv_isolated(torch, qk, workloads, reps=6, iters=20):
-    """GEMV M=1 over `reps` copies of the layer set (607 MB of NF4 state at 6),
-    cycled so the 256 MB last-level cache cannot hold them; HBM rate."""
-    dev = torch.device("cuda:0")
-    lv = qk.qk_make_codebook(qk.NF4)
-    states, xs, ys = [], {}, []
-    total_bytes = 0
-    for rep in range(reps):
-        for i, (name, N, K) in enumerate(workloads.LLAMA7B_SHAPES):
-            w = torch.randn((N, K), device=dev, dtype=torch.float32).mul_(0.02).to(torch.bfloat16)
-            qw = qk.quantize(w, 64, qk.NF4, True)
-            del w
-            states.append((qw, K, N))
-            ys.append(torch.empty((1, N), dtype=torch.bfloat16, device=dev))
-            total_bytes += bytes_gemv(1, N, K)
-    for K in (4096, 11008):
-        xs[K] = torch.randn((1, K), device=dev).to(torch.bfloat16)
-    torch.cuda.synchronize()
-    for (qw, K, N), y in zip(states, ys):
-        qk.qk_gemv_nf4(xs[K], qw.state, y)
+def _timed(torch, fn, iters):
+    """Seconds per call of fn (warm), between HIP events on the current stream."""
+    fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
-        for (qw, K, N), y in zip(states, ys):
-            qk.qk_gemv_nf4(xs[K], qw.state, y)
+        fn()
     e1.record()
     torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3
-    launches = iters * len(states)
-    return {"gb_per_s": total_bytes * iters / sec / 1e9, "us_per_layer": sec / (iters * reps) * 1e6,
-            "launches": launches, "working_set_mb": round(total_bytes / 1e6, 1)}
+    return e0.elapsed_time(e1) / iters * 1e-3
+
+
+def _graph_timed(torch, fn, iters):
+    """Seconds per replay of fn captured into a HIP graph (no host work per launch).
+    The library launches only kernels on the caller's stream, so capture records
+    exactly the eager launches."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    sec = _timed(torch, g.replay, iters)
+    del g
+    return sec
+
+
+def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
+    """The 70B-shaped stack: 8 layers of q, o [8192, 8192], k, v [1024, 8192],
+    gate, up [28672, 8192], down [8192, 28672] (the GQA layer of the 70B model),
+    bf16 ~ N(0, 0.015) drawn on the device (seeded Philox).  Bulk quantize
+    (NF4 block 64) + double quant of all 56 weights, then the grouped GEMV (one
+    call per layer, 7 weights) at batch 1, 4 and 8, eager and replayed from a HIP
+    graph.  Rates are algorithmic bytes over time."""
+    dev = torch.device("cuda:0")
+    L = workloads.LLAMA70B_LAYERS
+    shapes = workloads.LLAMA70B_LAYER_SHAPES
+    lv = qk.qk_make_codebook(qk.NF4)
+    lvc = (ctypes.c_float * 16)(*lv.tolist())
+    mats = []
+    for l in range(L):
+        for i, (name, N, K) in enumerate(shapes):
+            n = N * K
+            nb = nblk(n, 64)
+            mats.append({
+                "l": l, "N": N, "K": K,
+                "w": workloads.device_normal_bf16((N, K), 0.015, workloads.llama70b_seed(l, i)),
+                "codes": torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev),
+                "absmax": torch.empty(nb, dtype=torch.float32, device=dev),
+                "q8": torch.empty(nb, dtype=torch.int8, device=dev),
+                "scale": torch.empty(nblk(nb, 256), dtype=torch.float32, device=dev),
+                "mean": torch.empty(1, dtype=torch.float32, device=dev),
+                "ws": torch.empty(max(8, qk.qk_double_quant_workspace_size(nb)), dtype=torch.uint8, device=dev),
+            })
+
+    def quantize_all():
+        for m in mats:
+            qk.qk_quantize_blockwise(m["w"], 64, lvc, m["codes"], m["absmax"])
+
+    def dq_all():
+        for m in mats:
+            qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])
+
+    def both():
+        quantize_all()
+        dq_all()
+
+    t_both = _timed(torch, both, iters)
+    t_q = _timed(torch, quantize_all, iters)
+    t_dq = _timed(torch, dq_all, iters)
+    qbytes = sum(bytes_quantize(m["N"] * m["K"]) for m in mats)
+    dqbytes = sum(bytes_double_quant(nblk(m["N"] * m["K"], 64)) for m in mats)
+    out = {"layers": L, "weights": len(mats), "params": sum(m["N"] * m["K"] for m in mats),
+           "quantize_dq_ms": round(t_both * 1e3, 3),
+           "quantize_dq_tb_per_s": round((qbytes + dqbytes) / t_both / 1e12, 3),
+           "quantize_dq_frac_of_hbm": round((qbytes + dqbytes) / t_both / HBM_BPS, 4),
+           "quantize_only_ms": round(t_q * 1e3, 3), "quantize_only_tb_per_s": round(qbytes / t_q / 1e12, 3),
+           "dq_only_ms": round(t_dq * 1e3, 3), "dq_us_per_weight": round(t_dq / len(mats) * 1e6, 2)}
+    for m in mats:
+        m["state"] = qk.qk_state_init(qk.NF4, lv, m["N"], m["K"], 64, m["codes"], None, m["q8"], m["scale"],
+                                      m["mean"])
+        del m["w"], m["absmax"], m["ws"]
+    torch.cuda.empty_cache()
+    layers = [[m for m in mats if m["l"] == l] for l in range(L)]
+    gemv = {}
+    for M in (1, 4, 8):
+        xs = {K: torch.randn((M, K), device=dev).to(torch.bfloat16) for K in set(m["K"] for m in mats)}
+        ys = [[torch.empty((M, m["N"]), dtype=torch.bfloat16, device=dev) for m in lay] for lay in layers]
+        tasks = [[(xs[m["K"]], m["state"]) for m in lay] for lay in layers]
+
+        def run():
+            for t, y in zip(tasks, ys):
+                qk.qk_gemv_nf4_grouped(t, y)
+
+        nbytes = sum(bytes_gemv(M, m["N"], m["K"]) for m in mats)
+        te = _timed(torch, run, gemv_iters)
+        tg = _graph_timed(torch, run, gemv_iters)
+        gemv[f"M{M}"] = {"us_per_layer_graph": round(tg / L * 1e6, 2),
+                         "tb_per_s_graph": round(nbytes / tg / 1e12, 3),
+                         "frac_of_hbm_graph": round(nbytes / tg / HBM_BPS, 4),
+                         "us_per_layer_eager": round(te / L * 1e6, 2),
+                         "tb_per_s_eager": round(nbytes / te / 1e12, 3)}
+        del xs, ys, tasks
+    out["gemv_grouped"] = gemv
+    out["gemv_bytes_per_layer_m1"] = sum(bytes_gemv(1, m["N"], m["K"]) for m in layers[0])
+    del mats, layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def gemv_rotating(torch, qk, workloads, reps=6, iters=10):
+    """GEMV over `reps` replicas of the Llama-7B layer set (624 MB of NF4 state at
+    6, more than the 256 MB last-level cache), one grouped call per layer (7
+    weights), cycled through the replicas; M = 1 and 16; eager and replayed from a
+    HIP graph.  The replicas' weights are drawn on the device (seeded Philox,
+    N(0, 0.02))."""
+    dev = torch.device("cuda:0")
+    layers = []
+    for rep in range(reps):
+        lay = []
+        for i, (name, N, K) in enumerate(workloads.LLAMA7B_SHAPES):
+            w = workloads.device_normal_bf16((N, K), 0.02, 7_000_000 + 97 * rep + i)
+            lay.append((qk.quantize(w, 64, qk.NF4, True), N, K))
+            del w
+        layers.append(lay)
+    torch.cuda.empty_cache()
+    res = {"replicas": reps, "working_set_mb": round(sum(bytes_state(N * K) for lay in layers for _, N, K in lay) / 1e6, 1)}
+    for M in (1, 16):
+        xs = {K: torch.randn((M, K), device=dev).to(torch.bfloat16) for K in (4096, 11008)}
+        ys = [[torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N, _ in lay] for lay in layers]
+        tasks = [[(xs[K], qw.state) for qw, _, K in lay] for lay in layers]
+
+        def run():
+            for t, y in zip(tasks, ys):
+                qk.qk_gemv_nf4_grouped(t, y)
+
+        nbytes = sum(bytes_gemv(M, N, K) for lay in layers for _, N, K in lay)
+        te = _timed(torch, run, iters)
+        tg = _graph_timed(torch, run, iters)
+        res[f"M{M}"] = {"us_per_layer_graph": round(tg / reps * 1e6, 2), "tb_per_s_graph": round(nbytes / tg / 1e12, 3),
+                        "frac_of_hbm_graph": round(nbytes / tg / HBM_BPS, 4),
+                        "us_per_layer_eager": round(te / reps * 1e6, 2), "tb_per_s_eager": round(nbytes / te / 1e12, 3)}
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def single_1024_us(torch, qk, workloads, iters=200):
+    """The 1024 x 1024 weight (N(0, 0.02)) and one x ~ N(0, 1): quantize (NF4, block
+    64), double quant, dequantize and GEMV M = 1, microseconds per call (eager,
+    and the four calls replayed from a HIP graph)."""
+    W, x = workloads.single_1024()
+    w = torch.from_numpy(W.view("int16")).view(torch.bfloat16).cuda().reshape(1024, 1024)
+    xv = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda().reshape(1, 1024)
+    lv = qk.qk_make_codebook(qk.NF4)
+    lvc = (ctypes.c_float * 16)(*lv.tolist())
+    n = 1024 * 1024
+    nb = nblk(n, 64)
+    codes = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
+    absmax = torch.empty(nb, dtype=torch.float32, device="cuda")
+    q8 = torch.empty(nb, dtype=torch.int8, device="cuda")
+    scale = torch.empty(nblk(nb, 256), dtype=torch.float32, device="cuda")
+    mean = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(8, qk.qk_double_quant_workspace_size(nb)), dtype=torch.uint8, device="cuda")
+    deq = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((1, 1024), dtype=torch.bfloat16, device="cuda")
+    qk.qk_quantize_blockwise(w, 64, lvc, codes, absmax)
+    qk.qk_double_quant(absmax, 256, q8, scale, mean, ws)
+    st = qk.qk_state_init(qk.NF4, lv, 1024, 1024, 64, codes, None, q8, scale, mean)
+    ops = {"quantize": lambda: qk.qk_quantize_blockwise(w, 64, lvc, codes, absmax),
+           "double_quant": lambda: qk.qk_double_quant(absmax, 256, q8, scale, mean, ws),
+           "dequantize": lambda: qk.qk_dequantize(st, torch.bfloat16, deq),
+           "gemv_m1": lambda: qk.qk_gemv_nf4(xv, st, y)}
+    res = {f"{k}_us_eager": round(_timed(torch, f, iters) * 1e6, 2) for k, f in ops.items()}
+
+    def seq():
+        for f in ops.values():
+            f()
+
+    res["all_four_us_graph"] = round(_graph_timed(torch, seq, iters) * 1e6, 2)
+    return res
+
+
+def edge_us(torch, qk, workloads, iters=50):
+    """The edge set: W [3000, 4099] Student-t(3) x 0.02 with 1% of 256-element runs
+    zero and 0.1% of columns x50; blocks 64 / 128 / 256 with NF4 and FP4: quantize
+    + double quant, dequantize and GEMV M = 1, microseconds per call (K = 4099 is
+    not a multiple of 64: blocks straddle rows and the generic kernels run); and the
+    GEMM at M = 512 (NF4, block 64) with and without LoRA r = 16."""
+    N, K = 3000, 4099
+    Wb = workloads.edge_weight(N, K)
+    w = torch.from_numpy(Wb.view("int16")).view(torch.bfloat16).cuda().reshape(N, K)
+    X = torch.from_numpy(workloads.edge_activations(512, K).view("int16")).view(torch.bfloat16).cuda().reshape(512, K)
+    x1 = X[:1].contiguous()
+    res = {}
+    for kind, kname in ((qk.NF4, "nf4"), (qk.FP4, "fp4")):
+        for B in (64, 128, 256):
+            qw = qk.quantize(w, B, kind, double_quant=True)
+            lv = qk.qk_make_codebook(kind)
+            deq = torch.empty(N * K, dtype=torch.bfloat16, device="cuda")
+            y = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+            key = f"{kname}_b{B}"
+            res[f"{key}_quantize_dq_us"] = round(_timed(torch, lambda: qk.quantize(w, B, kind, double_quant=True),
+                                                        iters) * 1e6, 1)
+            res[f"{key}_dequantize_us"] = round(_timed(torch, lambda: qk.qk_dequantize(qw.state, torch.bfloat16, deq),
+                                                       iters) * 1e6, 1)
+            res[f"{key}_gemv_m1_us"] = round(_timed(torch, lambda: qk.qk_gemv_nf4(x1, qw.state, y), iters) * 1e6, 1)
+            del lv
+    qw = qk.quantize(w, 64, qk.NF4, double_quant=True)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    A = (torch.randn((K, 16), generator=g) * 0.01).to(torch.bfloat16).cuda()
+    Bm = (torch.randn((16, N), generator=g) * 0.01).to(torch.bfloat16).cuda()
+    Y = torch.empty((512, N), dtype=torch.bfloat16, device="cuda")
+    wsz = max(16, qk.qk_gemm_nf4_workspace_size(512, 16))
+    ws = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+    t0 = _timed(torch, lambda: qk.qk_gemm_nf4(X, qw.state, None, None, 0.0, Y), iters)
+    t1 = _timed(torch, lambda: qk.qk_gemm_nf4(X, qw.state, A, Bm, 2.0, Y, ws), iters)
+    res["gemm_m512_us"] = round(t0 * 1e6, 1)
+    res["gemm_m512_tflop_per_s"] = round(2 * 512 * N * K / t0 / 1e12, 2)
+    res["gemm_m512_lora_us"] = round(t1 * 1e6, 1)
+    return res
+
+
+def copy_ceiling(torch, iters=10):
+    """A plain 1 GiB device-to-device copy (torch): read + write bytes over time,
+    the practical HBM ceiling next to the 8 TB/s spec."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    t = _timed(torch, lambda: b.copy_(a), iters)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * n, "tb_per_s": round(2 * n / t / 1e12, 3)}
+
+
+def shader_clock(torch, qk, busy_fn):
+    """The shader clock reported by rocm-smi while a long run of busy_fn keeps the
+    GPU working (best effort: absent when rocm-smi is not there)."""
+    import re
+    import subprocess
+    for _ in range(40):
+        busy_fn()
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+    except Exception as e:  # noqa: BLE001 - report, do not fail the bench
+        torch.cuda.synchronize()
+        return {"error": str(e)[:120]}
+    torch.cuda.synchronize()
+    m = re.findall(r"sclk[^\n]*?\((\d+)\s*Mhz\)", txt, flags=re.I)
+    return {"sclk_mhz": [int(v) for v in m][:8], "source": "rocm-smi --showclocks during a busy loop"}
 
 
 def cpu_baseline(workloads):
@@ -549,8 +780,13 @@ def bench(args):
 
     extra = {"ms_per_step_without_events": round(step_noev_s * 1e3, 3),
              "ms_per_step_with_an_event_per_launch": round(step_allev_s * 1e3, 3)}
-    if not args.skip_isolated:
-        extra["gemv_m1_isolated_607MB"] = gemv_isolated(torch, qk, workloads)
+    if not args.skip_configs:
+        extra["copy_ceiling_1gib"] = copy_ceiling(torch)
+        extra["config_single_1024"] = single_1024_us(torch, qk, workloads)
+        extra["config_llama7b_gemv_rotating"] = gemv_rotating(torch, qk, workloads)
+        extra["config_llama70b_stack"] = llama70b_stack(torch, qk, workloads)
+        extra["config_edge_3000x4099"] = edge_us(torch, qk, workloads)
+        extra["shader_clock"] = shader_clock(torch, qk, lambda: run_step(calls))
 
     if not args.skip_rows:
         extra["lora_merge"] = merge_rate(torch, qk, wl)
@@ -669,7 +905,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--skip-isolated", action="store_true", help="skip the isolated GEMV HBM measurement")
+    ap.add_argument("--skip-configs", action="store_true",
+                    help="skip the other workloads (1024^2 weight, 7B GEMV rotating set, 70B stack, edge set)")
     ap.add_argument("--skip-rows", action="store_true",
                     help="skip the timings of the merge, backward, 8-bit state and LLM.int8 calls")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB device copy")
