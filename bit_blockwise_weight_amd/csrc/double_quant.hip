@@ -16,10 +16,13 @@
 //     exactly the tree's left and right subtrees), then the 4 waves pairwise.
 //     Applied until at most 4096 partials remain.  An aligned chunk of a
 //     power-of-two size is a subtree of the global tree, so the result is the
-//     tree sum bit for bit.
+//     tree sum bit for bit.  The fp32 level reads 16 bytes per load from a
+//     buffer range that ends at the array (the zero padding comes from the
+//     range check).
 //   dq_quantize: every workgroup first re-derives the mean from the final
-//     partials (the same tree, at most 32 KB read from L2), then each wave
-//     quantizes one block of 256 absmax (4 per lane).
+//     partials (the same tree, at most 32 KB read from L2), then each of its 4
+//     waves quantizes 4 blocks of 256 absmax (4 per lane), their loads issued
+//     together.
 #include "qk_internal.h"
 #include "qk_device.h"
 
@@ -58,6 +61,34 @@ __device__ __forceinline__ double chunk_tree(double (&a)[kPerThread], double* re
     return r;
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dq_rsrc(const void* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int32_t)bytes, 0x00020000);
+}
+
+// First level over the fp32 absmax: thread t of the workgroup holds values [16 t, 16 t + 16)
+// of the chunk, read with four 16-byte loads from a buffer whose range ends at the array's
+// end (values past it read as zero: the tree's zero padding).  The 4-byte alignment of the
+// array is enough for these loads.
+__global__ __launch_bounds__(kThreads) void tree_partials_f32(const float* __restrict__ in, int64_t count,
+                                                              double* __restrict__ out) {
+    __shared__ double red[kThreads / kWave];
+    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+    const int64_t rem = count - c0;
+    const __amdgpu_buffer_rsrc_t r = dq_rsrc(in + c0, 4 * (rem < kChunk ? rem : kChunk));
+    double a[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread / 4; ++j) {
+        const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        r, (uint32_t)(threadIdx.x * kPerThread * 4 + 16 * j), 0, 0));
+        a[4 * j] = (double)v.x;
+        a[4 * j + 1] = (double)v.y;
+        a[4 * j + 2] = (double)v.z;
+        a[4 * j + 3] = (double)v.w;
+    }
+    const double s = chunk_tree(a, red);
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void tree_partials(const T* __restrict__ in, int64_t count,
                                                           double* __restrict__ out) {
@@ -71,7 +102,8 @@ __global__ __launch_bounds__(kThreads) void tree_partials(const T* __restrict__ 
 }
 
 constexpr int kDqBlock = QK_DQ_BLOCK;           // 256 absmax per scale
-constexpr int kDqBlocksPerWg = kThreads / kWave; // one block per wave
+constexpr int kDqPerWave = 4;                    // dq blocks a wave quantizes
+constexpr int kDqBlocksPerWg = kThreads / kWave * kDqPerWave;
 
 __global__ __launch_bounds__(kThreads) void dq_quantize(const float* __restrict__ absmax, int64_t nb,
                                                         const double* __restrict__ partials, int64_t npart,
@@ -79,12 +111,18 @@ __global__ __launch_bounds__(kThreads) void dq_quantize(const float* __restrict_
                                                         float* __restrict__ mean_out) {
     __shared__ double red[kThreads / kWave];
     __shared__ float mean_sh;
-    // mean from the final partials (npart <= 4096), same tree as the partial kernel
+    // mean from the final partials (npart <= 4096), same tree as the partial kernel; eight
+    // 16-byte loads per thread, partials past npart read as zero
     {
-        const int64_t base = (int64_t)threadIdx.x * kPerThread;
+        const __amdgpu_buffer_rsrc_t pr = dq_rsrc(partials, 8 * npart);
         double a[kPerThread];
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) a[i] = (base + i < npart) ? partials[base + i] : 0.0;
+        for (int j = 0; j < kPerThread / 2; ++j) {
+            const double2 v = __builtin_bit_cast(double2, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              pr, (uint32_t)(threadIdx.x * kPerThread * 8 + 16 * j), 0, 0));
+            a[2 * j] = v.x;
+            a[2 * j + 1] = v.y;
+        }
         const double total = chunk_tree(a, red);
         if (threadIdx.x == 0) {
             const float mu = (float)(total / (double)nb);
@@ -95,37 +133,52 @@ __global__ __launch_bounds__(kThreads) void dq_quantize(const float* __restrict_
     }
     const float mu = mean_sh;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t d = (int64_t)blockIdx.x * kDqBlocksPerWg + threadIdx.x / kWave;
     const int64_t nd = (nb + kDqBlock - 1) / kDqBlock;
-    if (d >= nd) return;
-    const int64_t base = d * kDqBlock + lane * 4;
-    float c[4];
-    float m = 0.0f;
+    // this wave's kDqPerWave blocks: one 16-byte load per lane and block, all issued first
+    // (the buffer ends at the array's end; values past it are masked below)
+    const int64_t d0 = (int64_t)blockIdx.x * kDqBlocksPerWg + (threadIdx.x / kWave) * kDqPerWave;
+    if (d0 >= nd) return;
+    const int64_t e0 = d0 * kDqBlock;
+    const int64_t rem = nb - e0;
+    const __amdgpu_buffer_rsrc_t ar = dq_rsrc(absmax + e0, 4 * (rem < kDqPerWave * kDqBlock ? rem : kDqPerWave * kDqBlock));
+    float4 av[kDqPerWave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        c[i] = (base + i < nb) ? __fsub_rn(absmax[base + i], mu) : 0.0f;
-        m = fmaxf(m, fabsf(c[i]));
-    }
-    m = group_max<32>(m);
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    uint32_t word = 0;
+    for (int k = 0; k < kDqPerWave; ++k)
+        av[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ar, (uint32_t)(k * kDqBlock * 4 + 16 * lane), 0, 0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int q = 0;
-        if (m != 0.0f) {
-            const float ratio = c[i] / m;                      // IEEE division
-            q = (int)__builtin_rintf(__fmul_rn(ratio, 127.0f));
+    for (int k = 0; k < kDqPerWave; ++k) {
+        const int64_t d = d0 + k;
+        if (d >= nd) break;
+        const int64_t base = d * kDqBlock + lane * 4;
+        const float avk[4] = {av[k].x, av[k].y, av[k].z, av[k].w};
+        float c[4];
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[i] = (base + i < nb) ? __fsub_rn(avk[i], mu) : 0.0f;
+            m = fmaxf(m, fabsf(c[i]));
         }
-        word |= ((uint32_t)(q & 0xFF)) << (8 * i);
-    }
-    if (base + 4 <= nb) {
-        *reinterpret_cast<uint32_t*>(q8 + base) = word;
-    } else {
+        m = group_max<32>(m);
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        uint32_t word = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (base + i < nb) q8[base + i] = (int8_t)((word >> (8 * i)) & 0xFF);
+        for (int i = 0; i < 4; ++i) {
+            int q = 0;
+            if (m != 0.0f) {
+                const float ratio = c[i] / m;                      // IEEE division
+                q = (int)__builtin_rintf(__fmul_rn(ratio, 127.0f));
+            }
+            word |= ((uint32_t)(q & 0xFF)) << (8 * i);
+        }
+        if (base + 4 <= nb) {
+            *reinterpret_cast<uint32_t*>(q8 + base) = word;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (base + i < nb) q8[base + i] = (int8_t)((word >> (8 * i)) & 0xFF);
+        }
+        if (lane == 0) scale[d] = m / 127.0f;
     }
-    if (lane == 0) scale[d] = m / 127.0f;
 }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -147,7 +200,7 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int8_t* q8,
                                void* workspace, hipStream_t s) {
     double* ws = reinterpret_cast<double*>(workspace);
     int64_t cnt = cdiv(nblocks, kChunk);
-    hipLaunchKernelGGL(tree_partials<float>, dim3((unsigned)cnt), dim3(kThreads), 0, s, absmax, nblocks, ws);
+    hipLaunchKernelGGL(tree_partials_f32, dim3((unsigned)cnt), dim3(kThreads), 0, s, absmax, nblocks, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     double* cur = ws;
