@@ -179,8 +179,11 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
         const void* x;
         const void* sc;
         const void* dq_scale;
-        uint32_t crow[4];          // code offset of row 4 i + lane / 16 and this lane's piece
-        uint32_t qrow;             // scale index of the first block of row n
+        uint32_t crow[4];          // code offset of tile row 4 i + lane / 16 and this lane's piece (per slice)
+        uint32_t qrow;             // scale index of tile row n's first block, from the tile's first (per slice)
+        uint32_t qbase;            // scale index of the slice's first block
+        uint32_t tcode;            // code offset of the tile's first row (per tile, uniform)
+        uint32_t tq;               // scale index of the tile's first block (per tile, uniform)
     };
     struct CompCur {
         int32_t item, task, j, jobs;
@@ -204,21 +207,23 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
         c.x = T.x;
         c.sc = T.sc;
         c.dq_scale = T.dq_scale;
-    };
-    // rows past the slice's end are clamped to its last row (valid memory, never stored)
-    auto enter_tile = [&](LoadCur& c) {
-        const GemvTask& T = g.t[c.task];
-        const int32_t N = (int32_t)T.N;
-        const int32_t n0 = (c.item - c.item0) * 16;
-        const uint32_t row_bytes = (uint32_t)(c.K / 2);
+        // lane offsets relative to a tile's first row: they change only with the slice
+        const uint32_t row_bytes = (uint32_t)(T.K / 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 4 * i + (lane >> 4);
-            const int32_t gr = n0 + r < N ? n0 + r : N - 1;
-            c.crow[i] = (uint32_t)gr * row_bytes + 16u * (uint32_t)((lane & 15) ^ r);
+            c.crow[i] = (uint32_t)r * row_bytes + 16u * (uint32_t)((lane & 15) ^ r);
         }
-        const int32_t rowc = n0 + n < N ? n0 + n : N - 1;
-        c.qrow = (uint32_t)T.qbase + (uint32_t)rowc * (uint32_t)(c.K >> (QS + 6));
+        c.qrow = (uint32_t)n * (uint32_t)(T.K >> (QS + 6));
+        c.qbase = (uint32_t)T.qbase;
+    };
+    // the tile's first row enters the loads' scalar offsets; rows past the slice's end
+    // then lie past the code buffer's range and read zero (their outputs are never
+    // stored), and their scales are other rows' or zero
+    auto enter_tile = [&](LoadCur& c) {
+        const uint32_t n0 = (uint32_t)(c.item - c.item0) * 16u;
+        c.tcode = n0 * (uint32_t)(c.K / 2);
+        c.tq = c.qbase + n0 * (uint32_t)(c.K >> (QS + 6));
     };
     auto set_comp_task = [&](CompCur& c, int32_t t) {
         c.task = t;
@@ -268,17 +273,20 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
         // depends on the template, makes host compilation drop the kernel's launch stub)
         const int32_t K = c.K;
         const uint32_t qrow = c.qrow;
+        const uint32_t tcode = c.tcode;
+        const uint32_t tq = c.tq;
         const uint32_t crow[4] = {c.crow[0], c.crow[1], c.crow[2], c.crow[3]};
         const int32_t ch = c.j * S + wave;
         const bool live = ch < c.nchunk;                 // an idle wave's chunk: x reads zero
         const int32_t chc = live ? ch : c.nchunk - 1;
         // the job's quantization blocks of row n are consecutive from qf on
-        const uint32_t qf = qrow + (uint32_t)(chc * kJobQ);
+        const uint32_t qs0 = tq + (uint32_t)(chc * kJobQ);   // uniform part of the scale index
+        const uint32_t qf = qrow + qs0;
         if constexpr (kNested) {
             if constexpr (kAligned) {
                 // the job's kJobQ q8 bytes start at a multiple of kJobQ (8, 4 or 2)
                 if constexpr (QS == 0)
-                    jr.q.xy = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(lsr, qrow, (uint32_t)(chc * kJobQ), 0));
+                    jr.q.xy = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(lsr, qrow, qs0, 0));
                 else
                     jr.q.x = __builtin_amdgcn_raw_buffer_load_b32(lsr, qf & ~3u, 0, 0);
                 if constexpr (QS == 2) jr.qinfo = qf & 3u;
@@ -290,9 +298,9 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
             }
         } else {
             if constexpr (kAligned) {
-                jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, (uint32_t)(chc * kJobQ * 4), 0));
+                jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, qs0 * 4u, 0));
                 if constexpr (QS == 0)
-                    jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, (uint32_t)(chc * kJobQ * 4 + 16), 0));
+                    jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, qs0 * 4u + 16u, 0));
             } else {
                 jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qf * 4u, 0, 0));
                 if constexpr (QS == 0)
@@ -307,7 +315,7 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(lcr, (lds_ptr_t)(cdst + i * 1024), 16, crow[i],
-                                                         (uint32_t)chc * (kChunkK / 2), 0, 0);
+                                                         tcode + (uint32_t)chc * (kChunkK / 2), 0, 0);
         } else {
             // pieces past the end of a row, in a partial chunk, are clamped to the row's last
             // 16 bytes (their x is zero); the offset stays in the range-checked vector part
@@ -319,7 +327,7 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
                 const uint32_t piece = 16u * (uint32_t)((lane & 15) ^ r);
                 const uint32_t within = cofs + piece + 16u <= row_bytes ? cofs : row_bytes - 16u - piece;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(lcr, (lds_ptr_t)(cdst + i * 1024), 16, crow[i] + within,
-                                                         0, 0, 0);
+                                                         tcode, 0, 0);
             }
         }
         // x rows m < MX of the job's k, 16 bytes per lane: unit L of row m lands in slot unit
@@ -896,8 +904,17 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
     for (size_t f = 0; f < order.size(); ++f) {
         if (used[order[f]]) continue;
         const DeqArgs& w0 = *slice_w[order[f]];
-        // rows that are whole jobs take the kernel whose scales are one aligned run per job
-        const bool aligned = slices[order[f]].K % kChunkK == 0;
+        // rows that are whole jobs take the kernel whose scales are one aligned run per job;
+        // a weight whose rows are not puts the whole group on the general variant rather
+        // than costing a launch of its own
+        bool aligned = true;
+        for (size_t f2 = f; f2 < order.size(); ++f2) {
+            const size_t k = order[f2];
+            const DeqArgs& w = *slice_w[k];
+            if (!used[k] && w.nested == w0.nested && w.blocksize == w0.blocksize &&
+                std::memcmp(w.levels, w0.levels, sizeof(w.levels)) == 0 && slices[k].K % kChunkK != 0)
+                aligned = false;
+        }
         GemvGroup gg;
         std::memset(&gg, 0, sizeof(gg));
         std::memcpy(gg.levels, w0.levels, sizeof(gg.levels));
@@ -907,9 +924,11 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
             const size_t k = order[f2];
             if (used[k]) continue;
             const DeqArgs& w = *slice_w[k];
-            if (w.nested != w0.nested || w.blocksize != w0.blocksize || (slices[k].K % kChunkK == 0) != aligned ||
+            if (w.nested != w0.nested || w.blocksize != w0.blocksize ||
                 std::memcmp(w.levels, w0.levels, sizeof(w.levels)) != 0)
                 continue;
+            // an aligned launch takes only weights whose rows are whole jobs
+            if (aligned && slices[k].K % kChunkK != 0) continue;
             const int64_t tiles = (slices[k].N + 15) / 16;
             const int64_t units = rows ? (tiles + S - 1) / S : tiles;   // row-split: groups of S tiles
             if (nitems + units > max_tiles) continue;
