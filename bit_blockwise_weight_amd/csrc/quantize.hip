@@ -17,14 +17,16 @@
 // the compiler's wait leaves the next unit's load outstanding); the partial last
 // unit, if any, is done after the loop by one wave with per-element loads.
 //
-// Division.  For bf16 and fp16 inputs t = RN(x/a) is computed from one IEEE
-// reciprocal per block and Markstein's correction
+// Division.  For bf16 and fp16 inputs t = RN(x/a) is computed from one
+// reciprocal per block, r = RN(1/a), and Markstein's correction
 //     q0 = x*r,  e = fma(-q0, a, x),  t = fma(e, r, q0),
 // which equals the IEEE quotient bit for bit whenever 2^-36 <= a <= 2^64 and
-// |x| >= a*2^-64 (checked exhaustively over every bf16 and every fp16 pair by
-// the CPU test of the division).  Any lane holding an element outside that
-// region redoes its 8 divisions with the IEEE sequence; fp32 inputs always use
-// it.
+// |x| >= a*2^-64.  r itself is the hardware's approximate reciprocal y refined
+// once, r = fma(fma(-a, y, 1), y, y).  Both steps are checked exhaustively over
+// every bf16 and every fp16 value by the CPU test of the division (the
+// reciprocal for every y within 2 ulp of 1/a).  Any lane holding an element
+// outside that region redoes its 8 divisions with the IEEE sequence; fp32 inputs
+// always use it.
 //
 // Nearest level.  t is binned by the low 24 bits of fmaf(t, S, S + 2^23); each
 // bin of the LDS table holds at most one threshold T and the codes below and
@@ -115,7 +117,12 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
         bool ok = false;
         if constexpr (kFastDiv) {
             const bool fast_block = am >= kAMin && am <= kAMax;
-            const float r = 1.0f / (fast_block ? am : 1.0f);
+            // RN(1/a): the hardware reciprocal (within 1 ulp) and one correction step,
+            // exact for every bf16 and fp16 a of the fast region (CPU-checked, with a 2 ulp
+            // margin on the hardware's error)
+            const float ab = fast_block ? am : 1.0f;
+            const float r0 = __builtin_amdgcn_rcpf(ab);
+            const float r = __builtin_fmaf(__builtin_fmaf(-ab, r0, 1.0f), r0, r0);
             const float x_lo = fast_block ? am * kXRel : __builtin_inff();
             ok = mn >= x_lo;
 #pragma unroll
@@ -129,14 +136,22 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
             const float a_div = am == 0.0f ? 1.0f : am;   // zero block: x is +-0, t = +-0
 #pragma unroll
             for (int i = 0; i < 8; ++i) t[i] = v[i] / a_div;
+            if constexpr (kFastDiv) {
+                // finite input gives |t| <= 1; a non-finite block (outside the contract) is
+                // the only way here to anything else, and it maps to 0, so the table read
+                // below needs no clamp (the fast path never sees a non-finite absmax)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[i] = __builtin_fabsf(t[i]) <= 1.0f ? t[i] : 0.0f;
+            }
         }
 
         uint32_t word = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            // |t| <= 1 gives the pattern 0x4B000000 + bin, bin in [0, 2S]; the min only
-            // matters for non-finite input (outside the contract) and keeps the read in the table
-            const uint32_t bin = min(as_uint(__builtin_fmaf(t[i], S, C)), bin_cap);
+            // |t| <= 1 gives the pattern 0x4B000000 + bin, bin in [0, 2S]; for fp32 input the
+            // min keeps a non-finite t (outside the contract) inside the table
+            uint32_t bin = as_uint(__builtin_fmaf(t[i], S, C));
+            if constexpr (!kFastDiv) bin = min(bin, bin_cap);
             const uint32_t addr = __umul24(bin, kBinStride) + lane_off;
             const uint2 ent = *reinterpret_cast<const uint2*>(lds_bytes + addr);
             uint32_t code;
@@ -150,8 +165,11 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const void* __restr
         }
 
         if constexpr (!kTail) {
-            *reinterpret_cast<uint32_t*>(codes + base / 2) = word;
-            if ((lane % G) == 0) absmax[base / B] = am;
+            // the unit's bases are uniform: the stores take a scalar base and a lane offset
+            uint8_t* cu = codes + unit * (kUnitElems / 2);
+            float* au = absmax + unit * (kUnitElems / B);
+            *reinterpret_cast<uint32_t*>(cu + 4 * lane) = word;
+            if ((lane % G) == 0) au[lane / G] = am;
         } else {
             if (base < n) {
                 if (base + 8 <= n) {

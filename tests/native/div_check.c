@@ -18,7 +18,14 @@
  * residual e can underflow or the quotient is subnormal and the step is not
  * exact, which is why the kernel falls back there.
  *
- * usage: div_check bf16|fp16      prints "pairs P fast F mismatches M"; exit 0 iff M == 0
+ * The reciprocal itself is not an IEEE division in the kernel: it is the
+ * hardware's approximate reciprocal y (within 1 ulp of 1/a) refined by one
+ * correction step, r = RN(y + RN(1 - a*y)*y) with two fused multiply-adds.  For
+ * every a of the fast region and every binary32 y within 2 ulp of 1/a (twice the
+ * hardware's error bound) the program checks r == RN(1/a) first.
+ *
+ * usage: div_check bf16|fp16      prints "recips R recip_mismatches M1" and
+ *                                 "pairs P fast F mismatches M"; exit 0 iff M1 == M == 0
  */
 #include <math.h>
 #include <stdint.h>
@@ -41,7 +48,26 @@ int main(int argc, char** argv) {
     int is_bf16 = !(argc > 1 && strcmp(argv[1], "fp16") == 0);
     uint32_t top = is_bf16 ? 0x7F7F : 0x7BFF;   /* largest finite positive pattern */
     const float a_lo = ldexpf(1.0f, A_MIN_EXP), a_hi = ldexpf(1.0f, A_MAX_EXP);
-    unsigned long long pairs = 0, fast = 0, bad = 0;
+    unsigned long long pairs = 0, fast = 0, bad = 0, recips = 0, rbad = 0;
+    for (uint32_t ab = 1; ab <= top; ++ab) {
+        float a = is_bf16 ? bf16_to_f((uint16_t)ab) : fp16_to_f((uint16_t)ab);
+        if (!(a >= a_lo && a <= a_hi)) continue;
+        volatile float one = 1.0f;
+        const float rn = one / a;
+        const double inv = 1.0 / (double)a;
+        const double ulp = (double)nextafterf(rn, INFINITY) - (double)rn;
+        float y = nextafterf(nextafterf(nextafterf(rn, 0.0f), 0.0f), 0.0f);
+        for (int k = 0; k < 7; ++k, y = nextafterf(y, INFINITY)) {
+            if (fabs((double)y - inv) > 2.0 * ulp) continue;
+            ++recips;
+            const float r = fmaf(fmaf(-a, y, 1.0f), y, y);
+            if (memcmp(&r, &rn, 4) != 0) {
+                if (rbad < 10) printf("reciprocal mismatch a=%a y=%a got=%a want=%a\n", a, y, r, rn);
+                ++rbad;
+            }
+        }
+    }
+    printf("recips %llu recip_mismatches %llu\n", recips, rbad);
     for (uint32_t ab = 1; ab <= top; ++ab) {
         float a = is_bf16 ? bf16_to_f((uint16_t)ab) : fp16_to_f((uint16_t)ab);
         int block_fast = a >= a_lo && a <= a_hi;
@@ -67,5 +93,5 @@ int main(int argc, char** argv) {
         }
     }
     printf("pairs %llu fast %llu mismatches %llu\n", pairs, fast, bad);
-    return bad != 0;
+    return bad != 0 || rbad != 0;
 }

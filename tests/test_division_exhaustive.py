@@ -1,8 +1,10 @@
-"""Exhaustive CPU proof that the quantize kernel's fast division (one correctly
-rounded reciprocal per block plus Markstein's fused-multiply-add correction)
-returns the IEEE quotient RN(x/a) for every bf16 and every fp16 pair inside the
-region where the kernel uses it (see tests/native/div_check.c).  The kernel
-divides every other element with the full IEEE sequence."""
+"""Exhaustive CPU proof that the quantize kernel's fast division returns the IEEE
+quotient RN(x/a) for every bf16 and every fp16 pair inside the region where the
+kernel uses it (see tests/native/div_check.c): the per-block reciprocal (the
+hardware's approximate reciprocal refined by one fused-multiply-add step) is
+RN(1/a) for every approximation within 2 ulp, and Markstein's correction then
+gives the quotient.  The kernel divides every other element with the full IEEE
+sequence."""
 
 import os
 import shutil
@@ -28,6 +30,10 @@ def checker(tmp_path_factory):
 def test_fast_division_is_exact(checker, fmt):
     res = subprocess.run([checker, fmt], capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stdout + res.stderr
-    last = res.stdout.strip().splitlines()[-1].split()
+    lines = res.stdout.strip().splitlines()
+    rec = lines[-2].split()
+    assert rec[0] == "recips" and rec[-1] == "0"
+    assert int(rec[1]) > (20_000 if fmt == "bf16" else 50_000)   # every absmax of the fast region, 2-3 each
+    last = lines[-1].split()
     assert last[0] == "pairs" and last[-1] == "0"
     assert int(last[3]) > 200_000_000          # the fast region is the bulk of the pairs
