@@ -31,7 +31,11 @@ M = 512) and the shader clock under load.
 
 Other modes:
   --copy-calibration          run a plain 1 GiB device copy (for HBM counter scaling)
-  --summarize-pmc DIR KERNEL  summarize rocprofv3 --pmc output of FETCH_SIZE / WRITE_SIZE
+  --profile WORKLOAD          run one workload a few times under a profiler
+  --summarize-counters D.. O  per-kernel counter averages of rocprofv3 --pmc csv output
+                              (--workload W, --trace-dir D for durations)
+  --summarize-trace D O       summarize rocprofv3 --kernel-trace --stats csv output
+  --summarize-pmc F W CF CW O HBM traffic of the GEMM from FETCH_SIZE / WRITE_SIZE runs
 """
 
 import argparse
@@ -899,6 +903,184 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path
     return 0
 
 
+# ----------------------------------------------------------------- profiling drivers
+
+PROFILE_WORKLOADS = {
+    # name: description (per-dispatch element counts for the derived figures come from
+    # profile_elements below)
+    "llama70b-quantize": "quantize (NF4, block 64) + double quant of the 7 weights of one 70B-shaped layer, 3 passes",
+    "llama70b-gemv": "grouped GEMV over two 70B-shaped layers (7 weights each, one launch per layer), "
+                     "M = 1, 4, 8, 3 passes each",
+    "llama7b-gemv": "grouped GEMV over two Llama-7B layer sets (7 weights, one launch per layer), "
+                    "M = 1 and 16, 3 passes each",
+    "qlora-gemm": "QLoRA prefill GEMM X [4096, 4096] x NF4 W [N, 4096] + LoRA r = 16 (s = 2), N = 4096 and "
+                  "11008, 3 calls each",
+}
+
+
+def profile_elements(workload):
+    """Weight elements one dispatch of each main kernel covers, averaged over the
+    workload's dispatches: {kernel name prefix: (elements, algorithmic bytes per element)}."""
+    import workloads
+    if workload == "llama70b-quantize":
+        n = sum(N * K for _, N, K in workloads.LLAMA70B_LAYER_SHAPES) / len(workloads.LLAMA70B_LAYER_SHAPES)
+        # bf16 in, a nibble and a 64th of an fp32 absmax out
+        return {"quantize_kernel": (n, 2 + 0.5 + 4 / 64)}
+    if workload in ("llama70b-gemv", "llama7b-gemv"):
+        shapes = workloads.LLAMA70B_LAYER_SHAPES if workload == "llama70b-gemv" else workloads.LLAMA7B_SHAPES
+        n = sum(N * K for _, N, K in shapes)
+        # a nibble and a 64th of an int8 absmax code per element (x and y are negligible)
+        return {"gemv_": (n, 0.5 + 1 / 64)}
+    return {}
+
+
+def profile_workload(name):
+    """Runs one workload a few times (for rocprofv3 traces and counters)."""
+    import torch
+    import bit_blockwise_weight_amd as qk
+    import workloads
+    qk.lib()
+    dev = torch.device("cuda:0")
+    if name == "llama70b-quantize":
+        lv = qk.qk_make_codebook(qk.NF4)
+        lvc = (ctypes.c_float * 16)(*lv.tolist())
+        mats = []
+        for i, (_, N, K) in enumerate(workloads.LLAMA70B_LAYER_SHAPES):
+            n = N * K
+            nb = nblk(n, 64)
+            mats.append({"w": workloads.device_normal_bf16((N, K), 0.015, workloads.llama70b_seed(0, i)),
+                         "codes": torch.empty(n // 2, dtype=torch.uint8, device=dev),
+                         "absmax": torch.empty(nb, dtype=torch.float32, device=dev),
+                         "q8": torch.empty(nb, dtype=torch.int8, device=dev),
+                         "scale": torch.empty(nblk(nb, 256), dtype=torch.float32, device=dev),
+                         "mean": torch.empty(1, dtype=torch.float32, device=dev),
+                         "ws": torch.empty(max(8, qk.qk_double_quant_workspace_size(nb)), dtype=torch.uint8,
+                                           device=dev)})
+        for _ in range(3):
+            for m in mats:
+                qk.qk_quantize_blockwise(m["w"], 64, lvc, m["codes"], m["absmax"])
+                qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])
+    elif name in ("llama70b-gemv", "llama7b-gemv"):
+        shapes = workloads.LLAMA70B_LAYER_SHAPES if name == "llama70b-gemv" else workloads.LLAMA7B_SHAPES
+        std = 0.015 if name == "llama70b-gemv" else 0.02
+        layers = []
+        for l in range(2):
+            lay = []
+            for i, (_, N, K) in enumerate(shapes):
+                w = workloads.device_normal_bf16((N, K), std, 9_000_000 + 101 * l + i)
+                lay.append((qk.quantize(w, 64, qk.NF4, True), N, K))
+                del w
+            layers.append(lay)
+        torch.cuda.empty_cache()
+        for M in ((1, 4, 8) if name == "llama70b-gemv" else (1, 16)):
+            xs = {K: torch.randn((M, K), device=dev).to(torch.bfloat16) for K in set(K for _, _, K in shapes)}
+            ys = [[torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N, _ in lay] for lay in layers]
+            for _ in range(3):
+                for lay, y in zip(layers, ys):
+                    qk.qk_gemv_nf4_grouped([(xs[K], qw.state) for qw, _, K in lay], y)
+    elif name == "qlora-gemm":
+        for N in (4096, 11008):
+            X, W, A, B = workloads.qlora_prefill(N)
+            t = lambda b, shp: torch.from_numpy(b.view("int16")).view(torch.bfloat16).cuda().reshape(shp)
+            Xd, Wd, Ad, Bd = t(X, (4096, 4096)), t(W, (N, 4096)), t(A, (4096, 16)), t(B, (16, N))
+            qw = qk.quantize(Wd, 64, qk.NF4, True)
+            ws = torch.empty(qk.qk_gemm_nf4_workspace_size(4096, 16), dtype=torch.uint8, device=dev)
+            Y = torch.empty((4096, N), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                qk.qk_gemm_nf4(Xd, qw.state, Ad, Bd, 2.0, Y, ws)
+    else:
+        print(f"unknown workload {name}; one of {sorted(PROFILE_WORKLOADS)}", file=sys.stderr)
+        return 2
+    torch.cuda.synchronize()
+    print(f"profiled workload {name}: {PROFILE_WORKLOADS[name]}", flush=True)
+    return 0
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"([A-Za-z0-9_]+(?:<[^()]*>)?)\(", name)
+    base = m.group(1) if m else name[:60]
+    return base.replace("qk::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+
+
+def summarize_counters(dirs, out_path, command, workload="", trace_dir=None):
+    """Per-kernel averages (per dispatch) of the counters in rocprofv3 --pmc csv output
+    directories, for the library's kernels, with derived figures.  Kernel cycles are
+    SQ_BUSY_CYCLES / 32 (the counter sums over the 32 shader engines, 4 per XCD); the
+    matrix cores are busy SQ_VALU_MFMA_BUSY_CYCLES out of 1024 SIMDs x kernel cycles;
+    SQ_INSTS_VALU counts wave64 instructions.  With a kernel-trace directory of the
+    same workload the average durations give the clock and the achieved rate."""
+    vals = {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if "qk::" not in r["Kernel_Name"]:
+                continue
+            k = _short_kernel(r["Kernel_Name"])
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], {}).setdefault(r.get("Dispatch_Id", "0"), 0.0)
+            vals[k][r["Counter_Name"]][r.get("Dispatch_Id", "0")] += float(r["Counter_Value"])
+    if not vals:
+        print("no counters found", file=sys.stderr)
+        return 1
+    durations = {}
+    if trace_dir:
+        for r in _csv_rows(trace_dir, "kernel_stats.csv"):
+            durations[_short_kernel(r["Name"])] = float(r["AverageNs"]) * 1e-9
+    elems = profile_elements(workload)
+    lines = ["# rocprofv3 counters" + (f": {workload}" if workload else ""), ""]
+    if workload in PROFILE_WORKLOADS:
+        lines += [f"Workload: {PROFILE_WORKLOADS[workload]}.", ""]
+    lines += ["Commands (one counter pass each; the durations come from a --kernel-trace run of the same "
+              "workload):", "", "```", command, "```", "",
+              "Per-dispatch averages over the kernel's dispatches, summed over the chip.  Kernel cycles = "
+              "SQ_BUSY_CYCLES / 32 shader engines; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x "
+              "kernel cycles); CU busy = SQ_BUSY_CU_CYCLES / (256 CUs x kernel cycles); VALU = SQ_INSTS_VALU "
+              "(wave64 instructions).", ""]
+    for k in sorted(vals):
+        cs = vals[k]
+        avg = {c: sum(v.values()) / max(1, len(v)) for c, v in cs.items()}
+        nd = max(len(v) for v in cs.values())
+        lines.append(f"## `{k}` ({nd} dispatches)")
+        lines.append("")
+        lines.append("| Counter | Per dispatch |")
+        lines.append("|---|---|")
+        for c in sorted(avg):
+            lines.append(f"| {c} | {avg[c]:.4g} |")
+        derived = []
+        cyc = avg.get("SQ_BUSY_CYCLES", 0.0) / 32
+        if cyc > 0:
+            derived.append(f"kernel cycles = {cyc:.4g}")
+            dur = durations.get(k)
+            if dur:
+                derived.append(f"average duration {dur * 1e6:.2f} us, so the shader clock ran at "
+                               f"{cyc / dur / 1e9:.2f} GHz")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                derived.append(f"MFMA busy = {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * cyc):.3f} of the "
+                               f"SIMD cycles")
+            if "SQ_BUSY_CU_CYCLES" in avg:
+                derived.append(f"CU busy = {avg['SQ_BUSY_CU_CYCLES'] / (256 * cyc):.3f}")
+            if "SQ_ACTIVE_INST_VALU" in avg:
+                # a wave64 VALU instruction holds its SIMD for 4 cycles (1 per cycle per CU)
+                derived.append(f"VALU issue = {avg['SQ_INSTS_VALU'] / (256 * cyc):.3f} of the CU cycles "
+                               f"(one wave64 VALU instruction per CU per cycle at most)")
+        for prefix, (n, bpe) in elems.items():
+            if k.startswith(prefix) or prefix in k:
+                if "SQ_INSTS_VALU" in avg:
+                    derived.append(f"VALU per element = {avg['SQ_INSTS_VALU'] * 64 / n:.2f} lane instructions "
+                                   f"({n:.4g} weight elements per dispatch)")
+                dur = durations.get(k)
+                if dur:
+                    derived.append(f"achieved {n * bpe / dur / 1e12:.2f} TB/s of algorithmic bytes "
+                                   f"({bpe:.4g} B per element)")
+        if derived:
+            lines.append("")
+            lines += [f"- {d}" for d in derived]
+        lines.append("")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out_path}")
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -915,7 +1097,18 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT"),
                     help="GEMM HBM traffic per dispatch from rocprofv3 --pmc runs")
     ap.add_argument("--command", default="", help="the command recorded in a summary")
+    ap.add_argument("--profile", metavar="WORKLOAD", help="run one workload a few times (for rocprofv3): "
+                    + ", ".join(sorted(PROFILE_WORKLOADS)))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR_OR_OUT",
+                    help="DIR [DIR ...] OUT: per-kernel counter averages of rocprofv3 --pmc csv output")
+    ap.add_argument("--workload", default="", help="the workload a counter summary covers")
+    ap.add_argument("--trace-dir", default=None, help="kernel-trace output of the same workload (durations)")
     args = ap.parse_args()
+    if args.profile:
+        return profile_workload(args.profile)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1], args.command,
+                                  args.workload, args.trace_dir)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command)
     if args.summarize_pmc:
