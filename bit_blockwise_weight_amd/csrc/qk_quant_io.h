@@ -51,14 +51,22 @@ __device__ __forceinline__ void load_raw(const void* x, int64_t n, int64_t base,
 
 // The same for a lane whose 8 elements are known to be in range: no branch, so the
 // compiler can leave the load in flight across unrelated code.
+// The loads are nontemporal: the input is streamed once.
+typedef unsigned int u32x4_stream_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+    const u32x4_stream_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_stream_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T>
 __device__ __forceinline__ void load_raw_full(const void* x, int64_t base, typename RawOf<T>::type& r) {
     if constexpr (__is_same(T, F32In)) {
-        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + base);
-        r[0] = p[0];
-        r[1] = p[1];
+        const float* p = reinterpret_cast<const float*>(x) + base;
+        r[0] = stream_load16(p);
+        r[1] = stream_load16(p + 4);
     } else {
-        r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
+        r = stream_load16(reinterpret_cast<const uint16_t*>(x) + base);
     }
 }
 
