@@ -538,6 +538,20 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     }
 }
 
+// Swizzle of staged x row m in the row-split kernel.  A fragment read takes unit 8 b + 2 h
+// + t of row min(n, M - 1) in lane (n, h); a 16-byte unit covers 4 of the 64 banks, so a
+// row's units fall in 16 bank groups.  With up to 8 staged rows, bit 0 of m stays and
+// bits 1 and 2 move to bits 2 and 3, so xswz(m) is in {0, 1, 4, 5, 8, 9, 12, 13}: the two
+// h of a half wave (2 h in {0, 2} or {4, 6}) then reach 16 distinct groups, and the
+// counters show no bank conflict at M = 4 and 8, where the plain m swizzle (which pairs
+// row m of h with row m ^ 2 of h + 1) measured 0.7 conflict cycles per LDS instruction.
+// With 16 staged rows the plain m swizzle measured no conflict and is kept.
+template <int MX>
+__device__ __forceinline__ int xswz(int m) {
+    if constexpr (MX > 8) return m & 15;
+    else return (m & 1) | ((m & 2) << 1) | ((m & 4) << 1);
+}
+
 // Row-split kernel for M >= 2 rows of x: each wave owns whole 16-row tiles and walks the
 // row from k = 0 to K in 512-k jobs; the S waves of a workgroup own S consecutive tiles of
 // one slice (a "group", one workgroup each, launched longest rows first so the hardware
@@ -548,9 +562,8 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
 // The codes and scales of a job are loaded two jobs ahead into the wave's own LDS slot
 // and registers (as in the K-split kernel); the x chunk one job ahead into the shared
 // slot, after the barrier that ends every wave's use of that slot.  x row m sits in its
-// slot with its 16-byte units XOR-swizzled by m (unit u at u ^ m, the swizzle applied to
-// the global offsets of the copy), so the fragment reads of 16 rows fall in 16 distinct
-// bank groups without padding.
+// slot with its 16-byte units XOR-swizzled (unit u at u ^ xswz(m), the swizzle applied to
+// the global offsets of the copy); see xswz for the bank groups of the fragment reads.
 template <int S, int MX, bool kNested, int QS, bool kAligned>
 __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
     constexpr int C = kTabCopies;
@@ -645,7 +658,7 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
         for (int i = 0; i < kXL; ++i) {
             const int m = wave + S * i;
             const int ms = m < M ? m : M - 1;
-            const int u = lane ^ (m & 15);
+            const int u = lane ^ xswz<MX>(m);
             const uint32_t xo = j * kChunkK + 8 * u < K ? (uint32_t)(j * (kChunkK * 2) + 16 * u + ms * K * 2) : 0x80000000u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xdst + m * 1024), 16, xo, 0, 0, 0);
             xo_live[i] = xo;
@@ -702,7 +715,7 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
                     const uint32_t addr = __builtin_amdgcn_perm(cws[tt], lane_sel, 0x0C0C0400u | ((uint32_t)(4 + k4) << 8));
                     wv[k4] = *reinterpret_cast<const uint32_t*>(tabb + addr);
                 }
-                const u32x4_t xv = xf[(8 * bb + 2 * h + tt) ^ (xrow & 15)];
+                const u32x4_t xv = xf[(8 * bb + 2 * h + tt) ^ xswz<MX>(xrow)];
                 pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
                                                              __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3])),
                                                              pp, 0, 0, 0);
