@@ -21,8 +21,9 @@ absolute rate from a second pass of K steps with an event after every launch
 (kept out of the timed region: recording 43 events a step costs about 5% of
 it).  `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 
-`extra` also times the other workloads (skip with --skip-configs): a plain 1 GiB
-device copy (the practical HBM ceiling), the 1024 x 1024 weight (microseconds per
+`extra` also times the other workloads (skip with --skip-configs): the practical
+HBM ceilings (a plain 1 GiB device copy, and a stream of 16-byte loads alone,
+plain and nontemporal), the 1024 x 1024 weight (microseconds per
 call), GEMV over six replicas of the 7B layer set (624 MB, M = 1 and 16, one
 grouped call per layer, eager and replayed from a HIP graph), the 70B-shaped
 8-layer stack (bulk quantize + double quant of 56 weights, then grouped GEMV at
@@ -601,17 +602,42 @@ def edge_us(torch, qk, workloads, iters=50):
     return res
 
 
-def copy_ceiling(torch, iters=10):
-    """A plain 1 GiB device-to-device copy (torch): read + write bytes over time,
-    the practical HBM ceiling next to the 8 TB/s spec."""
+def hbm_ceilings(torch, iters=10):
+    """The practical HBM ceilings next to the 8 TB/s spec: a plain 1 GiB
+    device-to-device copy (torch; read + write bytes over time) and a 4 GiB stream
+    of 16-byte loads alone (libqk_probe.so, plain and nontemporal, the best of two
+    grid sizes)."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     t = _timed(torch, lambda: b.copy_(a), iters)
     del a, b
+    out = {"copy_1gib_tb_per_s": round(2 * n / t / 1e12, 3)}
+    probe = os.path.join(ROOT, "bit_blockwise_weight_amd", "libqk_probe.so")
+    if not os.path.exists(probe):
+        out["read_stream"] = "libqk_probe.so not built"
+        torch.cuda.empty_cache()
+        return out
+    lib = ctypes.CDLL(probe)
+    lib.qk_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p]
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    grids = (4096, 8192)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for nt, key in ((0, "read_plain_tb_per_s"), (1, "read_nontemporal_tb_per_s")):
+        best = 0.0
+        for grid in grids:
+            def run():
+                if lib.qk_probe_read_stream(src.data_ptr(), nbytes, sink.data_ptr(), grid, nt, stream) != 0:
+                    raise RuntimeError("qk_probe_read_stream failed")
+            best = max(best, nbytes / _timed(torch, run, iters) / 1e12)
+        out[key] = round(best, 3)
+    del src, sink
     torch.cuda.empty_cache()
-    return {"bytes_moved": 2 * n, "tb_per_s": round(2 * n / t / 1e12, 3)}
+    return out
 
 
 def shader_clock(torch, qk, busy_fn):
@@ -785,7 +811,7 @@ def bench(args):
     extra = {"ms_per_step_without_events": round(step_noev_s * 1e3, 3),
              "ms_per_step_with_an_event_per_launch": round(step_allev_s * 1e3, 3)}
     if not args.skip_configs:
-        extra["copy_ceiling_1gib"] = copy_ceiling(torch)
+        extra["hbm_ceilings"] = hbm_ceilings(torch)
         extra["config_single_1024"] = single_1024_us(torch, qk, workloads)
         extra["config_llama7b_gemv_rotating"] = gemv_rotating(torch, qk, workloads)
         extra["config_llama70b_stack"] = llama70b_stack(torch, qk, workloads)

@@ -10,7 +10,9 @@ Every source is compiled with hipcc for gfx950 only:
                                       can decide a code)
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                       no packed fp32 VALU instructions
-The library lands next to this file (bit_blockwise_weight_amd/libqk.so).
+The library lands next to this file (bit_blockwise_weight_amd/libqk.so), and
+with it libqk_probe.so: the HBM read-ceiling probe that bench.py times (not part
+of the C ABI).
 """
 
 import os
@@ -25,6 +27,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqk.so")
+PROBE_LIB = os.path.join(PKG, "libqk_probe.so")
+PROBE_SOURCE = "hbm_probe.hip"
 
 SOURCES = ["api.cpp", "codebook.cpp", "quantize.hip", "double_quant.hip", "dequantize.hip", "gemv.hip", "gemm.hip",
            "merge.hip", "backward.hip", "quantize8.hip", "int8mm.hip"]
@@ -68,6 +72,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    probe_obj = _compile(PROBE_SOURCE)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, probe_obj,
+           "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking libqk_probe.so failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
     return LIB
 
 

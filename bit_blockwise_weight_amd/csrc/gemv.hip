@@ -5,29 +5,38 @@
 // QLoRA 降低 LLM 訓練門檻？", section on speed (unpacking and dequantizing must be
 // fused, or 4-bit can be slower than 16-bit).  The weight is never written out.
 //
-// Fast path (K a multiple of 64 and of the block size, 16-byte aligned codes and x):
-//   * A workgroup owns 16 weight rows; its S waves split K in chunks of 512
-//     (wave w takes chunks w, w + S, ...).  S = 4 (80 KB of LDS: two workgroups
-//     per CU, one loading while the other computes) when there are at least two
-//     tiles per CU and K <= 4096; S = 8 otherwise.
-//   * Codes are loaded so that one instruction fetches 256 contiguous bytes from
-//     each of 4 rows; each wave writes its chunk to its own LDS area (no barrier)
-//     and reads it back in MFMA layout.  In that area the 16-byte piece p of row r
-//     sits in slot 16 r + (p ^ r), so the 16 rows a fragment read touches fall in
-//     16 different bank groups.  The next chunk's codes, x and scales are loaded
-//     before the current chunk is computed, by loads outside any branch.
-//   * v_mfma_f32_16x16x32_bf16 with A = x (16 x 32, rows m >= M are zero) and
-//     B = W^T (32 x 16 rows), so the 4 output registers of lane l are y[m][n] for
-//     m = 4(l / 16) + r, n = l % 16.  Lane l holds row n = l % 16 and, in 64-k block
-//     b, the 16 weights k = 64 b + 16 h + [0, 16), h = l / 16; the block's two MFMAs
-//     take k = 64 b + 16 h + 8 t + [0, 8), t = 0, 1, so both stay inside one block of
-//     64 and the row's block scale a' (fp32) multiplies the block's partial product:
-//     one FMA per output register per block, none per weight.
+// Fast path (every row length a multiple of 64 and of the block size, 16-byte
+// aligned codes and x), one launch for a whole group of weights (a layer: up to 16
+// slices of weights that share nothing but the launch, more launches beyond), the
+// weights cut into tiles of 16 rows sorted by row length:
+//   * M = 1: gemv_group_kernel.  One 8-wave workgroup per CU walks the tiles wg,
+//     wg + G, ...; in a tile, wave w takes the 512-k jobs w, w + 8, ... and keeps
+//     its partial 16 outputs in LDS until the end, when the 8 partials of every
+//     tile are added in wave order (no barrier inside the loop).
+//   * 2 <= M <= 16: gemv_rows_kernel.  One workgroup per group of 8 consecutive
+//     tiles of one slice; each wave owns a tile and walks its rows from k = 0 to K,
+//     the 8 waves taking the same job at the same time so that the x chunk of a
+//     job (M rows x 1 KB) is copied to LDS once and shared.
+//   Both: a job's codes (16 rows x 256 bytes) arrive by 4 buffer loads with the
+//   LDS bit and the nontemporal hint, each fetching 256 contiguous bytes of 4 rows
+//   into the wave's own LDS slot (piece p of row r in slot 16 r + (p ^ r), so the
+//   16 rows a fragment read touches fall in 16 different bank groups); the scales
+//   come by one or two plain loads, x by LDS copies as well.  Two slots per wave:
+//   the next job's loads are issued before the current job's compute, and explicit
+//   s_waitcnt counts (the compiler's own waits drained every copy in flight)
+//   let a job wait for its own loads only.
+//   * v_mfma_f32_16x16x32_bf16 with A = x (16 x 32; A rows m >= M repeat row M - 1
+//     and feed outputs that are never stored) and B = W^T (32 x 16 rows), so the 4
+//     output registers of lane l are y[m][n] for m = 4(l / 16) + r, n = l % 16.
+//     Lane l holds row n = l % 16 and, in 64-k block b, the 16 weights k = 64 b +
+//     16 h + [0, 16), h = l / 16; the block's two MFMAs take k = 64 b + 16 h + 8 t
+//     + [0, 8), t = 0, 1, so both stay inside one block of 64 and the row's block
+//     scale a' (fp32) multiplies the block's partial product: one FMA per output
+//     register per block, none per weight.
 //   * Decoding: an LDS table maps a code byte to the pair (bf16 level of the high
 //     nibble, bf16 level of the low nibble) as one dword, replicated 64 times and
 //     interleaved so that lane l reads copy l: the address (byte << 8 | 4l) is one
 //     v_perm, the read never conflicts.
-//   * The S waves' partial tiles are summed through LDS in a fixed order.
 // The levels are used as bf16 and the block scale is applied in fp32 after the
 // bf16 products; the result agrees with the fp64 product on the bf16-dequantized
 // weight within the documented tolerance.

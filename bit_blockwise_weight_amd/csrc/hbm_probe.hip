@@ -1,0 +1,50 @@
+// HBM read ceiling for the measurement script (not part of the qk C ABI): a grid of
+// 256-thread workgroups streams a buffer with 16-byte loads, 16 per lane in flight,
+// plain or with the nontemporal hint, and folds the words into one value per thread so
+// that no load is dropped.  bench.py times it with HIP events next to a device copy.
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr int kUnroll = 16;
+
+template <bool kNontemporal>
+__global__ __launch_bounds__(kThreads) void read_stream_kernel(const u32x4_t* __restrict__ p, size_t n16,
+                                                               uint32_t* __restrict__ out) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    uint32_t acc = 0;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride * kUnroll) {
+        u32x4_t v[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const size_t k = i + (size_t)j * stride;
+            if (k < n16) v[j] = kNontemporal ? __builtin_nontemporal_load(p + k) : p[k];
+            else v[j] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    out[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+// Reads nbytes (a multiple of 16, 16-byte aligned) at src; out holds grid * 256 words.
+// Returns 0, or a nonzero code for bad arguments or a failed launch.
+extern "C" int qk_probe_read_stream(const void* src, size_t nbytes, uint32_t* out, int grid, int nontemporal,
+                                    void* stream) {
+    if (src == nullptr || out == nullptr || nbytes == 0 || nbytes % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(src) % 16 != 0 || grid <= 0)
+        return 1;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4_t* p = static_cast<const u32x4_t*>(src);
+    if (nontemporal)
+        hipLaunchKernelGGL(read_stream_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p, nbytes / 16, out);
+    else
+        hipLaunchKernelGGL(read_stream_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p, nbytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
