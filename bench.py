@@ -8,8 +8,9 @@ v, o [4096, 4096]; gate, up [11008, 4096]; down [4096, 11008]; bf16 weights
   for each of the 7 weights:
     qk_quantize_blockwise (NF4, block 64) + qk_double_quant   (steps a2-a5)
     qk_dequantize to bf16                                     (a6)
-    qk_gemv_nf4 at M = 1 and M = 16                           (a7)
     qk_gemm_nf4 at M = 4096 tokens with LoRA r = 16, alpha/r = 2   (a8)
+  qk_gemv_nf4_grouped over the 7 weights at M = 1, then at M = 16   (a7:
+    one launch per layer, as a decoder runs it)
 Inputs are resident in HBM before timing starts.
 
 Output: one JSON line.  `value` is the step's time at the MI355X roofline
@@ -18,8 +19,8 @@ divided by the measured step time, in percent.  The timed region records HIP
 events only around the GEMM calls (the dominant kernel), on the stream the
 kernels run on; `roofline` comes from those.  `breakdown` gives each stage's
 absolute rate from a second pass of K steps with an event after every launch
-(kept out of the timed region: recording 43 events a step costs about 5% of
-it).  `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
+(kept out of the timed region: recording an event after each of the 30
+launches of a step costs a few percent of it).  `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 
 `extra` also times the other workloads (skip with --skip-configs): the practical
 HBM ceilings (a plain 1 GiB device copy, and a stream of 16-byte loads alone,
@@ -159,21 +160,27 @@ OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lo
 
 def step_calls(torch, qk, wl):
     """The launches of one pass of the hot path over the layer set, in order, as
-    (op, matrix, callable)."""
+    (op, matrices, callable): per weight quantize, double quant, dequantize and
+    the prefill GEMM with LoRA; then the decode GEMV of the whole layer at M = 1
+    and at M = 16, one grouped call each (qk_gemv_nf4_grouped: the way a decoder
+    runs a layer)."""
     lv = wl["levels_c"]
+    mats = wl["mats"]
     calls = []
-    for m in wl["mats"]:
+    for m in mats:
         a = wl["acts"][m["K"]]
         A, Bm = wl["lora"][m["name"]]
         calls += [
-            ("quantize", m, lambda m=m: qk.qk_quantize_blockwise(m["w"], 64, lv, m["codes"], m["absmax"])),
-            ("double_quant", m, lambda m=m: qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])),
-            ("dequantize", m, lambda m=m: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])),
-            ("gemv_m1", m, lambda m=m, a=a: qk.qk_gemv_nf4(a["x1"], m["state"], m["y1"])),
-            ("gemv_m16", m, lambda m=m, a=a: qk.qk_gemv_nf4(a["x16"], m["state"], m["y16"])),
-            ("gemm_lora", m, lambda m=m, a=a, A=A, Bm=Bm: qk.qk_gemm_nf4(a["X"], m["state"], A, Bm, 2.0, m["Y"],
-                                                                         wl["gemm_ws"])),
+            ("quantize", [m], lambda m=m: qk.qk_quantize_blockwise(m["w"], 64, lv, m["codes"], m["absmax"])),
+            ("double_quant", [m], lambda m=m: qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])),
+            ("dequantize", [m], lambda m=m: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])),
+            ("gemm_lora", [m], lambda m=m, a=a, A=A, Bm=Bm: qk.qk_gemm_nf4(a["X"], m["state"], A, Bm, 2.0, m["Y"],
+                                                                           wl["gemm_ws"])),
         ]
+    for op, xk, yk in (("gemv_m1", "x1", "y1"), ("gemv_m16", "x16", "y16")):
+        items = [(wl["acts"][m["K"]][xk], m["state"]) for m in mats]
+        ys = [m[yk] for m in mats]
+        calls.append((op, list(mats), lambda items=items, ys=ys: qk.qk_gemv_nf4_grouped(items, ys)))
     return calls
 
 
@@ -204,7 +211,16 @@ def run_step(calls, events=None, only=None):
         events[i + 1].record()
 
 
-def work_of(op, m, wl):
+def work_of(op, ms, wl):
+    """Algorithmic (bytes, flops) of one launch over the matrices ms."""
+    if len(ms) != 1:
+        tot = [0, 0]
+        for m in ms:
+            b, f = work_of(op, [m], wl)
+            tot[0] += b
+            tot[1] += f
+        return tot[0], tot[1]
+    m = ms[0]
     N, K = m["N"], m["K"]
     n = N * K
     if op == "quantize":

@@ -65,6 +65,9 @@ constexpr int kTabCopies = 64;
 // scales keep the default policy: a job reads 8 bytes of a row's 128-byte line and the
 // next job of the tile the next 8, from L2.
 constexpr int kStream = 2;
+// parts of a job's loads (the K-split kernel issues its codes and its x at different times)
+constexpr int kLoadCodes = 1;   // block scales and codes
+constexpr int kLoadX = 2;       // x rows
 // rows of x from which the row-split kernel (shared x chunk) replaces the K-split one
 constexpr int kRowsMinM = 2;
 
@@ -275,8 +278,10 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     cc.j = 0;
     set_comp_task(cc, lc.task);
 
-    auto load = [&](const LoadCur& c, JobRegs& jr, auto slot) {
+    // what = kLoadCodes (scales and codes), kLoadX (x rows) or both
+    auto load = [&](const LoadCur& c, JobRegs& jr, auto slot, auto what) {
         constexpr bool kB = decltype(slot)::value;
+        constexpr int kWhat = decltype(what)::value;
         // a job past the end of the work (after the last one) reloads its last tile's rows
         // (valid memory, mostly from the cache); it is never stored
         const __amdgpu_buffer_rsrc_t lcr = buf_rsrc(c.codes, c.code_bytes);
@@ -296,54 +301,57 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
         // the job's quantization blocks of row n are consecutive from qf on
         const uint32_t qs0 = tq + (uint32_t)(chc * kJobQ);   // uniform part of the scale index
         const uint32_t qf = qrow + qs0;
-        if constexpr (kNested) {
-            if constexpr (kAligned) {
-                // the job's kJobQ q8 bytes start at a multiple of kJobQ (8, 4 or 2)
-                if constexpr (QS == 0)
-                    jr.q.xy = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(lsr, qrow, qs0, 0));
-                else
-                    jr.q.x = __builtin_amdgcn_raw_buffer_load_b32(lsr, qf & ~3u, 0, 0);
-                if constexpr (QS == 2) jr.qinfo = qf & 3u;
-                jr.d.x = __builtin_amdgcn_raw_buffer_load_b32(ldr, (qf / QK_DQ_BLOCK) * 4u, 0, 0);
+        if constexpr ((kWhat & kLoadCodes) != 0) {
+            if constexpr (kNested) {
+                if constexpr (kAligned) {
+                    // the job's kJobQ q8 bytes start at a multiple of kJobQ (8, 4 or 2)
+                    if constexpr (QS == 0)
+                        jr.q.xy = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(lsr, qrow, qs0, 0));
+                    else
+                        jr.q.x = __builtin_amdgcn_raw_buffer_load_b32(lsr, qf & ~3u, 0, 0);
+                    if constexpr (QS == 2) jr.qinfo = qf & 3u;
+                    jr.d.x = __builtin_amdgcn_raw_buffer_load_b32(ldr, (qf / QK_DQ_BLOCK) * 4u, 0, 0);
+                } else {
+                    jr.q = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(lsr, qf & ~3u, 0, 0));
+                    jr.d = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ldr, (qf / QK_DQ_BLOCK) * 4u, 0, 0));
+                    jr.qinfo = (qf & 3u) | ((QK_DQ_BLOCK - qf % QK_DQ_BLOCK) << 2);
+                }
             } else {
-                jr.q = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(lsr, qf & ~3u, 0, 0));
-                jr.d = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ldr, (qf / QK_DQ_BLOCK) * 4u, 0, 0));
-                jr.qinfo = (qf & 3u) | ((QK_DQ_BLOCK - qf % QK_DQ_BLOCK) << 2);
+                if constexpr (kAligned) {
+                    jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, qs0 * 4u, 0));
+                    if constexpr (QS == 0)
+                        jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, qs0 * 4u + 16u, 0));
+                } else {
+                    jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qf * 4u, 0, 0));
+                    if constexpr (QS == 0)
+                        jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qf * 4u + 16u, 0, 0));
+                }
             }
-        } else {
+            __attribute__((address_space(3))) char* cdst =
+                (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? cb1 : cb0) + wave * 4096;
+            // codes: load i, lane L fetches piece (L % 16) ^ r of row r = 4 i + L / 16, which lands
+            // in slot unit 64 i + L
             if constexpr (kAligned) {
-                jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, qs0 * 4u, 0));
-                if constexpr (QS == 0)
-                    jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qrow * 4u, qs0 * 4u + 16u, 0));
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(lcr, (lds_ptr_t)(cdst + i * 1024), 16, crow[i],
+                                                             tcode + (uint32_t)chc * (kChunkK / 2), 0, kStream);
             } else {
-                jr.f0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qf * 4u, 0, 0));
-                if constexpr (QS == 0)
-                    jr.f1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(lsr, qf * 4u + 16u, 0, 0));
+                // pieces past the end of a row, in a partial chunk, are clamped to the row's last
+                // 16 bytes (their x is zero); the offset stays in the range-checked vector part
+                const uint32_t row_bytes = (uint32_t)(K / 2);
+                const uint32_t cofs = (uint32_t)chc * (kChunkK / 2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * i + (lane >> 4);
+                    const uint32_t piece = 16u * (uint32_t)((lane & 15) ^ r);
+                    const uint32_t within = cofs + piece + 16u <= row_bytes ? cofs : row_bytes - 16u - piece;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(lcr, (lds_ptr_t)(cdst + i * 1024), 16, crow[i] + within,
+                                                             tcode, 0, kStream);
+                }
             }
         }
-        __attribute__((address_space(3))) char* cdst =
-            (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? cb1 : cb0) + wave * 4096;
-        // codes: load i, lane L fetches piece (L % 16) ^ r of row r = 4 i + L / 16, which lands
-        // in slot unit 64 i + L
-        if constexpr (kAligned) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(lcr, (lds_ptr_t)(cdst + i * 1024), 16, crow[i],
-                                                         tcode + (uint32_t)chc * (kChunkK / 2), 0, kStream);
-        } else {
-            // pieces past the end of a row, in a partial chunk, are clamped to the row's last
-            // 16 bytes (their x is zero); the offset stays in the range-checked vector part
-            const uint32_t row_bytes = (uint32_t)(K / 2);
-            const uint32_t cofs = (uint32_t)chc * (kChunkK / 2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * i + (lane >> 4);
-                const uint32_t piece = 16u * (uint32_t)((lane & 15) ^ r);
-                const uint32_t within = cofs + piece + 16u <= row_bytes ? cofs : row_bytes - 16u - piece;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(lcr, (lds_ptr_t)(cdst + i * 1024), 16, crow[i] + within,
-                                                         tcode, 0, kStream);
-            }
-        }
+        if constexpr ((kWhat & kLoadX) == 0) return;
         // x rows m < MX of the job's k, 16 bytes per lane: unit L of row m lands in slot unit
         // m * kXPitch + xrot(m) + L.  An idle wave's chunk and the k past the row in a partial
         // chunk take an offset beyond the buffer and read zero, so those products vanish
@@ -365,7 +373,11 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     // never stored
     const int xrow = n < M ? n : M - 1;
     const int xunit = xrow * kXPitch + xrot(xrow) + 2 * h;
-    auto compute = [&](const CompCur& c, const JobRegs& jr, auto slot) {
+    // A job: its scales are taken from the registers and its code words from the LDS slot
+    // first; once those reads have returned, refill() issues the scale and code loads of the
+    // job two ahead into the same registers and slot, so they are in flight while this job's
+    // table lookups and MFMAs run (x stays in its slot until the end of the job).
+    auto compute = [&](const CompCur& c, const JobRegs jr, auto slot, auto&& refill) {
         constexpr bool kB = decltype(slot)::value;
         const char* mb = reinterpret_cast<const char*>(kB ? cb1 : cb0) + wave * 4096;
         const u32x4_t* xf = reinterpret_cast<const u32x4_t*>(kB ? xs1 : xs0) + wave * kSlotX + xunit;
@@ -393,26 +405,57 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
                 dsc1 = __builtin_bit_cast(float, d1);
             }
         }
+        uint32_t fsel[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        if constexpr (!kNested) {
+            const u32x4_t f0 = jr.f0, f1 = jr.f1;
+            fsel[0] = f0[0]; fsel[1] = f0[1]; fsel[2] = f0[2]; fsel[3] = f0[3];
+            fsel[4] = f1[0]; fsel[5] = f1[1]; fsel[6] = f1[2]; fsel[7] = f1[3];
+        }
+        // the job's code words: row n, 16-weight group h of each of the 8 blocks (a plain
+        // vector load: a copy of a HIP vector struct becomes a memcpy that loses the LDS
+        // object's identity, and then every copy in flight is waited for)
+        u32x2_t cwv[kChunkBlocks];
 #pragma unroll
         for (int bb = 0; bb < kChunkBlocks; ++bb) {
             const int piece = 2 * bb + (h >> 1);
-            // a plain vector load (a copy of a HIP vector struct becomes a memcpy that
-            // loses the LDS object's identity, and then every copy in flight is waited for)
-            const u32x2_t cw = *reinterpret_cast<const u32x2_t*>(mb + (16 * n + (piece ^ n)) * 16 + 8 * (h & 1));
+            cwv[bb] = *reinterpret_cast<const u32x2_t*>(mb + (16 * n + (piece ^ n)) * 16 + 8 * (h & 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the code reads have returned
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        refill();
+        __builtin_amdgcn_sched_barrier(0);
+        // block bb's table reads and x reads are issued before block bb - 1's MFMAs (two
+        // register sets, alternating), so a block's LDS round trip overlaps the previous
+        // block's work instead of stalling the wave once per block
+        uint32_t wv[2][8];
+        u32x4_t xv[2][2];
+        auto fetch = [&](int bb) {
+            const u32x2_t cw = cwv[bb];
             const uint32_t cws[2] = {cw[0], cw[1]};
-            floatx4_t pp = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                uint32_t wv[4];
 #pragma unroll
                 for (int k4 = 0; k4 < 4; ++k4) {
                     uint32_t addr = __builtin_amdgcn_perm(cws[t], lane_sel, 0x0C0C0400u | ((uint32_t)(4 + k4) << 8));
                     if constexpr (C == 32) addr >>= 1;
-                    wv[k4] = *reinterpret_cast<const uint32_t*>(tabb + addr);
+                    wv[bb & 1][4 * t + k4] = *reinterpret_cast<const uint32_t*>(tabb + addr);
                 }
-                const u32x4_t xv = xf[8 * bb + t];
-                pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
-                                                             __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3])),
+                xv[bb & 1][t] = xf[8 * bb + t];
+            }
+        };
+        fetch(0);
+#pragma unroll
+        for (int bb = 0; bb < kChunkBlocks; ++bb) {
+            if (bb + 1 < kChunkBlocks) fetch(bb + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            floatx4_t pp = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t* w = &wv[bb & 1][4 * t];
+                pp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[bb & 1][t]),
+                                                             __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3])),
                                                              pp, 0, 0, 0);
             }
             // the block's scale: quantization block bb >> QS of the job
@@ -424,11 +467,11 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
                 const float dsc = qq < split ? dsc0 : dsc1;
                 a = __fadd_rn(__fmul_rn((float)q8, dsc), c.mu);
             } else {
-                const uint32_t fsel[8] = {jr.f0[0], jr.f0[1], jr.f0[2], jr.f0[3], jr.f1[0], jr.f1[1], jr.f1[2], jr.f1[3]};
                 a = __builtin_bit_cast(float, fsel[qq]);
             }
 #pragma unroll
             for (int r = 0; r < kR; ++r) acc[r] = __builtin_fmaf(pp[r], a, acc[r]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -460,10 +503,13 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
 
     using SlotA = std::integral_constant<bool, false>;
     using SlotB = std::integral_constant<bool, true>;
+    using LoadAll = std::integral_constant<int, kLoadCodes | kLoadX>;
+    using LoadCodes = std::integral_constant<int, kLoadCodes>;
+    using LoadX = std::integral_constant<int, kLoadX>;
     JobRegs ra, rb;
-    load(lc, ra, SlotA{});
+    load(lc, ra, SlotA{}, LoadAll{});
     advance_load(lc);
-    load(lc, rb, SlotB{});
+    load(lc, rb, SlotB{}, LoadAll{});
     advance_load(lc);
     {
         // pair table: entry C b + copy for byte b.  Wave w writes the bytes b = w + S j,
@@ -485,19 +531,18 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // Two jobs in flight: each job is computed from its LDS slot (the wait is for its own
-    // copies, issued before the other slot's), then its slot is refilled with the job two
-    // ahead.  The loop runs whole pairs of jobs with no condition around a load (the last
-    // pair may end with a job past the end, whose sums are never stored), has no barrier and
-    // writes no global memory, so the compiler's wait before each compute leaves the other
-    // slot's copies outstanding.  A slot is refilled only after every LDS read of it has
-    // returned: the compute consumes all of them.
+    // Two slots of jobs in flight.  Job j's scales and codes are issued at the start of job
+    // j - 2's compute (as soon as that job's code words are in registers) and its x at the
+    // end of it (once that job's x reads have returned), so the loads of a job issue in
+    // the order scales + codes, x, and between job j's x and its compute only job j + 1's
+    // kLoads loads are issued.  The loop runs whole pairs of jobs with no condition around a
+    // load (the last pair may end with a job past the end, whose sums are never stored), has
+    // no barrier and writes no global memory.
     //
-    // The waits are explicit: before a job is computed, at most the other job's kLoads
-    // loads may still be in flight (so every copy into this job's slot has landed), and
-    // before a slot is refilled every LDS read of it has returned.  (The compiler's own
-    // tracking of copies into LDS is not relied on: it can miss the copies issued before
-    // the loop.)
+    // The waits are explicit: before a job is computed, at most kLoads loads may still be in
+    // flight (so every copy of this job has landed), and before a slot is refilled every LDS
+    // read of it has returned.  (The compiler's own tracking of copies into LDS is not
+    // relied on: it can miss the copies issued before the loop.)
     auto wait_job = [] {
         __builtin_amdgcn_s_waitcnt((kLoads & 15) | ((kLoads >> 4) << 14) | (7 << 4) | (15 << 8));
         asm volatile("" ::: "memory");
@@ -510,15 +555,15 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     int32_t it = 0;
     do {
         wait_job();
-        compute(cc, ra, SlotA{});
+        compute(cc, ra, SlotA{}, [&] { load(lc, ra, SlotA{}, LoadCodes{}); });
         wait_lds();
-        load(lc, ra, SlotA{});
+        load(lc, ra, SlotA{}, LoadX{});
         advance_load(lc);
         end_job();
         wait_job();
-        compute(cc, rb, SlotB{});
+        compute(cc, rb, SlotB{}, [&] { load(lc, rb, SlotB{}, LoadCodes{}); });
         wait_lds();
-        load(lc, rb, SlotB{});
+        load(lc, rb, SlotB{}, LoadX{});
         advance_load(lc);
         end_job();
     } while (++it < npairs);
