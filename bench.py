@@ -5,11 +5,12 @@
 One step = every stage of the path over one Llama-7B-shaped layer set (q, k,
 v, o [4096, 4096]; gate, up [11008, 4096]; down [4096, 11008]; bf16 weights
 ~ N(0, 0.02), synthetic):
+  qk_quantize_blockwise (NF4, block 64) of each of the 7 weights   (a2-a4)
+  qk_double_quant_grouped of the 7 absmax arrays                   (a5)
   for each of the 7 weights:
-    qk_quantize_blockwise (NF4, block 64) + qk_double_quant   (steps a2-a5)
-    qk_dequantize to bf16                                     (a6)
-    qk_gemm_nf4 at M = 4096 tokens with LoRA r = 16, alpha/r = 2   (a8)
-  qk_gemv_nf4_grouped over the 7 weights at M = 1, then at M = 16   (a7:
+    qk_dequantize to bf16                                          (a6)
+    qk_gemm_nf4 at M = 4096 tokens with LoRA r = 16, alpha/r = 2    (a8)
+  qk_gemv_nf4_grouped over the 7 weights at M = 1, then at M = 16  (a7:
     one launch per layer, as a decoder runs it)
 Inputs are resident in HBM before timing starts.
 
@@ -19,7 +20,7 @@ divided by the measured step time, in percent.  The timed region records HIP
 events only around the GEMM calls (the dominant kernel), on the stream the
 kernels run on; `roofline` comes from those.  `breakdown` gives each stage's
 absolute rate from a second pass of K steps with an event after every launch
-(kept out of the timed region: recording an event after each of the 30
+(kept out of the timed region: recording an event after each of the 24
 launches of a step costs a few percent of it).  `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 
 `extra` also times the other workloads (skip with --skip-configs): the practical
@@ -152,7 +153,7 @@ def build_workload(torch, qk, workloads):
     gemm_ws = torch.empty(max(16, qk.qk_gemm_nf4_workspace_size(M_TOK, R)), dtype=torch.uint8, device=dev)
     levels_c = (ctypes.c_float * 16)(*lv.tolist())
     return {"mats": mats, "acts": acts, "lora": lora, "M": M_TOK, "r": R, "levels": lv, "levels_c": levels_c,
-            "gemm_ws": gemm_ws}
+            "gemm_ws": gemm_ws, "dq_call": dq_group_call(torch, qk, mats)}
 
 
 OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lora"]
@@ -160,19 +161,20 @@ OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lo
 
 def step_calls(torch, qk, wl):
     """The launches of one pass of the hot path over the layer set, in order, as
-    (op, matrices, callable): per weight quantize, double quant, dequantize and
-    the prefill GEMM with LoRA; then the decode GEMV of the whole layer at M = 1
-    and at M = 16, one grouped call each (qk_gemv_nf4_grouped: the way a decoder
-    runs a layer)."""
+    (op, matrices, callable): quantize of each weight, the double quantization of
+    the layer's absmax arrays in one grouped call, per weight dequantize and the
+    prefill GEMM with LoRA; then the decode GEMV of the whole layer at M = 1 and at
+    M = 16, one grouped call each (the way a decoder runs a layer)."""
     lv = wl["levels_c"]
     mats = wl["mats"]
     calls = []
     for m in mats:
+        calls.append(("quantize", [m], lambda m=m: qk.qk_quantize_blockwise(m["w"], 64, lv, m["codes"], m["absmax"])))
+    calls.append(("double_quant", list(mats), wl["dq_call"]))
+    for m in mats:
         a = wl["acts"][m["K"]]
         A, Bm = wl["lora"][m["name"]]
         calls += [
-            ("quantize", [m], lambda m=m: qk.qk_quantize_blockwise(m["w"], 64, lv, m["codes"], m["absmax"])),
-            ("double_quant", [m], lambda m=m: qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])),
             ("dequantize", [m], lambda m=m: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])),
             ("gemm_lora", [m], lambda m=m, a=a, A=A, Bm=Bm: qk.qk_gemm_nf4(a["X"], m["state"], A, Bm, 2.0, m["Y"],
                                                                            wl["gemm_ws"])),
@@ -422,13 +424,36 @@ def _graph_timed(torch, fn, iters):
     return sec
 
 
+def dq_group_call(torch, qk, mats):
+    """A prepared qk_double_quant_grouped over the matrices' absmax arrays (the
+    task array and the workspace built once, so a timed loop pays no Python
+    marshalling)."""
+    arr = (qk.DqTask * len(mats))()
+    for i, m in enumerate(mats):
+        arr[i].absmax, arr[i].nblocks = m["absmax"].data_ptr(), m["absmax"].numel()
+        arr[i].q8, arr[i].scale, arr[i].mean = m["q8"].data_ptr(), m["scale"].data_ptr(), m["mean"].data_ptr()
+    ws = torch.empty(max(8, qk.qk_double_quant_grouped_workspace_size([m["absmax"].numel() for m in mats])),
+                     dtype=torch.uint8, device=mats[0]["absmax"].device)
+    L = qk.lib()
+    n = len(mats)
+
+    def call():
+        rc = L.qk_double_quant_grouped(arr, n, 256, ws.data_ptr(), ws.numel(),
+                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"qk_double_quant_grouped: {qk.qk_last_error()}")
+
+    call.keep = (arr, ws, mats)
+    return call
+
+
 def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
-    """The 70B-shaped stack: 8 layers of q, o [8192, 8192], k, v [1024, 8192],
-    gate, up [28672, 8192], down [8192, 28672] (the GQA layer of the 70B model),
-    bf16 ~ N(0, 0.015) drawn on the device (seeded Philox).  Bulk quantize
-    (NF4 block 64) + double quant of all 56 weights, then the grouped GEMV (one
-    call per layer, 7 weights) at batch 1, 4 and 8, eager and replayed from a HIP
-    graph.  Rates are algorithmic bytes over time."""
+    """The 70B-shaped stack: 8 layers of 4 x [8192, 8192], 2 x [28672, 8192] and
+    [8192, 28672], bf16 ~ N(0, 0.015) drawn on the device (seeded Philox).  Bulk
+    quantize (NF4 block 64, one call per weight) + double quant (one grouped call
+    per layer) of all 56 weights, then the grouped GEMV (one call per layer, 7
+    weights) at batch 1, 4 and 8, eager and replayed from a HIP graph.  Rates are
+    algorithmic bytes over time."""
     dev = torch.device("cuda:0")
     L = workloads.LLAMA70B_LAYERS
     shapes = workloads.LLAMA70B_LAYER_SHAPES
@@ -449,12 +474,17 @@ def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
                 "mean": torch.empty(1, dtype=torch.float32, device=dev),
                 "ws": torch.empty(max(8, qk.qk_double_quant_workspace_size(nb)), dtype=torch.uint8, device=dev),
             })
+    dq_calls = [dq_group_call(torch, qk, [m for m in mats if m["l"] == l]) for l in range(L)]
 
     def quantize_all():
         for m in mats:
             qk.qk_quantize_blockwise(m["w"], 64, lvc, m["codes"], m["absmax"])
 
     def dq_all():
+        for call in dq_calls:
+            call()
+
+    def dq_single_all():
         for m in mats:
             qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])
 
@@ -465,6 +495,7 @@ def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
     t_both = _timed(torch, both, iters)
     t_q = _timed(torch, quantize_all, iters)
     t_dq = _timed(torch, dq_all, iters)
+    t_dq1 = _timed(torch, dq_single_all, iters)
     qbytes = sum(bytes_quantize(m["N"] * m["K"]) for m in mats)
     dqbytes = sum(bytes_double_quant(nblk(m["N"] * m["K"], 64)) for m in mats)
     out = {"layers": L, "weights": len(mats), "params": sum(m["N"] * m["K"] for m in mats),
@@ -472,11 +503,13 @@ def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
            "quantize_dq_tb_per_s": round((qbytes + dqbytes) / t_both / 1e12, 3),
            "quantize_dq_frac_of_hbm": round((qbytes + dqbytes) / t_both / HBM_BPS, 4),
            "quantize_only_ms": round(t_q * 1e3, 3), "quantize_only_tb_per_s": round(qbytes / t_q / 1e12, 3),
-           "dq_only_ms": round(t_dq * 1e3, 3), "dq_us_per_weight": round(t_dq / len(mats) * 1e6, 2)}
+           "dq_only_ms": round(t_dq * 1e3, 3), "dq_us_per_layer_grouped": round(t_dq / L * 1e6, 2),
+           "dq_us_per_weight_single_calls": round(t_dq1 / len(mats) * 1e6, 2)}
     for m in mats:
         m["state"] = qk.qk_state_init(qk.NF4, lv, m["N"], m["K"], 64, m["codes"], None, m["q8"], m["scale"],
                                       m["mean"])
         del m["w"], m["absmax"], m["ws"]
+    del dq_calls
     torch.cuda.empty_cache()
     layers = [[m for m in mats if m["l"] == l] for l in range(L)]
     gemv = {}
@@ -950,7 +983,8 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path
 PROFILE_WORKLOADS = {
     # name: description (per-dispatch element counts for the derived figures come from
     # profile_elements below)
-    "llama70b-quantize": "quantize (NF4, block 64) + double quant of the 7 weights of one 70B-shaped layer, 3 passes",
+    "llama70b-quantize": "quantize (NF4, block 64) of the 7 weights of one 70B-shaped layer + their grouped double "
+                         "quant, 3 passes",
     "llama70b-gemv": "grouped GEMV over two 70B-shaped layers (7 weights each, one launch per layer), "
                      "M = 1, 4, 8, 3 passes each",
     "llama7b-gemv": "grouped GEMV over two Llama-7B layer sets (7 weights, one launch per layer), "
@@ -998,10 +1032,11 @@ def profile_workload(name):
                          "mean": torch.empty(1, dtype=torch.float32, device=dev),
                          "ws": torch.empty(max(8, qk.qk_double_quant_workspace_size(nb)), dtype=torch.uint8,
                                            device=dev)})
+        dq = dq_group_call(torch, qk, mats)
         for _ in range(3):
             for m in mats:
                 qk.qk_quantize_blockwise(m["w"], 64, lvc, m["codes"], m["absmax"])
-                qk.qk_double_quant(m["absmax"], 256, m["q8"], m["scale"], m["mean"], m["ws"])
+            dq()
     elif name in ("llama70b-gemv", "llama7b-gemv"):
         shapes = workloads.LLAMA70B_LAYER_SHAPES if name == "llama70b-gemv" else workloads.LLAMA7B_SHAPES
         std = 0.015 if name == "llama70b-gemv" else 0.02

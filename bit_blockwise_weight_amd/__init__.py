@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "QKError", "QuantState", "QuantizedWeight", "NF4", "FP4", "CUSTOM", "lib",
     "qk_make_codebook", "qk_quantize_blockwise", "qk_double_quant_workspace_size", "qk_double_quant",
+    "qk_double_quant_grouped_workspace_size", "qk_double_quant_grouped",
     "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemv_nf4_grouped", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_gemm_nf4_noalloc", "qk_last_error", "qk_version",
     "qk_backend_info", "quantize",
 ]
@@ -68,6 +69,12 @@ class QuantState(ctypes.Structure):
     ]
 
 
+class DqTask(ctypes.Structure):
+    """qk_dq_task."""
+    _fields_ = [("absmax", ctypes.c_void_p), ("nblocks", ctypes.c_int64), ("q8", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("mean", ctypes.c_void_p)]
+
+
 class GemvTask(ctypes.Structure):
     """Mirror of qk_gemv_task (include/qk.h)."""
     _fields_ = [("x", ctypes.c_void_p), ("st", ctypes.POINTER(QuantState)), ("y", ctypes.c_void_p)]
@@ -100,6 +107,8 @@ def lib():
         "qk_quantize_blockwise": [vp, i32, i64, i32, ctypes.POINTER(ctypes.c_float), vp, vp, vp],
         "qk_double_quant_workspace_size": [i64, ctypes.POINTER(ctypes.c_size_t)],
         "qk_double_quant": [vp, i64, i32, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "qk_double_quant_grouped_workspace_size": [ctypes.POINTER(DqTask), i32, ctypes.POINTER(ctypes.c_size_t)],
+        "qk_double_quant_grouped": [ctypes.POINTER(DqTask), i32, i32, vp, ctypes.c_size_t, vp],
         "qk_state_init": [st_p, i32, ctypes.POINTER(ctypes.c_float), i64, i64, i32, vp, vp, vp, vp, vp],
         "qk_dequantize": [st_p, vp, i32, vp],
         "qk_gemv_nf4": [vp, i32, st_p, vp, vp],
@@ -349,6 +358,56 @@ def qk_double_quant(absmax: torch.Tensor, dq_blocksize: int = QK_DQ_BLOCK, q8=No
         _check(lib().qk_double_quant(_ptr(absmax), nb, int(dq_blocksize), _ptr(q8), _ptr(scale), _ptr(mean),
                                      _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(absmax))))
     return q8, scale, mean
+
+
+def _dq_tasks(absmaxes, q8s=None, scales=None, means=None, dq_blocksize=QK_DQ_BLOCK):
+    absmaxes = list(absmaxes)
+    if not absmaxes:
+        raise ValueError("double quantization of a group needs at least one absmax array")
+    outs = []
+    arr = (DqTask * len(absmaxes))()
+    for i, a in enumerate(absmaxes):
+        if a.dtype != torch.float32:
+            raise ValueError(f"task {i}: absmax must be fp32")
+        _require_cuda(a)
+        nb = a.numel()
+        dev = a.device
+        q8 = q8s[i] if q8s is not None else torch.empty(nb, dtype=torch.int8, device=dev)
+        scale = scales[i] if scales is not None else torch.empty((nb + dq_blocksize - 1) // max(1, dq_blocksize),
+                                                                   dtype=torch.float32, device=dev)
+        mean = means[i] if means is not None else torch.empty(1, dtype=torch.float32, device=dev)
+        _require_cuda(q8, scale, mean)
+        arr[i].absmax, arr[i].nblocks = _ptr(a), nb
+        arr[i].q8, arr[i].scale, arr[i].mean = _ptr(q8), _ptr(scale), _ptr(mean)
+        outs.append((q8, scale, mean))
+    return arr, outs
+
+
+def qk_double_quant_grouped_workspace_size(nblocks) -> int:
+    nblocks = [int(n) for n in nblocks]
+    arr = (DqTask * len(nblocks))()
+    for i, n in enumerate(nblocks):
+        arr[i].nblocks = n
+    out = ctypes.c_size_t(0)
+    _check(lib().qk_double_quant_grouped_workspace_size(arr, len(nblocks), ctypes.byref(out)))
+    return int(out.value)
+
+
+def qk_double_quant_grouped(absmaxes, dq_blocksize: int = QK_DQ_BLOCK, q8s=None, scales=None, means=None,
+                            workspace=None):
+    """qk_double_quant of several absmax arrays in two launches per run of up to 16;
+    returns [(q8, scale, mean)] in the order of absmaxes."""
+    arr, outs = _dq_tasks(absmaxes, q8s, scales, means, dq_blocksize)
+    first = list(absmaxes)[0]
+    dev = first.device
+    if workspace is None:
+        workspace = torch.empty(max(8, qk_double_quant_grouped_workspace_size([a.numel() for a in absmaxes])),
+                                dtype=torch.uint8, device=dev)
+    _require_cuda(workspace)
+    with _on(dev):
+        _check(lib().qk_double_quant_grouped(arr, len(outs), int(dq_blocksize), _ptr(workspace), workspace.numel(),
+                                             ctypes.c_void_p(_stream(first))))
+    return outs
 
 
 def qk_state_init(codebook_kind: int, levels, rows: int, cols: int, blocksize: int, codes: torch.Tensor,

@@ -287,6 +287,87 @@ qk_status qk_double_quant(const float* absmax, int64_t nblocks, int32_t dq_block
                     "qk_double_quant");
 }
 
+namespace {
+
+// the grouped double quantization's arguments (no device access): sizes, pointers,
+// alignment, and that no output overlaps another output or an input
+qk_status check_dq_tasks(const qk_dq_task* tasks, int32_t ntasks, const char* who) {
+    if (!tasks) return fail(QK_ERR_INVALID_ARG, "%s: tasks is NULL", who);
+    if (ntasks < 1 || ntasks > 256) return fail(QK_ERR_INVALID_ARG, "%s: ntasks must be in 1..256 (got %d)", who, ntasks);
+    struct Span {
+        uintptr_t lo, hi;
+        bool out;
+        int32_t task;
+    };
+    std::vector<Span> spans;
+    for (int32_t i = 0; i < ntasks; ++i) {
+        const qk_dq_task& t = tasks[i];
+        if (t.nblocks < 1) return fail(QK_ERR_INVALID_ARG, "%s: task %d: nblocks must be >= 1", who, i);
+        if (!t.absmax || !t.q8 || !t.scale || !t.mean)
+            return fail(QK_ERR_INVALID_ARG, "%s: task %d: NULL pointer argument", who, i);
+        if (!aligned(t.absmax, 4) || !aligned(t.q8, 4) || !aligned(t.scale, 4) || !aligned(t.mean, 4))
+            return fail(QK_ERR_INVALID_ARG, "%s: task %d: absmax, q8, scale and mean must be 4-byte aligned", who, i);
+        const uintptr_t nb = (uintptr_t)t.nblocks;
+        const uintptr_t nd = (nb + QK_DQ_BLOCK - 1) / QK_DQ_BLOCK;
+        spans.push_back({reinterpret_cast<uintptr_t>(t.absmax), reinterpret_cast<uintptr_t>(t.absmax) + 4 * nb, false, i});
+        spans.push_back({reinterpret_cast<uintptr_t>(t.q8), reinterpret_cast<uintptr_t>(t.q8) + nb, true, i});
+        spans.push_back({reinterpret_cast<uintptr_t>(t.scale), reinterpret_cast<uintptr_t>(t.scale) + 4 * nd, true, i});
+        spans.push_back({reinterpret_cast<uintptr_t>(t.mean), reinterpret_cast<uintptr_t>(t.mean) + 4, true, i});
+    }
+    for (size_t a = 0; a < spans.size(); ++a) {
+        if (!spans[a].out) continue;
+        for (size_t b = 0; b < spans.size(); ++b) {
+            if (a == b) continue;
+            if (spans[a].lo < spans[b].hi && spans[b].lo < spans[a].hi)
+                return fail(QK_ERR_INVALID_ARG, "%s: an output of task %d overlaps %s of task %d", who, spans[a].task,
+                            spans[b].out ? "an output" : "the absmax", spans[b].task);
+        }
+    }
+    return ok();
+}
+
+size_t dq_group_workspace(const qk_dq_task* tasks, int32_t ntasks) {
+    size_t total = 0;
+    for (int32_t i = 0; i < ntasks; ++i) total += qk::dq_workspace_bytes(tasks[i].nblocks);
+    return total;
+}
+
+}  // namespace
+
+qk_status qk_double_quant_grouped_workspace_size(const qk_dq_task* tasks, int32_t ntasks, size_t* bytes) {
+    if (!bytes) return fail(QK_ERR_INVALID_ARG, "qk_double_quant_grouped_workspace_size: bytes is NULL");
+    if (!tasks) return fail(QK_ERR_INVALID_ARG, "qk_double_quant_grouped_workspace_size: tasks is NULL");
+    if (ntasks < 1 || ntasks > 256)
+        return fail(QK_ERR_INVALID_ARG, "qk_double_quant_grouped_workspace_size: ntasks must be in 1..256 (got %d)",
+                    ntasks);
+    for (int32_t i = 0; i < ntasks; ++i)
+        if (tasks[i].nblocks < 1)
+            return fail(QK_ERR_INVALID_ARG, "qk_double_quant_grouped_workspace_size: task %d: nblocks must be >= 1", i);
+    *bytes = dq_group_workspace(tasks, ntasks);
+    return ok();
+}
+
+qk_status qk_double_quant_grouped(const qk_dq_task* tasks, int32_t ntasks, int32_t dq_blocksize, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    const qk_status v = check_dq_tasks(tasks, ntasks, "qk_double_quant_grouped");
+    if (v != QK_OK) return v;
+    if (dq_blocksize != QK_DQ_BLOCK)
+        return fail(QK_ERR_UNSUPPORTED, "qk_double_quant_grouped: dq_blocksize %d (only 256 is implemented)", dq_blocksize);
+    const size_t need = dq_group_workspace(tasks, ntasks);
+    if (!workspace || workspace_bytes < need)
+        return fail(QK_ERR_WORKSPACE, "qk_double_quant_grouped: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 8))
+        return fail(QK_ERR_INVALID_ARG, "qk_double_quant_grouped: workspace must be 8-byte aligned");
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    std::vector<qk::DqItem> items((size_t)ntasks);
+    for (int32_t i = 0; i < ntasks; ++i)
+        items[(size_t)i] = qk::DqItem{tasks[i].absmax, tasks[i].nblocks, tasks[i].q8, tasks[i].scale, tasks[i].mean};
+    return launched(qk::launch_double_quant_group(items.data(), ntasks, workspace, reinterpret_cast<hipStream_t>(stream)),
+                    "qk_double_quant_grouped");
+}
+
 qk_status qk_state_init(qk_quant_state* st, int32_t codebook_kind, const float* levels, int64_t rows, int64_t cols,
                         int32_t blocksize, const uint8_t* codes, const float* absmax, const int8_t* q8,
                         const float* dq_scale, const float* dq_mean) {

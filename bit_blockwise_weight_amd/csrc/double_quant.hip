@@ -23,6 +23,8 @@
 //     partials (the same tree, at most 32 KB read from L2), then each of its 4
 //     waves quantizes 4 blocks of 256 absmax (4 per lane), their loads issued
 //     together.
+#include <vector>
+
 #include "qk_internal.h"
 #include "qk_device.h"
 
@@ -69,10 +71,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dq_rsrc(const void* p, int64_t
 // of the chunk, read with four 16-byte loads from a buffer whose range ends at the array's
 // end (values past it read as zero: the tree's zero padding).  The 4-byte alignment of the
 // array is enough for these loads.
-__global__ __launch_bounds__(kThreads) void tree_partials_f32(const float* __restrict__ in, int64_t count,
-                                                              double* __restrict__ out) {
-    __shared__ double red[kThreads / kWave];
-    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+__device__ __forceinline__ void partial_of_chunk(const float* __restrict__ in, int64_t count, int64_t chunk,
+                                                 double* __restrict__ out, double* red) {
+    const int64_t c0 = chunk * kChunk;
     const int64_t rem = count - c0;
     const __amdgpu_buffer_rsrc_t r = dq_rsrc(in + c0, 4 * (rem < kChunk ? rem : kChunk));
     double a[kPerThread];
@@ -86,7 +87,13 @@ __global__ __launch_bounds__(kThreads) void tree_partials_f32(const float* __res
         a[4 * j + 3] = (double)v.w;
     }
     const double s = chunk_tree(a, red);
-    if (threadIdx.x == 0) out[blockIdx.x] = s;
+    if (threadIdx.x == 0) out[chunk] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void tree_partials_f32(const float* __restrict__ in, int64_t count,
+                                                              double* __restrict__ out) {
+    __shared__ double red[kThreads / kWave];
+    partial_of_chunk(in, count, blockIdx.x, out, red);
 }
 
 template <typename T>
@@ -102,15 +109,17 @@ __global__ __launch_bounds__(kThreads) void tree_partials(const T* __restrict__ 
 }
 
 constexpr int kDqBlock = QK_DQ_BLOCK;           // 256 absmax per scale
+constexpr int kMaxDqGroup = 16;                  // arrays per grouped launch
 constexpr int kDqPerWave = 4;                    // dq blocks a wave quantizes
 constexpr int kDqBlocksPerWg = kThreads / kWave * kDqPerWave;
 
-__global__ __launch_bounds__(kThreads) void dq_quantize(const float* __restrict__ absmax, int64_t nb,
-                                                        const double* __restrict__ partials, int64_t npart,
-                                                        int8_t* __restrict__ q8, float* __restrict__ scale,
-                                                        float* __restrict__ mean_out) {
-    __shared__ double red[kThreads / kWave];
-    __shared__ float mean_sh;
+// Workgroup wg of the quantization of one array: the mean from its final partials, then
+// the workgroup's kDqBlocksPerWg blocks of 256 (workgroup 0 also stores the mean).
+__device__ __forceinline__ void dq_quantize_wg(const float* __restrict__ absmax, int64_t nb,
+                                               const double* __restrict__ partials, int64_t npart,
+                                               int8_t* __restrict__ q8, float* __restrict__ scale,
+                                               float* __restrict__ mean_out, int64_t wg, double* red,
+                                               float* mean_sh) {
     // mean from the final partials (npart <= 4096), same tree as the partial kernel; eight
     // 16-byte loads per thread, partials past npart read as zero
     {
@@ -126,17 +135,17 @@ __global__ __launch_bounds__(kThreads) void dq_quantize(const float* __restrict_
         const double total = chunk_tree(a, red);
         if (threadIdx.x == 0) {
             const float mu = (float)(total / (double)nb);
-            mean_sh = mu;
-            if (blockIdx.x == 0) *mean_out = mu;
+            *mean_sh = mu;
+            if (wg == 0) *mean_out = mu;
         }
         __syncthreads();
     }
-    const float mu = mean_sh;
+    const float mu = *mean_sh;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nd = (nb + kDqBlock - 1) / kDqBlock;
     // this wave's kDqPerWave blocks: one 16-byte load per lane and block, all issued first
     // (the buffer ends at the array's end; values past it are masked below)
-    const int64_t d0 = (int64_t)blockIdx.x * kDqBlocksPerWg + (threadIdx.x / kWave) * kDqPerWave;
+    const int64_t d0 = wg * kDqBlocksPerWg + (threadIdx.x / kWave) * kDqPerWave;
     if (d0 >= nd) return;
     const int64_t e0 = d0 * kDqBlock;
     const int64_t rem = nb - e0;
@@ -181,6 +190,53 @@ __global__ __launch_bounds__(kThreads) void dq_quantize(const float* __restrict_
     }
 }
 
+__global__ __launch_bounds__(kThreads) void dq_quantize(const float* __restrict__ absmax, int64_t nb,
+                                                        const double* __restrict__ partials, int64_t npart,
+                                                        int8_t* __restrict__ q8, float* __restrict__ scale,
+                                                        float* __restrict__ mean_out) {
+    __shared__ double red[kThreads / kWave];
+    __shared__ float mean_sh;
+    dq_quantize_wg(absmax, nb, partials, npart, q8, scale, mean_out, blockIdx.x, red, &mean_sh);
+}
+
+// Several arrays in one launch each: workgroup w of the launch belongs to the array t with
+// first[t] <= w < first[t + 1] (a uniform search over at most kMaxDqGroup entries) and
+// does that array's work item w - first[t], exactly as the single-array kernels do.
+struct DqGroup {
+    const float* absmax[kMaxDqGroup];
+    double* part[kMaxDqGroup];       // the array's final (and only) level of partials
+    int8_t* q8[kMaxDqGroup];
+    float* scale[kMaxDqGroup];
+    float* mean[kMaxDqGroup];
+    int64_t nb[kMaxDqGroup];
+    int32_t chunk0[kMaxDqGroup + 1]; // first workgroup of each array in the partials launch
+    int32_t wg0[kMaxDqGroup + 1];    // first workgroup of each array in the quantization launch
+    int32_t count;
+};
+
+__device__ __forceinline__ int dq_task_of(const int32_t* first, int32_t count, int32_t w) {
+    int t = 0;
+    while (t + 1 < count && w >= first[t + 1]) ++t;
+    return t;
+}
+
+__global__ __launch_bounds__(kThreads) void tree_partials_f32_group(DqGroup g) {
+    __shared__ double red[kThreads / kWave];
+    const int32_t w = (int32_t)blockIdx.x;
+    const int t = dq_task_of(g.chunk0, g.count, w);
+    partial_of_chunk(g.absmax[t], g.nb[t], w - g.chunk0[t], g.part[t], red);
+}
+
+__global__ __launch_bounds__(kThreads) void dq_quantize_group(DqGroup g) {
+    __shared__ double red[kThreads / kWave];
+    __shared__ float mean_sh;
+    const int32_t w = (int32_t)blockIdx.x;
+    const int t = dq_task_of(g.wg0, g.count, w);
+    const int64_t nb = g.nb[t];
+    dq_quantize_wg(g.absmax[t], nb, g.part[t], (nb + kChunk - 1) / kChunk, g.q8[t], g.scale[t], g.mean[t],
+                   w - g.wg0[t], red, &mean_sh);
+}
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
@@ -217,6 +273,60 @@ hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int8_t* q8,
     hipLaunchKernelGGL(dq_quantize, dim3((unsigned)grid), dim3(kThreads), 0, s, absmax, nblocks, cur, cnt, q8, scale,
                        mean);
     return hipGetLastError();
+}
+
+hipError_t launch_double_quant_group(const DqItem* items, int32_t count, void* workspace, hipStream_t s) {
+    // each array's partials sit at its own offset of the workspace (the sizes are whole
+    // doubles); an array whose partials take more than one level goes alone
+    std::vector<size_t> offs((size_t)count);
+    size_t off = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        offs[(size_t)i] = off;
+        off += dq_workspace_bytes(items[i].nblocks);
+    }
+    char* ws = reinterpret_cast<char*>(workspace);
+    DqGroup g;
+    auto flush = [&]() -> hipError_t {
+        if (g.count == 0) return hipSuccess;
+        hipLaunchKernelGGL(tree_partials_f32_group, dim3((unsigned)g.chunk0[g.count]), dim3(kThreads), 0, s, g);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(dq_quantize_group, dim3((unsigned)g.wg0[g.count]), dim3(kThreads), 0, s, g);
+        e = hipGetLastError();
+        g.count = 0;
+        return e;
+    };
+    g.count = 0;
+    g.chunk0[0] = 0;
+    g.wg0[0] = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const DqItem& it = items[i];
+        double* part = reinterpret_cast<double*>(ws + offs[(size_t)i]);
+        const int64_t chunks = cdiv(it.nblocks, kChunk);
+        if (chunks > kChunk) {
+            const hipError_t e = launch_double_quant(it.absmax, it.nblocks, it.q8, it.scale, it.mean, part, s);
+            if (e != hipSuccess) return e;
+            continue;
+        }
+        const int64_t wgs = cdiv(cdiv(it.nblocks, kDqBlock), kDqBlocksPerWg);
+        // launch sizes stay far below 2^31 workgroups: flush before they could not
+        if (g.count == kMaxDqGroup || (int64_t)g.chunk0[g.count] + chunks > (1 << 30) ||
+            (int64_t)g.wg0[g.count] + wgs > (1 << 30)) {
+            const hipError_t e = flush();
+            if (e != hipSuccess) return e;
+        }
+        const int t = g.count;
+        g.absmax[t] = it.absmax;
+        g.part[t] = part;
+        g.q8[t] = it.q8;
+        g.scale[t] = it.scale;
+        g.mean[t] = it.mean;
+        g.nb[t] = it.nblocks;
+        g.chunk0[t + 1] = g.chunk0[t] + (int32_t)chunks;
+        g.wg0[t + 1] = g.wg0[t] + (int32_t)wgs;
+        g.count = t + 1;
+    }
+    return flush();
 }
 
 }  // namespace qk

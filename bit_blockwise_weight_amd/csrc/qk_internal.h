@@ -98,6 +98,16 @@ hipError_t launch_int8_matmul(const int8_t* Xq, const float* SX, const int8_t* C
 size_t dq_workspace_bytes(int64_t nblocks);
 hipError_t launch_double_quant(const float* absmax, int64_t nblocks, int8_t* q8, float* scale,
                                float* mean, void* workspace, hipStream_t s);
+// one array of a grouped double quantization
+struct DqItem {
+    const float* absmax;
+    int64_t nblocks;
+    int8_t* q8;
+    float* scale;
+    float* mean;
+};
+// workspace: the items' dq_workspace_bytes() back to back, in item order
+hipError_t launch_double_quant_group(const DqItem* items, int32_t count, void* workspace, hipStream_t s);
 
 struct DeqArgs {
     const uint8_t* codes;

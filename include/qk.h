@@ -193,6 +193,40 @@ qk_status qk_double_quant(const float* absmax, int64_t nblocks, int32_t dq_block
                           void* stream);
 
 /*
+ * qk_double_quant_grouped — device.  qk_double_quant of several independent absmax
+ * arrays (the weights of a layer quantized together), same passages and the same
+ * definition per array, in two launches for every run of up to 16 arrays: one for
+ * the fp64 tree partials of all of them, one for their int8 codes (an array of more
+ * than 4096 * 4096 absmax values goes alone).  Each array's q8, scale and mean are
+ * bit-for-bit what qk_double_quant of that array alone writes.
+ *   tasks: host array of ntasks entries, each as the arguments of qk_double_quant:
+ *     absmax: device, [nblocks] fp32 (nblocks >= 1), 4-byte aligned, read;
+ *     q8: device, [nblocks] int8; scale: device, [ceil(nblocks/256)] fp32;
+ *     mean: device, [1] fp32; all written, 4-byte aligned.
+ *   ntasks: 1..256.   dq_blocksize: 256.
+ *   workspace: device, at least qk_double_quant_grouped_workspace_size() bytes for
+ *     the same tasks, 8-byte aligned; contents on entry are ignored.
+ *   No output may overlap another output or any absmax (else QK_ERR_INVALID_ARG).
+ *   Errors: QK_ERR_INVALID_ARG, QK_ERR_UNSUPPORTED, QK_ERR_WORKSPACE, QK_ERR_HIP.
+ */
+typedef struct qk_dq_task {
+    const float* absmax;
+    int64_t nblocks;
+    int8_t* q8;
+    float* scale;
+    float* mean;
+} qk_dq_task;
+
+/*
+ * qk_double_quant_grouped_workspace_size — host.  Bytes of device workspace that
+ * qk_double_quant_grouped needs for these tasks (only nblocks is read).
+ */
+qk_status qk_double_quant_grouped_workspace_size(const qk_dq_task* tasks, int32_t ntasks, size_t* bytes);
+
+qk_status qk_double_quant_grouped(const qk_dq_task* tasks, int32_t ntasks, int32_t dq_blocksize, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * qk_state_init — host.  Fills a descriptor.  Pass absmax for a plain state,
  * or q8 / dq_scale / dq_mean (and absmax == NULL) for a nested one.
  *   levels: host float[16] in code order, copied.

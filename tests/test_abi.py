@@ -383,3 +383,45 @@ def test_gemv_grouped_argument_errors(L):
     assert "overlaps y" in qk.qk_last_error()
     assert call(arr((X0, st, Y0), (X0, st, X0 + 64)), 2, 1, None) == qk.QK_ERR_INVALID_ARG
     assert "overlaps x" in qk.qk_last_error()
+
+
+def test_double_quant_grouped_argument_errors(L):
+    T = qk.DqTask
+
+    def arr(*entries):
+        a = (T * len(entries))()
+        for i, (am, nb, q8, sc, mu) in enumerate(entries):
+            a[i].absmax, a[i].nblocks, a[i].q8, a[i].scale, a[i].mean = am, nb, q8, sc, mu
+        return a
+
+    A0, A1, Q0, Q1, S0, S1, M0, M1 = (0x100000 * k for k in range(1, 9))
+    one = arr((A0, 1000, Q0, S0, M0))
+    two = arr((A0, 1000, Q0, S0, M0), (A1, 5000, Q1, S1, M1))
+    size = ctypes.c_size_t()
+    ws = L.qk_double_quant_grouped_workspace_size
+    assert ws(two, 2, ctypes.byref(size)) == qk.QK_OK
+    assert size.value == qk.qk_double_quant_workspace_size(1000) + qk.qk_double_quant_workspace_size(5000)
+    assert qk.qk_double_quant_grouped_workspace_size([1000, 5000]) == size.value
+    assert ws(None, 1, ctypes.byref(size)) == qk.QK_ERR_INVALID_ARG
+    assert ws(one, 0, ctypes.byref(size)) == qk.QK_ERR_INVALID_ARG
+    assert ws(one, 1, None) == qk.QK_ERR_INVALID_ARG
+    assert ws(arr((A0, 0, Q0, S0, M0)), 1, ctypes.byref(size)) == qk.QK_ERR_INVALID_ARG
+    call = L.qk_double_quant_grouped
+    big = 1 << 20
+    assert call(None, 1, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 0, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 257, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 1, 128, FAKE, big, None) == qk.QK_ERR_UNSUPPORTED
+    assert call(one, 1, 256, None, 0, None) == qk.QK_ERR_WORKSPACE
+    assert call(two, 2, 256, FAKE, qk.qk_double_quant_workspace_size(1000), None) == qk.QK_ERR_WORKSPACE
+    assert call(arr((A0, 1000, None, S0, M0)), 1, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((A0, 0, Q0, S0, M0)), 1, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((A0 + 2, 1000, Q0, S0, M0)), 1, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 1, 256, ctypes.c_void_p(0x10004), big, None) == qk.QK_ERR_INVALID_ARG   # workspace alignment
+    # an output over another task's output, over an absmax, or two outputs of one task
+    assert call(arr((A0, 1000, Q0, S0, M0), (A1, 1000, Q0 + 512, S1, M1)), 2, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    assert "overlaps" in qk.qk_last_error()
+    assert call(arr((A0, 1000, Q0, S0, M0), (A1, 1000, Q1, S1, A0 + 4)), 2, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((A0, 1000, Q0, S0, S0 + 8)), 1, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
+    # two tasks may read the same absmax
+    assert ws(arr((A0, 1000, Q0, S0, M0), (A0, 1000, Q1, S1, M1)), 2, ctypes.byref(size)) == qk.QK_OK
