@@ -236,7 +236,11 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_group_kernel(GemvGroup g) {
     };
     // the tile's first row enters the loads' scalar offsets; rows past the slice's end
     // then lie past the code buffer's range and read zero (their outputs are never
-    // stored), and their scales are other rows' or zero
+    // stored), and their scales are other rows' or zero.  On gfx950 the range check of
+    // a raw buffer load compares the vector plus the scalar offset with the buffer's
+    // size (measured: with 512 bytes in range and a scalar offset of 256, lanes whose
+    // vector offset is 256 or more read zero although their addresses lie inside the
+    // allocation), so a scalar offset cannot carry a load past the buffer.
     auto enter_tile = [&](LoadCur& c) {
         const uint32_t n0 = (uint32_t)(c.item - c.item0) * 16u;
         c.tcode = n0 * (uint32_t)(c.K / 2);
