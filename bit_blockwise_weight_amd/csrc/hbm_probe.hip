@@ -48,3 +48,37 @@ extern "C" int qk_probe_read_stream(const void* src, size_t nbytes, uint32_t* ou
         hipLaunchKernelGGL(read_stream_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p, nbytes / 16, out);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
+
+// The range check of a raw buffer load that writes into LDS: one wave, 64 lanes,
+// lane l loads 16 bytes at vector offset 16 l and the given scalar offset from a
+// resource of num_records = 512 bytes at src (which must hold at least 512 +
+// soffset bytes so that every address stays in the allocation); out[4 l .. 4 l + 4)
+// receives what landed in LDS.  Lanes whose vector + scalar offset reach 512 read
+// zero where the scalar offset takes part in the check.
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__global__ __launch_bounds__(64) void buffer_range_kernel(const uint32_t* src, uint32_t* out, uint32_t soffset) {
+    __shared__ __attribute__((aligned(16))) uint32_t buf[256];
+    const int lane = threadIdx.x;
+    for (int i = 0; i < 4; ++i) buf[4 * lane + i] = 0xFFFFFFFFu;
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(src), (short)0, 512, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)buf, 16, 16u * (uint32_t)lane, soffset, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    for (int i = 0; i < 4; ++i) out[4 * lane + i] = buf[4 * lane + i];
+}
+
+}  // namespace
+
+extern "C" int qk_probe_buffer_range(const void* src, size_t src_bytes, uint32_t* out, uint32_t soffset,
+                                     void* stream) {
+    if (src == nullptr || out == nullptr || soffset % 16 != 0 || src_bytes < 512 + (size_t)soffset + 1024)
+        return 1;
+    hipLaunchKernelGGL(buffer_range_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint32_t*>(src), out, soffset);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
