@@ -5,7 +5,7 @@
 One step = every stage of the path over one Llama-7B-shaped layer set (q, k,
 v, o [4096, 4096]; gate, up [11008, 4096]; down [4096, 11008]; bf16 weights
 ~ N(0, 0.02), synthetic):
-  qk_quantize_blockwise (NF4, block 64) of each of the 7 weights   (a2-a4)
+  qk_quantize_blockwise_grouped (NF4, block 64) of the 7 weights  (a2-a4)
   qk_double_quant_grouped of the 7 absmax arrays                   (a5)
   for each of the 7 weights:
     qk_dequantize to bf16                                          (a6)
@@ -20,7 +20,7 @@ divided by the measured step time, in percent.  The timed region records HIP
 events only around the GEMM calls (the dominant kernel), on the stream the
 kernels run on; `roofline` comes from those.  `breakdown` gives each stage's
 absolute rate from a second pass of K steps with an event after every launch
-(kept out of the timed region: recording an event after each of the 24
+(kept out of the timed region: recording an event after each of the 18
 launches of a step costs a few percent of it).  `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 
 `extra` also times the other workloads (skip with --skip-configs): the practical
@@ -153,7 +153,8 @@ def build_workload(torch, qk, workloads):
     gemm_ws = torch.empty(max(16, qk.qk_gemm_nf4_workspace_size(M_TOK, R)), dtype=torch.uint8, device=dev)
     levels_c = (ctypes.c_float * 16)(*lv.tolist())
     return {"mats": mats, "acts": acts, "lora": lora, "M": M_TOK, "r": R, "levels": lv, "levels_c": levels_c,
-            "gemm_ws": gemm_ws, "dq_call": dq_group_call(torch, qk, mats)}
+            "gemm_ws": gemm_ws, "dq_call": dq_group_call(torch, qk, mats),
+            "q_call": quant_group_call(torch, qk, mats, levels_c)}
 
 
 OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lora"]
@@ -161,15 +162,15 @@ OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lo
 
 def step_calls(torch, qk, wl):
     """The launches of one pass of the hot path over the layer set, in order, as
-    (op, matrices, callable): quantize of each weight, the double quantization of
-    the layer's absmax arrays in one grouped call, per weight dequantize and the
+    (op, matrices, callable): the quantization of the layer's weights and the
+    double quantization of their absmax arrays, one grouped call each, per weight
+    dequantize and the
     prefill GEMM with LoRA; then the decode GEMV of the whole layer at M = 1 and at
     M = 16, one grouped call each (the way a decoder runs a layer)."""
     lv = wl["levels_c"]
     mats = wl["mats"]
     calls = []
-    for m in mats:
-        calls.append(("quantize", [m], lambda m=m: qk.qk_quantize_blockwise(m["w"], 64, lv, m["codes"], m["absmax"])))
+    calls.append(("quantize", list(mats), wl["q_call"]))
     calls.append(("double_quant", list(mats), wl["dq_call"]))
     for m in mats:
         a = wl["acts"][m["K"]]
@@ -424,6 +425,26 @@ def _graph_timed(torch, fn, iters):
     return sec
 
 
+def quant_group_call(torch, qk, mats, levels_c, blocksize=64):
+    """A prepared qk_quantize_blockwise_grouped over the matrices' bf16 weights (the
+    task array built once, so a timed loop pays no Python marshalling)."""
+    arr = (qk.QuantTask * len(mats))()
+    for i, m in enumerate(mats):
+        arr[i].x, arr[i].n = m["w"].data_ptr(), m["w"].numel()
+        arr[i].codes, arr[i].absmax = m["codes"].data_ptr(), m["absmax"].data_ptr()
+    L = qk.lib()
+    n = len(mats)
+
+    def call():
+        rc = L.qk_quantize_blockwise_grouped(arr, n, qk.QK_BF16, blocksize, levels_c,
+                                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"qk_quantize_blockwise_grouped: {qk.qk_last_error()}")
+
+    call.keep = (arr, mats, levels_c)
+    return call
+
+
 def dq_group_call(torch, qk, mats):
     """A prepared qk_double_quant_grouped over the matrices' absmax arrays (the
     task array and the workspace built once, so a timed loop pays no Python
@@ -450,8 +471,9 @@ def dq_group_call(torch, qk, mats):
 def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
     """The 70B-shaped stack: 8 layers of 4 x [8192, 8192], 2 x [28672, 8192] and
     [8192, 28672], bf16 ~ N(0, 0.015) drawn on the device (seeded Philox).  Bulk
-    quantize (NF4 block 64, one call per weight) + double quant (one grouped call
-    per layer) of all 56 weights, then the grouped GEMV (one call per layer, 7
+    quantize (NF4 block 64) + double quant of all 56 weights, one grouped call of
+    each per layer (and the quantization by single calls for comparison), then the
+    grouped GEMV (one call per layer, 7
     weights) at batch 1, 4 and 8, eager and replayed from a HIP graph.  Rates are
     algorithmic bytes over time."""
     dev = torch.device("cuda:0")
@@ -475,8 +497,13 @@ def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
                 "ws": torch.empty(max(8, qk.qk_double_quant_workspace_size(nb)), dtype=torch.uint8, device=dev),
             })
     dq_calls = [dq_group_call(torch, qk, [m for m in mats if m["l"] == l]) for l in range(L)]
+    q_calls = [quant_group_call(torch, qk, [m for m in mats if m["l"] == l], lvc) for l in range(L)]
 
     def quantize_all():
+        for call in q_calls:
+            call()
+
+    def quantize_single_all():
         for m in mats:
             qk.qk_quantize_blockwise(m["w"], 64, lvc, m["codes"], m["absmax"])
 
@@ -494,6 +521,7 @@ def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
 
     t_both = _timed(torch, both, iters)
     t_q = _timed(torch, quantize_all, iters)
+    t_q1 = _timed(torch, quantize_single_all, iters)
     t_dq = _timed(torch, dq_all, iters)
     t_dq1 = _timed(torch, dq_single_all, iters)
     qbytes = sum(bytes_quantize(m["N"] * m["K"]) for m in mats)
@@ -503,13 +531,14 @@ def llama70b_stack(torch, qk, workloads, iters=3, gemv_iters=10):
            "quantize_dq_tb_per_s": round((qbytes + dqbytes) / t_both / 1e12, 3),
            "quantize_dq_frac_of_hbm": round((qbytes + dqbytes) / t_both / HBM_BPS, 4),
            "quantize_only_ms": round(t_q * 1e3, 3), "quantize_only_tb_per_s": round(qbytes / t_q / 1e12, 3),
+           "quantize_single_calls_ms": round(t_q1 * 1e3, 3),
            "dq_only_ms": round(t_dq * 1e3, 3), "dq_us_per_layer_grouped": round(t_dq / L * 1e6, 2),
            "dq_us_per_weight_single_calls": round(t_dq1 / len(mats) * 1e6, 2)}
     for m in mats:
         m["state"] = qk.qk_state_init(qk.NF4, lv, m["N"], m["K"], 64, m["codes"], None, m["q8"], m["scale"],
                                       m["mean"])
         del m["w"], m["absmax"], m["ws"]
-    del dq_calls
+    del dq_calls, q_calls
     torch.cuda.empty_cache()
     layers = [[m for m in mats if m["l"] == l] for l in range(L)]
     gemv = {}

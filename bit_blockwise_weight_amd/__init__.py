@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "QKError", "QuantState", "QuantizedWeight", "NF4", "FP4", "CUSTOM", "lib",
-    "qk_make_codebook", "qk_quantize_blockwise", "qk_double_quant_workspace_size", "qk_double_quant",
+    "qk_make_codebook", "qk_quantize_blockwise", "qk_quantize_blockwise_grouped", "qk_double_quant_workspace_size",
+    "qk_double_quant",
     "qk_double_quant_grouped_workspace_size", "qk_double_quant_grouped",
     "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemv_nf4_grouped", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_gemm_nf4_noalloc", "qk_last_error", "qk_version",
     "qk_backend_info", "quantize",
@@ -69,6 +70,12 @@ class QuantState(ctypes.Structure):
     ]
 
 
+class QuantTask(ctypes.Structure):
+    """qk_quant_task."""
+    _fields_ = [("x", ctypes.c_void_p), ("n", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("absmax", ctypes.c_void_p)]
+
+
 class DqTask(ctypes.Structure):
     """qk_dq_task."""
     _fields_ = [("absmax", ctypes.c_void_p), ("nblocks", ctypes.c_int64), ("q8", ctypes.c_void_p),
@@ -105,6 +112,7 @@ def lib():
     sigs = {
         "qk_make_codebook": [i32, ctypes.POINTER(ctypes.c_float)],
         "qk_quantize_blockwise": [vp, i32, i64, i32, ctypes.POINTER(ctypes.c_float), vp, vp, vp],
+        "qk_quantize_blockwise_grouped": [ctypes.POINTER(QuantTask), i32, i32, i32, ctypes.POINTER(ctypes.c_float), vp],
         "qk_double_quant_workspace_size": [i64, ctypes.POINTER(ctypes.c_size_t)],
         "qk_double_quant": [vp, i64, i32, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "qk_double_quant_grouped_workspace_size": [ctypes.POINTER(DqTask), i32, ctypes.POINTER(ctypes.c_size_t)],
@@ -213,6 +221,41 @@ def qk_quantize_blockwise(x: torch.Tensor, blocksize: int = 64, levels=None, cod
         _check(lib().qk_quantize_blockwise(_ptr(x), _DTYPE_CODE[x.dtype], n, int(blocksize), lv, _ptr(codes),
                                            _ptr(absmax), ctypes.c_void_p(_stream(x))))
     return codes, absmax
+
+
+def qk_quantize_blockwise_grouped(xs, blocksize: int = 64, levels=None, codes=None, absmaxes=None):
+    """qk_quantize_blockwise of several tensors of one dtype in one launch per run of
+    up to 16; returns [(codes, absmax)] in the order of xs."""
+    xs = list(xs)
+    if not xs:
+        raise ValueError("grouped quantization needs at least one tensor")
+    dt = xs[0].dtype
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported input dtype {dt}")
+    if levels is None:
+        levels = qk_make_codebook(NF4)
+    lv, _ = _levels_arg(levels)
+    arr = (QuantTask * len(xs))()
+    outs = []
+    for i, x in enumerate(xs):
+        if x.dtype != dt:
+            raise ValueError(f"task {i}: every tensor needs the dtype of the first ({dt}), got {x.dtype}")
+        _require_cuda(x)
+        n = x.numel()
+        c = codes[i] if codes is not None else torch.empty((n + 1) // 2, dtype=torch.uint8, device=x.device)
+        a = absmaxes[i] if absmaxes is not None else torch.empty((n + blocksize - 1) // blocksize,
+                                                                 dtype=torch.float32, device=x.device)
+        _require_cuda(c, a)
+        if c.dtype != torch.uint8 or c.numel() < (n + 1) // 2:
+            raise ValueError(f"task {i}: codes must be uint8 with at least {(n + 1) // 2} elements")
+        if a.dtype != torch.float32 or a.numel() < (n + blocksize - 1) // blocksize:
+            raise ValueError(f"task {i}: absmax must be fp32 with at least {(n + blocksize - 1) // blocksize} elements")
+        arr[i].x, arr[i].n, arr[i].codes, arr[i].absmax = _ptr(x), n, _ptr(c), _ptr(a)
+        outs.append((c, a))
+    with _on(xs[0].device):
+        _check(lib().qk_quantize_blockwise_grouped(arr, len(xs), _DTYPE_CODE[dt], int(blocksize), lv,
+                                                   ctypes.c_void_p(_stream(xs[0]))))
+    return outs
 
 
 def qk_make_dynamic_map(signed: bool = True) -> torch.Tensor:

@@ -133,7 +133,8 @@ qk_status qk_quantize_blockwise(const void* x, int32_t x_dtype, int64_t n, int32
                                 uint8_t* codes, float* absmax, void* stream) {
     if (!x || !levels || !codes || !absmax)
         return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: NULL pointer argument");
-    if (n < 1) return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: n must be >= 1 (got %lld)", (long long)n);
+    if (n < 1 || n > ((int64_t)1 << 40))
+        return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: n must be in 1..2^40 (got %lld)", (long long)n);
     if (x_dtype != QK_BF16 && x_dtype != QK_F16 && x_dtype != QK_F32)
         return fail(QK_ERR_INVALID_ARG, "qk_quantize_blockwise: unknown x dtype %d", x_dtype);
     if (!valid_blocksize(blocksize))
@@ -149,6 +150,57 @@ qk_status qk_quantize_blockwise(const void* x, int32_t x_dtype, int64_t n, int32
     return launched(qk::launch_quantize(x, x_dtype, n, blocksize, lut, codes, absmax,
                                         reinterpret_cast<hipStream_t>(stream)),
                     "qk_quantize_blockwise");
+}
+
+qk_status qk_quantize_blockwise_grouped(const qk_quant_task* tasks, int32_t ntasks, int32_t x_dtype,
+                                        int32_t blocksize, const float* levels, void* stream) {
+    const char* who = "qk_quantize_blockwise_grouped";
+    if (!tasks || !levels) return fail(QK_ERR_INVALID_ARG, "%s: NULL tasks or levels", who);
+    if (ntasks < 1 || ntasks > 256) return fail(QK_ERR_INVALID_ARG, "%s: ntasks must be in 1..256 (got %d)", who, ntasks);
+    if (x_dtype != QK_BF16 && x_dtype != QK_F16 && x_dtype != QK_F32)
+        return fail(QK_ERR_INVALID_ARG, "%s: unknown x dtype %d", who, x_dtype);
+    if (!valid_blocksize(blocksize))
+        return fail(QK_ERR_INVALID_ARG, "%s: block size %d (expected 64, 128 or 256)", who, blocksize);
+    const uintptr_t esize = x_dtype == QK_F32 ? 4 : 2;
+    struct Span {
+        uintptr_t lo, hi;
+        bool out;
+        int32_t task;
+    };
+    std::vector<Span> spans;
+    std::vector<qk::QuantItem> items((size_t)ntasks);
+    for (int32_t i = 0; i < ntasks; ++i) {
+        const qk_quant_task& t = tasks[i];
+        if (!t.x || !t.codes || !t.absmax) return fail(QK_ERR_INVALID_ARG, "%s: task %d: NULL pointer argument", who, i);
+        if (t.n < 1 || t.n > ((int64_t)1 << 40))
+            return fail(QK_ERR_INVALID_ARG, "%s: task %d: n must be in 1..2^40 (got %lld)", who, i, (long long)t.n);
+        if (!aligned(t.x, 16) || !aligned(t.codes, 4) || !aligned(t.absmax, 4))
+            return fail(QK_ERR_INVALID_ARG, "%s: task %d: x must be 16-byte aligned, codes and absmax 4-byte", who, i);
+        const uintptr_t n = (uintptr_t)t.n;
+        const uintptr_t nb = (n + (uintptr_t)blocksize - 1) / (uintptr_t)blocksize;
+        spans.push_back({reinterpret_cast<uintptr_t>(t.x), reinterpret_cast<uintptr_t>(t.x) + esize * n, false, i});
+        spans.push_back({reinterpret_cast<uintptr_t>(t.codes), reinterpret_cast<uintptr_t>(t.codes) + (n + 1) / 2, true, i});
+        spans.push_back({reinterpret_cast<uintptr_t>(t.absmax), reinterpret_cast<uintptr_t>(t.absmax) + 4 * nb, true, i});
+        items[(size_t)i] = qk::QuantItem{t.x, t.n, t.codes, t.absmax};
+    }
+    for (size_t a = 0; a < spans.size(); ++a) {
+        if (!spans[a].out) continue;
+        for (size_t b = 0; b < spans.size(); ++b) {
+            if (a == b) continue;
+            if (spans[a].lo < spans[b].hi && spans[b].lo < spans[a].hi)
+                return fail(QK_ERR_INVALID_ARG, "%s: an output of task %d overlaps %s of task %d", who, spans[a].task,
+                            spans[b].out ? "an output" : "the input", spans[b].task);
+        }
+    }
+    qk::QuantLut lut;
+    const char* why = "";
+    const qk_status lst = qk::build_quant_lut(levels, &lut, &why);
+    if (lst != QK_OK) return fail(lst, "%s: %s", who, why);
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_quantize_group(items.data(), ntasks, x_dtype, blocksize, lut,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                    who);
 }
 
 qk_status qk_make_dynamic_map(int32_t is_signed, float* levels_out) {

@@ -81,6 +81,15 @@ int device_cu_count();
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize,
                            const QuantLut& lut, uint8_t* codes, float* absmax, hipStream_t s);
+// one array of a grouped quantization (same dtype, block size and level table for all)
+struct QuantItem {
+    const void* x;
+    int64_t n;
+    uint8_t* codes;
+    float* absmax;
+};
+hipError_t launch_quantize_group(const QuantItem* items, int32_t count, int32_t x_dtype, int32_t blocksize,
+                                 const QuantLut& lut, hipStream_t s);
 
 hipError_t launch_quantize8(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize, const QuantLut8& lut,
                             uint8_t* codes, float* absmax, hipStream_t s);

@@ -147,7 +147,7 @@ qk_status qk_make_codebook(int32_t kind, float* levels_out);
  *   and the codes are packed two per byte, high nibble first.
  *   x:         device, [n] elements of x_dtype (QK_BF16, QK_F16 or QK_F32),
  *              16-byte aligned.
- *   n:         number of elements, >= 1.
+ *   n:         number of elements, 1..2^40.
  *   blocksize: 64, 128 or 256.
  *   levels:    host, float[16] in code order (any finite table in [-1, 1]
  *              whose distinct values have binary64-exact midpoints; both
@@ -161,6 +161,32 @@ qk_status qk_make_codebook(int32_t kind, float* levels_out);
  */
 qk_status qk_quantize_blockwise(const void* x, int32_t x_dtype, int64_t n, int32_t blocksize,
                                 const float* levels, uint8_t* codes, float* absmax, void* stream);
+
+/*
+ * qk_quantize_blockwise_grouped — device.  qk_quantize_blockwise of several
+ * independent tensors (the weights of a layer) that share the input dtype, the
+ * block size and the level table, same passages and the same definition per
+ * tensor, in one launch for every run of up to 16 tensors of fewer than 2^26
+ * elements (a larger tensor streams best in a launch of its own and gets one).
+ * Each tensor's codes and absmax are bit-for-bit what qk_quantize_blockwise of
+ * that tensor alone writes.
+ *   tasks: host array of ntasks entries, each as the arguments of
+ *     qk_quantize_blockwise: x (device, [n] elements, 16-byte aligned, read),
+ *     n in 1..2^40, codes (device, [ceil(n/2)] bytes, 4-byte aligned, written),
+ *     absmax (device, [ceil(n/blocksize)] fp32, 4-byte aligned, written).
+ *   ntasks: 1..256.   x_dtype, blocksize, levels: as for qk_quantize_blockwise.
+ *   No output may overlap another output or any input (else QK_ERR_INVALID_ARG).
+ *   Errors: those of qk_quantize_blockwise.
+ */
+typedef struct qk_quant_task {
+    const void* x;
+    int64_t n;
+    uint8_t* codes;
+    float* absmax;
+} qk_quant_task;
+
+qk_status qk_quantize_blockwise_grouped(const qk_quant_task* tasks, int32_t ntasks, int32_t x_dtype,
+                                        int32_t blocksize, const float* levels, void* stream);
 
 /*
  * qk_double_quant_workspace_size — host.  Bytes of device workspace that

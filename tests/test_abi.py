@@ -425,3 +425,37 @@ def test_double_quant_grouped_argument_errors(L):
     assert call(arr((A0, 1000, Q0, S0, S0 + 8)), 1, 256, FAKE, big, None) == qk.QK_ERR_INVALID_ARG
     # two tasks may read the same absmax
     assert ws(arr((A0, 1000, Q0, S0, M0), (A0, 1000, Q1, S1, M1)), 2, ctypes.byref(size)) == qk.QK_OK
+
+
+def test_quantize_grouped_argument_errors(L):
+    T = qk.QuantTask
+    lv = _levels()
+
+    def arr(*entries):
+        a = (T * len(entries))()
+        for i, (x, n, c, am) in enumerate(entries):
+            a[i].x, a[i].n, a[i].codes, a[i].absmax = x, n, c, am
+        return a
+
+    X0, X1, C0, C1, A0, A1 = (0x1000000 * k for k in range(1, 7))
+    one = arr((X0, 4096, C0, A0))
+    call = L.qk_quantize_blockwise_grouped
+    assert call(None, 1, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 1, qk.QK_BF16, 64, None, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 0, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 257, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 1, 9, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(one, 1, qk.QK_BF16, 32, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((X0, 0, C0, A0)), 1, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((X0, (1 << 40) + 1, C0, A0)), 1, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((None, 4096, C0, A0)), 1, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((X0 + 8, 4096, C0, A0)), 1, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG   # x alignment
+    assert call(arr((X0, 4096, C0 + 2, A0)), 1, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG   # codes alignment
+    # an output over another task's output or over an input (bf16: 2 bytes per element)
+    assert call(arr((X0, 4096, C0, A0), (X1, 4096, C0 + 1024, A1)), 2, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert "overlaps" in qk.qk_last_error()
+    assert call(arr((X0, 4096, C0, A0), (X1, 4096, C1, X0 + 8188)), 2, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((X0, 4096, C0, C0 + 2044)), 1, qk.QK_BF16, 64, lv, None) == qk.QK_ERR_INVALID_ARG
+    bad = (ctypes.c_float * 16)(*([2.0] * 16))
+    assert call(one, 1, qk.QK_BF16, 64, bad, None) == qk.QK_ERR_INVALID_ARG
+    assert L.qk_quantize_blockwise(FAKE, qk.QK_BF16, (1 << 40) + 1, 64, lv, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
