@@ -108,3 +108,18 @@ def test_grouped_with_a_tensor_launched_alone():
     for i, ((c, a), (sc, sa)) in enumerate(zip(got, single)):
         assert_bits_equal(host(c), host(sc), f"tensor {i} codes")
         assert_bits_equal(host(a), host(sa), f"tensor {i} absmax")
+
+
+def test_grouped_of_tensors_smaller_than_a_batch():
+    """Every tensor under one batch (1024 elements): the launch has no full batch and
+    every unit goes through the per-element tail path."""
+    lv = ocb.nf4_levels()
+    sizes = [1, 2, 33, 511, 512, 513, 1023]
+    vals, devs = _inputs(torch.bfloat16, sizes, seed=17)
+    say(f"case: grouped quantize of {len(sizes)} tensors under 1024 elements")
+    got = qk.qk_quantize_blockwise_grouped(devs, 64, torch.from_numpy(lv))
+    torch.cuda.synchronize()
+    for n, v, (c, a) in zip(sizes, vals, got):
+        oc, oa = obw.quantize_blockwise(v, 64, lv)
+        assert_bits_equal(host(c), oc, f"n={n} codes vs oracle")
+        assert_bits_equal(host(a), oa, f"n={n} absmax vs oracle")
