@@ -38,6 +38,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128;
 constexpr int BN = 128;
@@ -67,7 +68,11 @@ __device__ __forceinline__ uint32_t deq_pair(const float* lev, uint32_t byte, fl
     return pack_bf16x2(__fmul_rn(lev[byte >> 4], sc), __fmul_rn(lev[byte & 15u], sc));
 }
 
-template <bool kGeneric, bool kLora>
+// kVecGen (generic path, K < 2^22): X, codes and block scales of a step are fetched with
+// 16-byte buffer loads from 4-byte aligned bases (rows past M and codes past the weight
+// read zero through the range check; a row's elements past K are masked), not element by
+// element; the dequantized values are the same.
+template <bool kGeneric, bool kLora, bool kVecGen>
 __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
     __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN * kLdsStride];
@@ -97,9 +102,35 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
     uint4 xr[4];
     uint4 cr;
     float csc;
-    uint16_t xg[kGeneric ? 32 : 1];   // generic path: 32 X elements per thread
-    uint32_t cg[kGeneric ? 16 : 1];   // generic path: 16 packed code bytes (re-packed)
-    float scg[kGeneric ? 32 : 1];
+    uint16_t xg[kGeneric && !kVecGen ? 32 : 1];   // generic path: 32 X elements per thread
+    uint32_t cg[kGeneric && !kVecGen ? 16 : 1];   // generic path: 16 packed code bytes (re-packed)
+    float scg[kGeneric && !kVecGen ? 32 : 1];
+    // vectorized generic path: the thread's 32 X elements as 16 words, its 32 codes as 4
+    // words (first element in the high nibble), the block scales and where they change
+    uint32_t xq[kVecGen ? 16 : 1];
+    uint32_t cq[kVecGen ? 4 : 1];
+    float vsc0 = 0.0f, vsc1 = 0.0f;
+    int vsplit = 32, vlive = 32;
+    // per-tile buffer resources over 4-byte aligned bases: X rows m0 .. m0 + BM and the
+    // codes of weight rows n0 .. n0 + BN
+    __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
+    __amdgpu_buffer_rsrc_t crs = xrs;
+    uint32_t x_mis = 0, c_mis = 0, c_phase0 = 0;
+    if constexpr (kVecGen) {
+        const uintptr_t xa = reinterpret_cast<uintptr_t>(a.X + m0 * K);
+        x_mis = (uint32_t)(xa & 3u);
+        const int64_t xrows = M - m0 < BM ? M - m0 : BM;
+        xrs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(xa - x_mis), (short)0,
+                                               (int32_t)(xrows * K * 2 + x_mis), 0x00020000);
+        const int64_t cfirst = n0 * K;                       // flat element of the tile's first weight
+        const uintptr_t ca = reinterpret_cast<uintptr_t>(a.w.codes + (cfirst >> 1));
+        c_mis = (uint32_t)(ca & 3u);
+        c_phase0 = (uint32_t)(cfirst & 1);
+        const int64_t wrows = N - n0 < BN ? N - n0 : BN;
+        const int64_t cend = (cfirst + wrows * K + 1) >> 1;  // bytes of the tile's weights end here
+        crs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ca - c_mis), (short)0,
+                                               (int32_t)(cend - (cfirst >> 1) + c_mis), 0x00020000);
+    }
     constexpr int kAPer = kLora ? kMaxRank * BK / kThreads : 1;   // 16
     uint16_t ag[kAPer];               // LoRA A^T elements owned by this thread
 
@@ -120,6 +151,71 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
             } else {
                 cr = make_uint4(0, 0, 0, 0);
                 csc = 0.0f;
+            }
+        } else if constexpr (kVecGen) {
+            // X: row tid / 2 of the tile, elements k0 + 32 h + [0, 32): 17 words from the
+            // 4-byte aligned byte offset, shifted by one half word when the row starts there
+            {
+                const int row = tid >> 1, h = tid & 1;
+                const uint32_t xb = x_mis + 2u * (uint32_t)(row * K + k0 + 32 * h);
+                const uint32_t xb4 = xb & ~3u;
+                uint32_t w[17];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrs, xb4 + 16u * q, 0, 0));
+                    w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
+                }
+                w[16] = __builtin_amdgcn_raw_buffer_load_b32(xrs, xb4 + 64u, 0, 0);
+                const uint32_t sh = xb & 2u;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) xq[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], sh);
+                // elements past the row's end (the last step of a K that is not a multiple of 64)
+                const int64_t kb = k0 + 32 * h;
+                if (kb + 32 > K) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const uint32_t lo = kb + 2 * j < K ? 0x0000FFFFu : 0u;
+                        const uint32_t hi = kb + 2 * j + 1 < K ? 0xFFFF0000u : 0u;
+                        xq[j] &= lo | hi;
+                    }
+                }
+            }
+            // W: weight row n0 + tid / 2, elements k0 + 32 whalf + [0, 32) (flat er from the
+            // tile's first weight): 20 bytes from the aligned byte offset, the 16 or 17 bytes of
+            // the run realigned, the nibble stream moved by one when the run starts odd
+            {
+                const uint32_t er = (uint32_t)(wrow * K + k0 + 32 * whalf);
+                const uint32_t ep = c_phase0 + er;                  // from the tile's first byte
+                const uint32_t cb = c_mis + (ep >> 1);
+                const uint32_t cb4 = cb & ~3u;
+                const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cb4, 0, 0));
+                const uint32_t w4 = __builtin_amdgcn_raw_buffer_load_b32(crs, cb4 + 16u, 0, 0);
+                const uint32_t w[5] = {v[0], v[1], v[2], v[3], w4};
+                const uint32_t csh = cb & 3u;
+                uint32_t o[5];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], csh);
+                o[4] = w[4] >> (8u * csh);
+                if (ep & 1u) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        cq[j] = ((o[j] << 4) & 0xF0F0F0F0u) | ((__builtin_amdgcn_alignbyte(o[j + 1], o[j], 1) >> 4) & 0x0F0F0F0Fu);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cq[j] = o[j];
+                }
+                // block scales: the run's elements fall in the block of its first element and
+                // perhaps the next; elements past the row's end (and rows past N) get scale 0
+                const int64_t e0 = wn_row * K + k0 + 32 * whalf;
+                const int64_t kb = k0 + 32 * whalf;
+                vlive = !wrow_ok ? 0 : (kb + 32 <= K ? 32 : (kb < K ? (int)(K - kb) : 0));
+                if (vlive > 0) {
+                    const int64_t blk0 = e0 >> a.w.blocksize_log2;
+                    const int64_t into = e0 & (a.w.blocksize - 1);
+                    vsplit = a.w.blocksize - into < 32 ? (int)(a.w.blocksize - into) : 32;
+                    vsc0 = wscale(a.w, blk0);
+                    vsc1 = vsplit < vlive ? wscale(a.w, blk0 + 1) : vsc0;
+                }
             }
         } else {
             // X: thread handles row tid/2, 32 elements starting at (tid%2)*32
@@ -173,6 +269,23 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
             for (int q = 0; q < 4; ++q) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b) o[4 * q + b] = deq_pair(lev, (cw[q] >> (8 * b)) & 0xFFu, csc);
+            }
+            uint4* dst = reinterpret_cast<uint4*>(&ws[buf][wrow * kLdsStride + whalf * 32]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        } else if constexpr (kVecGen) {
+            const int row = tid >> 1, h = tid & 1;
+            uint4* xd = reinterpret_cast<uint4*>(&xs[buf][row * kLdsStride + h * 32]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xd[q] = make_uint4(xq[4 * q], xq[4 * q + 1], xq[4 * q + 2], xq[4 * q + 3]);
+            uint32_t o[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const uint32_t byte = (cq[m >> 2] >> (8 * (m & 3))) & 0xFFu;
+                const int i0 = 2 * m, i1 = 2 * m + 1;
+                const float s0 = i0 < vlive ? (i0 < vsplit ? vsc0 : vsc1) : 0.0f;
+                const float s1 = i1 < vlive ? (i1 < vsplit ? vsc0 : vsc1) : 0.0f;
+                o[m] = pack_bf16x2(__fmul_rn(lev[byte >> 4], s0), __fmul_rn(lev[byte & 15u], s1));
             }
             uint4* dst = reinterpret_cast<uint4*>(&ws[buf][wrow * kLdsStride + whalf * 32]);
 #pragma unroll
@@ -340,13 +453,13 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
     }
 }
 
-template <bool kGeneric>
+template <bool kGeneric, bool kVecGen>
 hipError_t launch_typed(const GemmArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
     if (a.A)
-        hipLaunchKernelGGL((gemm_tile128_kernel<kGeneric, true>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((gemm_tile128_kernel<kGeneric, true, kVecGen>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((gemm_tile128_kernel<kGeneric, false>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((gemm_tile128_kernel<kGeneric, false, kVecGen>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1003,8 +1116,13 @@ hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A
         *variant = "mfma 32x32x16 bf16, 256x256x64 tiles, W dequantized into B fragments, LoRA X*A pre-pass + epilogue";
         return launch_fast(a, workspace, s);
     }
+    // the vectorized generic loads use 32-bit byte offsets within a 128-row tile
+    if (w.K < ((int64_t)1 << 22)) {
+        *variant = "generic (16-byte loads realigned, flat-index block scales), 128x128x64 tiles";
+        return launch_typed<true, true>(a, s);
+    }
     *variant = "generic (element loads, flat-index dequantization), 128x128x64 tiles";
-    return launch_typed<true>(a, s);
+    return launch_typed<true, false>(a, s);
 }
 
 }  // namespace qk
