@@ -112,7 +112,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
     float vsc0 = 0.0f, vsc1 = 0.0f;
     int vsplit = 32, vlive = 32;
     // per-tile buffer resources over 4-byte aligned bases: X rows m0 .. m0 + BM and the
-    // codes of weight rows n0 .. n0 + BN
+    // codes of weight rows n0 .. n0 + BN.  Each range is rounded up to whole dwords, so a
+    // dword that holds the last element is read whole whichever way the hardware checks a
+    // dword that straddles the end; the extra bytes share that dword's page and feed only
+    // masked elements.
     __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
     __amdgpu_buffer_rsrc_t crs = xrs;
     uint32_t x_mis = 0, c_mis = 0, c_phase0 = 0;
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
         x_mis = (uint32_t)(xa & 3u);
         const int64_t xrows = M - m0 < BM ? M - m0 : BM;
         xrs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(xa - x_mis), (short)0,
-                                               (int32_t)(xrows * K * 2 + x_mis), 0x00020000);
+                                               (int32_t)((xrows * K * 2 + x_mis + 3) & ~3LL), 0x00020000);
         const int64_t cfirst = n0 * K;                       // flat element of the tile's first weight
         const uintptr_t ca = reinterpret_cast<uintptr_t>(a.w.codes + (cfirst >> 1));
         c_mis = (uint32_t)(ca & 3u);
@@ -129,10 +132,27 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
         const int64_t wrows = N - n0 < BN ? N - n0 : BN;
         const int64_t cend = (cfirst + wrows * K + 1) >> 1;  // bytes of the tile's weights end here
         crs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ca - c_mis), (short)0,
-                                               (int32_t)(cend - (cfirst >> 1) + c_mis), 0x00020000);
+                                               (int32_t)((cend - (cfirst >> 1) + c_mis + 3) & ~3LL), 0x00020000);
     }
     constexpr int kAPer = kLora ? kMaxRank * BK / kThreads : 1;   // 16
     uint16_t ag[kAPer];               // LoRA A^T elements owned by this thread
+    // vectorized generic path with r % 8 == 0: the step's A rows k0 .. k0 + 64 are one
+    // contiguous run of 64 r elements; piece p = tid + 256 v holds its elements 8 p .. 8 p + 8,
+    // which lie in one row kk = 8 p / r, ranks 8 p % r + [0, 8)
+    constexpr int kAPieces = kLora ? kMaxRank * BK / 8 / kThreads : 1;   // 2
+    uint32_t aq[kAPieces][4];
+    int64_t vk0 = 0;                  // the k0 of the pieces in aq
+    const bool a_vec = kVecGen && kLora && (a.r % 8) == 0;
+    __amdgpu_buffer_rsrc_t ars = xrs;
+    uint32_t a_mis = 0;
+    if constexpr (kVecGen && kLora) {
+        if (a_vec) {
+            const uintptr_t aa = reinterpret_cast<uintptr_t>(a.A);
+            a_mis = (uint32_t)(aa & 3u);
+            ars = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(aa - a_mis), (short)0,
+                                                   (int32_t)((K * a.r * 2 + a_mis + 3) & ~3LL), 0x00020000);
+        }
+    }
 
     auto load_step = [&](int64_t kt) {
         const int64_t k0 = kt * BK;
@@ -243,6 +263,23 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
                 scg[i] = sc;
             }
         }
+        if constexpr (kLora && kVecGen) {
+            if (a_vec) {
+                vk0 = k0;
+#pragma unroll
+                for (int v = 0; v < kAPieces; ++v) {
+                    const uint32_t p = (uint32_t)(tid + kThreads * v);
+                    const uint32_t ab = a_mis + 2u * (uint32_t)(k0 * a.r + 8 * p);
+                    const uint32_t ab4 = ab & ~3u;
+                    const u32x4_t w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ars, ab4, 0, 0));
+                    const uint32_t w4 = __builtin_amdgcn_raw_buffer_load_b32(ars, ab4 + 16u, 0, 0);
+                    const uint32_t ww[5] = {w[0], w[1], w[2], w[3], w4};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) aq[v][q] = __builtin_amdgcn_alignbyte(ww[q + 1], ww[q], ab & 2u);
+                }
+                return;
+            }
+        }
         if constexpr (kLora) {
             // A^T tile: [rpad][BK]; thread covers elements e = tid + 256 * v of rpad*BK
 #pragma unroll
@@ -301,6 +338,22 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
                     (uint16_t)(pack_bf16x2(__fmul_rn(lev[code], scg[i]), 0.0f) & 0xFFFFu);
             }
         }
+        if constexpr (kLora && kVecGen) {
+            if (a_vec) {
+                // the step's k0 is the one loaded for this buffer: rows past K are zero
+#pragma unroll
+                for (int v = 0; v < kAPieces; ++v) {
+                    const int p = tid + kThreads * v;
+                    if (p >= 8 * a.r) continue;
+                    const int kk = (8 * p) / a.r, j0 = (8 * p) % a.r;
+                    const bool live = vk0 + kk < K;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        as_[(j0 + i) * kLdsStride + kk] = live ? (uint16_t)(aq[v][i >> 1] >> ((i & 1) ? 16 : 0)) : (uint16_t)0;
+                }
+                return;
+            }
+        }
         if constexpr (kLora) {
 #pragma unroll
             for (int v = 0; v < kAPer; ++v) {
@@ -326,6 +379,13 @@ __global__ __launch_bounds__(kThreads) void gemm_tile128_kernel(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) tacc[i][j][r] = 0.0f;
 
+    if constexpr (kLora && kVecGen) {
+        // ranks r .. rpad of the A^T tile stay zero: the vectorized stores never write them
+        if (a_vec) {
+            for (int e = tid; e < (rpad - a.r) * BK; e += kThreads)
+                as_[(a.r + e / BK) * kLdsStride + (e % BK)] = (uint16_t)0;
+        }
+    }
     __syncthreads();   // lev ready
     load_step(0);
     store_step(0);

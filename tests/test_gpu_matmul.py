@@ -210,3 +210,31 @@ def test_gemm_edge_generic_path(B, kind):
     ref = omm.qlora_forward_f64(bf16_bits_to_f32(X).reshape(M, K), wd, bf16_bits_to_f32(A).reshape(K, r),
                                 bf16_bits_to_f32(Bm).reshape(r, N), 2.0)
     check_close(bf16_bits_to_f32(Y).reshape(M, N), ref, "gemm edge")
+
+
+def _at_offset(bits: np.ndarray, off: int, shape) -> torch.Tensor:
+    """A device bf16 tensor of `shape` whose data starts `off` elements into a
+    larger allocation, so its address is 2-byte but not 4- or 16-byte aligned."""
+    flat = dev_bf16(np.concatenate([np.zeros(off, dtype=np.uint16), bits.reshape(-1)]))
+    return flat[off:].reshape(shape)
+
+
+@pytest.mark.parametrize("r", [8, 24, 64, 16, 17, 1])
+@pytest.mark.parametrize("xoff,aoff", [(0, 0), (1, 1), (3, 2)])
+def test_gemm_generic_lora_ranks_and_offsets(r, xoff, aoff):
+    """K = 333 (blocks straddle rows, odd row starts) with X and A at element
+    offsets: the generic kernel's realigned X, code and LoRA A loads, including
+    ranks that leave padding rows of the A tile (8, 24) and ranks not a multiple
+    of 8, which take the element loads."""
+    M, N, K, B = 130, 200, 333, 64
+    say(f"case: gemm generic M={M} N={N} K={K} r={r} xoff={xoff} aoff={aoff}")
+    g = np.random.default_rng(1000 + r)
+    W = ofl.f32_to_bf16_bits(g.standard_normal((N, K)).astype(np.float32) * np.float32(0.02))
+    X = ofl.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    A, Bm = _lora(K, N, r, 7 + r)
+    qw = _quantized(W, N, K, B, ocb.NF4, True)
+    Y = host(qw.gemm(_at_offset(X, xoff, (M, K)), _at_offset(A, aoff, (K, r)), dev_bf16(Bm).reshape(r, N), 2.0))
+    wd = oracle_wd(W, N, K, B, ocb.NF4, True)
+    ref = omm.qlora_forward_f64(bf16_bits_to_f32(X).reshape(M, K), wd, bf16_bits_to_f32(A).reshape(K, r),
+                                bf16_bits_to_f32(Bm).reshape(r, N), 2.0)
+    check_close(bf16_bits_to_f32(Y).reshape(M, N), ref, "gemm generic lora")
