@@ -16,7 +16,8 @@
 //   * 2 <= M <= 16: gemv_rows_kernel.  One workgroup per group of 8 consecutive
 //     tiles of one slice; each wave owns a tile and walks its rows from k = 0 to K,
 //     the 8 waves taking the same job at the same time so that the x chunk of a
-//     job (M rows x 1 KB) is copied to LDS once and shared.
+//     job (M rows x 1 KB) is copied to LDS once and shared.  At M <= 4 two waves
+//     share a tile (its even and its odd jobs) and a workgroup owns 4 tiles.
 //   Both: a job's codes (16 rows x 256 bytes) arrive by 4 buffer loads with the
 //   LDS bit and the nontemporal hint, each fetching 256 contiguous bytes of 4 rows
 //   into the wave's own LDS slot (piece p of row r in slot 16 r + (p ^ r), so the
@@ -622,13 +623,22 @@ __device__ __forceinline__ int xswz(int m) {
 // slot, after the barrier that ends every wave's use of that slot.  x row m sits in its
 // slot with its 16-byte units XOR-swizzled (unit u at u ^ xswz(m), the swizzle applied to
 // the global offsets of the copy); see xswz for the bank groups of the fragment reads.
-template <int S, int MX, bool kNested, int QS, bool kAligned>
+//
+// kPair: the S waves own S / 2 tiles, two waves a tile, which take its even and its odd
+// jobs; a step of the loop then covers two jobs (1024 k), whose x chunks the x slot holds
+// side by side (row-chunk 2 m + c = chunk c of row m), and the two waves' sums are added
+// through LDS at the end.  A workgroup then owns 64 rows, not 128: where one weight's rows
+// are much longer than the others' (the down projection of a layer), the hardware
+// dispatcher can balance the smaller workgroups over the CUs more evenly.
+template <int S, int MX, bool kNested, int QS, bool kAligned, bool kPair>
 __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
     constexpr int C = kTabCopies;
     constexpr int kJobQ = kChunkBlocks >> QS;
     constexpr int kLc = (kNested || QS == 0 ? 2 : 1) + 4;   // a job's scale loads and code copies
-    constexpr int kXL = (MX + S - 1) / S;                     // x rows a wave copies per job
-    constexpr int kXR = kXL * S;                              // rows of an x slot (rows >= MX are never read)
+    constexpr int kTiles = kPair ? S / 2 : S;                 // tiles of a workgroup
+    constexpr int kXC = kPair ? 2 * MX : MX;                  // row-chunks (1 KB each) of an x slot in use
+    constexpr int kXL = (kXC + S - 1) / S;                    // row-chunks a wave copies per step
+    constexpr int kXR = kXL * S;                              // row-chunks of an x slot (those >= kXC are never read)
     __shared__ __attribute__((aligned(4096))) uint32_t tab[256 * C];
     __shared__ __attribute__((aligned(1024))) uint4 cb0[S * 256];
     __shared__ __attribute__((aligned(1024))) uint4 cb1[S * 256];
@@ -649,7 +659,9 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
     const int32_t K = T.K;
     const int32_t nchunk = T.nchunk;
     const uint32_t row_bytes = (uint32_t)(K / 2);
-    const int32_t n0 = ((item - T.item0) * S + wave) * 16;   // may be past N: rows clamped, never stored
+    const int tw = kPair ? (wave & (kTiles - 1)) : wave;      // this wave's tile in the workgroup
+    const int hf = kPair ? wave / kTiles : 0;                 // kPair: the wave takes jobs 2 i + hf
+    const int32_t n0 = ((item - T.item0) * kTiles + tw) * 16;   // may be past N: rows clamped, never stored
     const float mu = kNested ? *(const __attribute__((address_space(4))) float*)(uintptr_t)T.dq_mean : 0.0f;
     const __amdgpu_buffer_rsrc_t cr = buf_rsrc(T.codes, T.code_bytes);
     const __amdgpu_buffer_rsrc_t xr = buf_rsrc(T.x, M * K * 2);
@@ -704,9 +716,11 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr_t)(cdst + i * 1024), 16, off, 0, 0, kStream);
         }
     };
-    // x rows m = wave + S i of job j, unit L of the row from global unit L ^ m (k past the
-    // row in a partial chunk reads zero).  Rows m >= M copy row M - 1 (they feed only
-    // outputs that are never stored): every wave issues the same copies, with no branch.
+    // x row-chunks rc = wave + S i of step j (row m = rc, chunk j; kPair: row m = rc / 2,
+    // chunk 2 j + rc % 2), unit L of the row from global unit L ^ m (k past the row in a
+    // partial chunk, or a chunk past the row, reads zero).  Rows m >= M copy row M - 1 (they
+    // feed only outputs that are never stored): every wave issues the same copies, with no
+    // branch.
     uint32_t xo_live[kXL];
     auto load_x = [&](int32_t j, auto slot) {
         constexpr bool kB = decltype(slot)::value;
@@ -714,11 +728,13 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
             (__attribute__((address_space(3))) char*)reinterpret_cast<char*>(kB ? xs1 : xs0);
 #pragma unroll
         for (int i = 0; i < kXL; ++i) {
-            const int m = wave + S * i;
+            const int rc = wave + S * i;
+            const int m = kPair ? rc >> 1 : rc;
+            const int32_t ch = kPair ? 2 * j + (rc & 1) : j;
             const int ms = m < M ? m : M - 1;
             const int u = lane ^ xswz<MX>(m);
-            const uint32_t xo = j * kChunkK + 8 * u < K ? (uint32_t)(j * (kChunkK * 2) + 16 * u + ms * K * 2) : 0x80000000u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xdst + m * 1024), 16, xo, 0, 0, 0);
+            const uint32_t xo = ch * kChunkK + 8 * u < K ? (uint32_t)(ch * (kChunkK * 2) + 16 * u + ms * K * 2) : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xdst + rc * 1024), 16, xo, 0, 0, 0);
             xo_live[i] = xo;
         }
     };
@@ -736,7 +752,7 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
     auto compute = [&](const JobRegs& jr, auto slot) {
         constexpr bool kB = decltype(slot)::value;
         const char* mb = reinterpret_cast<const char*>(kB ? cb1 : cb0) + wave * 4096;
-        const u32x4_t* xf = reinterpret_cast<const u32x4_t*>(kB ? xs1 : xs0) + xrow * 64;
+        const u32x4_t* xf = reinterpret_cast<const u32x4_t*>(kB ? xs1 : xs0) + (kPair ? 2 * xrow + hf : xrow) * 64;
         uint32_t qlo = 0, qhi = 0, split = 8;
         float dsc0 = 0.0f, dsc1 = 0.0f;
         if constexpr (kNested) {
@@ -797,11 +813,14 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
     using SlotA = std::integral_constant<bool, false>;
     using SlotB = std::integral_constant<bool, true>;
     JobRegs ra, rb;
-    // issue order codes(0), x(0), codes(1): the wait before job j allows only the codes of
-    // job j + 1 in flight
-    load_codes(0, ra, SlotA{});
+    // the job of this wave in step j, and the steps
+    auto cj = [&](int32_t j) { return kPair ? 2 * j + hf : j; };
+    const int32_t nsteps = kPair ? (nchunk + 1) / 2 : nchunk;
+    // issue order codes(0), x(0), codes(1): the wait before step j allows only the codes of
+    // step j + 1 in flight
+    load_codes(cj(0), ra, SlotA{});
     load_x(0, SlotA{});
-    load_codes(1, rb, SlotB{});
+    load_codes(cj(1), rb, SlotB{});
     {
         constexpr int kLo = 16 / S;
         float lo[kLo];
@@ -841,7 +860,7 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
     // job j + 1's x; after the job, its code slot takes job j + 2.  The loop runs whole pairs
     // of jobs with no condition around a load or a read (a condition makes the compiler
     // wait for every copy in flight): a job past the end reads x as zero and adds nothing.
-    for (int32_t j = 0; j < nchunk; j += 2) {
+    for (int32_t j = 0; j < nsteps; j += 2) {
         wait_job();
         wait_lds();
         barrier();
@@ -849,16 +868,28 @@ __global__ __launch_bounds__(S * 64, 1) void gemv_rows_kernel(GemvGroup g) {
         compute(ra, SlotA{});
         keep_x();
         wait_lds();
-        load_codes(j + 2, ra, SlotA{});
+        load_codes(cj(j + 2), ra, SlotA{});
         wait_job();
         barrier();
         load_x(j + 2, SlotA{});
         compute(rb, SlotB{});
         keep_x();
         wait_lds();
-        load_codes(j + 3, rb, SlotB{});
+        load_codes(cj(j + 3), rb, SlotB{});
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no copy into LDS outlives the workgroup
+    if constexpr (kPair) {
+        // the odd jobs' sums go through the wave's own code slot to the wave of the even
+        // jobs, which adds them to its own (in that order) and stores the tile
+        floatx4_t* mine = reinterpret_cast<floatx4_t*>(reinterpret_cast<char*>(cb0) + wave * 4096) + lane;
+        if (hf == 1) *mine = acc;
+        __syncthreads();
+        if (hf == 1) return;
+        const floatx4_t other = *reinterpret_cast<const floatx4_t*>(reinterpret_cast<const char*>(cb0) +
+                                                                    (wave + kTiles) * 4096 + 16 * lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += other[r];
+    }
     // outputs: register r of lane l is y[4 (l / 16) + r][n0 + l % 16]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -911,6 +942,11 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
     const bool rows = M >= kRowsMinM;
     const int S = 8;
     const int MX = rows ? (M <= 4 ? 4 : M <= 8 ? 8 : 16) : 1;
+    // row-split: two waves a tile (4 tiles a workgroup) at M <= 4, else one (8 tiles).  On
+    // the 70B-shaped layer (M = 4) the pairs took 120 us against 124 (alternating runs on
+    // one GPU); at M = 8, where a step copies 16 KB of x, they were no faster.
+    const bool pair = rows && MX == 4;
+    const int tiles_per_wg = pair ? S / 2 : S;
     const int64_t cus = device_cu_count();
     // tiles per launch: the K-split kernel's LDS holds each workgroup's partials; the
     // row-split kernel's groups are only bounded by the grid
@@ -1006,7 +1042,7 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
             // an aligned launch takes only weights whose rows are whole jobs
             if (aligned && slices[k].K % kChunkK != 0) continue;
             const int64_t tiles = (slices[k].N + 15) / 16;
-            const int64_t units = rows ? (tiles + S - 1) / S : tiles;   // row-split: groups of S tiles
+            const int64_t units = rows ? (tiles + tiles_per_wg - 1) / tiles_per_wg : tiles;   // row-split: groups of tiles
             if (nitems + units > max_tiles) continue;
             GemvTask& t = gg.t[gg.ntasks++];
             t = slices[k];
@@ -1017,15 +1053,17 @@ hipError_t launch_gemv_group(const GemvItem* items, int32_t count, int32_t M, hi
         gg.nitems = (int32_t)nitems;
         gg.qs = w0.blocksize_log2 - 6;
         const unsigned grid = rows ? (unsigned)nitems : (unsigned)(nitems < cus ? nitems : cus);
-        *variant = rows ? "mfma 16x16x32 bf16, row-split grouped launch: one workgroup per 8 tiles of 16 rows, each wave "
+        *variant = pair ? "mfma 16x16x32 bf16, row-split grouped launch: one workgroup per 4 tiles of 16 rows, two waves "
+                          "a tile (even and odd 512-k jobs), the x chunks shared through LDS, codes and scales two steps ahead"
+                 : rows ? "mfma 16x16x32 bf16, row-split grouped launch: one workgroup per 8 tiles of 16 rows, each wave "
                           "a whole tile, the x chunk shared through LDS, codes and scales two 512-k jobs ahead"
                         : "mfma 16x16x32 bf16, persistent grouped launch: 16-row tiles split over 8 waves in 512-k jobs, "
                           "two jobs in flight per wave, codes and x copied to LDS";
         if (rows) {
 #define QK_GEMV_ROWS_A(MXX, NN, QQ)                                                                                    \
     do {                                                                                                               \
-        if (aligned) hipLaunchKernelGGL((gemv_rows_kernel<8, MXX, NN, QQ, true>), dim3(grid), dim3(8 * 64), 0, s, gg); \
-        else hipLaunchKernelGGL((gemv_rows_kernel<8, MXX, NN, QQ, false>), dim3(grid), dim3(8 * 64), 0, s, gg);        \
+        if (aligned) hipLaunchKernelGGL((gemv_rows_kernel<8, MXX, NN, QQ, true, (MXX == 4)>), dim3(grid), dim3(8 * 64), 0, s, gg); \
+        else hipLaunchKernelGGL((gemv_rows_kernel<8, MXX, NN, QQ, false, (MXX == 4)>), dim3(grid), dim3(8 * 64), 0, s, gg);        \
     } while (0)
 #define QK_GEMV_ROWS_Q(MXX, QQ)                                  \
     do {                                                         \
