@@ -195,6 +195,9 @@ qk_status build_quant_lut(const float levels[16], QuantLut* lut, const char** wh
         lut->C = Cf;
         lut->nbins = nb;
         lut->sorted = sorted ? 1 : 0;
+        lut->tiny_free = 1;
+        for (int s = 0; s + 1 < U; ++s)
+            if (T[s] > -0x1p-60f && T[s] <= 0x1p-60f) lut->tiny_free = 0;
         for (int bi = 0; bi < kLutMaxBins; ++bi) {
             lut->T[bi] = 2.0f;
             lut->c[bi] = 0;

@@ -49,13 +49,15 @@ __device__ __forceinline__ float group_max(float v) {
 
 // The same for unsigned integers (for instance the bit patterns of non-negative
 // floats, whose order is the order of the values): no NaN canonicalization, and
-// the moves fold into the max instructions.
+// each move folds into its max instruction (v_max_u32 with a DPP source).  The
+// folding needs the move's old value to be the identity of the max (0); every lane
+// has a source in these patterns, so the old value is never used.
 template <int G>
 __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
-    if constexpr (G >= 2) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-    if constexpr (G >= 4) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
-    if constexpr (G >= 8) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
-    if constexpr (G >= 16) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+    if constexpr (G >= 2) v = max((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true), v);
+    if constexpr (G >= 4) v = max((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true), v);
+    if constexpr (G >= 8) v = max((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true), v);
+    if constexpr (G >= 16) v = max((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true), v);
     if constexpr (G >= 32) v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
     return v;
 }

@@ -31,6 +31,7 @@ struct QuantLut {
     float C;                 // S + 2^23
     int32_t nbins;           // 2S + 1
     int32_t sorted;          // 1: code order is value order (codes are c_lo + [t >= T])
+    int32_t tiny_free;       // 1: no threshold in (-2^-60, 2^-60], so every |t| < 2^-60 gets one code
     float T[kLutMaxBins];    // threshold of each bin
     uint32_t c[kLutMaxBins]; // sorted: c_lo; otherwise c_lo | (c_hi << 16)
 };

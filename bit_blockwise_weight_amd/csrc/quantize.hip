@@ -26,7 +26,10 @@
 // every bf16 and every fp16 value by the CPU test of the division (the
 // reciprocal for every y within 2 ulp of 1/a).  Any lane holding an element
 // outside that region redoes its 8 divisions with the IEEE sequence; fp32 inputs
-// always use it.
+// always use it.  When no decision threshold of the level table lies in
+// (-2^-60, 2^-60] (NF4 and FP4 among them), the condition on |x| is dropped: an x
+// with |x| < a*2^-64 has |x/a| < 2^-64 and a computed t below 2^-60 in magnitude,
+// and every t in that range gets the same code.
 //
 // Nearest level.  t is binned by the low 24 bits of fmaf(t, S, S + 2^23); each
 // bin of the LDS table holds at most one threshold T and the codes below and
@@ -74,7 +77,7 @@ struct QuantGroup {
     int32_t count;
 };
 
-template <typename InT, int B, bool kSorted>
+template <typename InT, int B, bool kSorted, bool kTinyFree>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantGroup g, QuantLut lut) {
     constexpr int G = B / 8;                       // lanes per block
     constexpr bool kFastDiv = !__is_same(InT, F32In);
@@ -157,15 +160,16 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(QuantGroup g, Quant
         float t[8];
         bool ok = false;
         if constexpr (kFastDiv) {
-            const bool fast_block = am >= kAMin && am <= kAMax;
+            // am is a non-negative float (or NaN, above the range), so its bit pattern
+            // orders like its value
+            const bool fast_block = as_uint(am) - as_uint(kAMin) <= as_uint(kAMax) - as_uint(kAMin);
             // RN(1/a): the hardware reciprocal (within 1 ulp) and one correction step,
             // exact for every bf16 and fp16 a of the fast region (CPU-checked, with a 2 ulp
-            // margin on the hardware's error)
-            const float ab = fast_block ? am : 1.0f;
-            const float r0 = __builtin_amdgcn_rcpf(ab);
-            const float r = __builtin_fmaf(__builtin_fmaf(-ab, r0, 1.0f), r0, r0);
-            const float x_lo = fast_block ? am * kXRel : __builtin_inff();
-            ok = mn >= x_lo;
+            // margin on the hardware's error).  Outside the region t is recomputed below.
+            const float r0 = __builtin_amdgcn_rcpf(am);
+            const float r = __builtin_fmaf(__builtin_fmaf(-am, r0, 1.0f), r0, r0);
+            if constexpr (kTinyFree) ok = fast_block;
+            else ok = fast_block && mn >= am * kXRel;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float q0 = v[i] * r;
@@ -322,10 +326,15 @@ hipError_t launch_typed(const QuantGroup& g, int64_t nunits_total, const QuantLu
     const int64_t cap = (int64_t)num_cus() * kWgsPerCu;   // persistent: the LDS table is filled once per workgroup
     const int grid = (int)(wgs_needed < cap ? wgs_needed : cap);
     const size_t lds = (size_t)lut.nbins * kLutCopies * sizeof(uint2);
-    if (lut.sorted)
-        hipLaunchKernelGGL((quantize_kernel<InT, B, true>), dim3(grid), dim3(kQThreads), lds, s, g, lut);
-    else
-        hipLaunchKernelGGL((quantize_kernel<InT, B, false>), dim3(grid), dim3(kQThreads), lds, s, g, lut);
+    // the condition on small |x| only exists for the reciprocal division of 16-bit input
+    const bool tiny_free = lut.tiny_free != 0 && !__is_same(InT, F32In);
+    if (lut.sorted) {
+        if (tiny_free) hipLaunchKernelGGL((quantize_kernel<InT, B, true, true>), dim3(grid), dim3(kQThreads), lds, s, g, lut);
+        else hipLaunchKernelGGL((quantize_kernel<InT, B, true, false>), dim3(grid), dim3(kQThreads), lds, s, g, lut);
+    } else {
+        if (tiny_free) hipLaunchKernelGGL((quantize_kernel<InT, B, false, true>), dim3(grid), dim3(kQThreads), lds, s, g, lut);
+        else hipLaunchKernelGGL((quantize_kernel<InT, B, false, false>), dim3(grid), dim3(kQThreads), lds, s, g, lut);
+    }
     return hipGetLastError();
 }
 

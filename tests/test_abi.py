@@ -90,6 +90,16 @@ def test_quantize_rejects_table_whose_lookup_is_not_exact(L):
     assert L.qk_quantize_blockwise(FAKE, qk.QK_BF16, 64, 64, arr, FAKE, FAKE, None) == qk.QK_ERR_UNSUPPORTED
 
 
+def test_quantize_accepts_table_with_a_threshold_at_zero(L):
+    """Levels +-2^-40 (threshold: the least positive float) pass the table build:
+    on a host without a GPU the call gets as far as the device check."""
+    lv = [-1, -0.75, -0.5, -0.375, -0.25, -0.125, -0.0625, -2.0 ** -40, 2.0 ** -40, 0.0625, 0.125, 0.25,
+          0.375, 0.5, 0.75, 1]
+    arr = (ctypes.c_float * 16)(*lv)
+    st = L.qk_quantize_blockwise(FAKE, qk.QK_BF16, 64, 64, arr, FAKE, FAKE, None)
+    assert st not in (qk.QK_OK, qk.QK_ERR_INVALID_ARG, qk.QK_ERR_UNSUPPORTED), qk.qk_last_error()
+
+
 def test_double_quant_errors_and_workspace(L):
     assert qk.qk_double_quant_workspace_size(1) >= 8
     assert qk.qk_double_quant_workspace_size(4096 * 4096 + 1) >= 8 * 4097

@@ -197,6 +197,47 @@ def test_bf16_input_hard_cases(kind):
     _check_quant(hf[:n], dev_f16(hf[:n]), B, kind, "fp16 hard cases")
 
 
+# A level table whose two smallest levels are -2^-40 and 2^-40: their decision threshold
+# is the least positive float (a tie at t = 0 goes to the smaller code), so the code of an
+# element far below its block's absmax depends on its sign and on whether its quotient
+# rounds to zero.  For such a table the kernel divides exactly (IEEE) for those elements;
+# for NF4 and FP4, whose thresholds are all far from 0, it does not need to.
+_ZERO_THRESHOLD_LEVELS = np.array([-1, -0.75, -0.5, -0.375, -0.25, -0.125, -0.0625, -2.0 ** -40,
+                                   2.0 ** -40, 0.0625, 0.125, 0.25, 0.375, 0.5, 0.75, 1], dtype=np.float32)
+
+
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
+def test_bf16_tiny_elements_with_a_threshold_at_zero(order):
+    say(f"case: bf16 tiny elements, level table with a threshold at zero ({order})")
+    lv = _ZERO_THRESHOLD_LEVELS.copy()
+    if order == "shuffled":
+        lv = lv[np.random.default_rng(3).permutation(16)]
+    g = np.random.default_rng(41)
+    B = 64
+    tiny = np.array([2.0 ** -133, -(2.0 ** -133), 3 * 2.0 ** -133, 2.0 ** -130, -(2.0 ** -127), 2.0 ** -100,
+                     -(2.0 ** -90), 0.0, -0.0, 1e-30, -1e-25, 2.0 ** -126, -(2.0 ** -126)], dtype=np.float32)
+    blocks = []
+    for a in [1.0, 3.0, 0.75, 2.0 ** -20, 5.0, 2.0 ** 40]:
+        for rep in range(4):
+            b = (g.standard_normal(B) * 0.3).astype(np.float32) * np.float32(a)
+            b[0] = np.float32(a) * np.float32(1.5)
+            idx = g.choice(np.arange(1, B), size=tiny.size, replace=False)
+            b[idx] = tiny * np.float32(1 + rep)
+            blocks.append(b)
+    x = np.concatenate(blocks)
+    bits = ofl.f32_to_bf16_bits(x)
+    xf = bf16_bits_to_f32(bits)
+    codes, absmax = qk.qk_quantize_blockwise(dev_bf16(bits), B, torch.from_numpy(lv))
+    torch.cuda.synchronize()
+    want_codes, want_absmax = obw.quantize_blockwise(xf, B, lv)
+    assert_bits_equal(host(absmax), want_absmax, "absmax")
+    assert_bits_equal(host(codes), want_codes, "codes")
+    # the tiny elements do not all get one code: the table really separates them
+    nib = np.stack([host(codes) >> 4, host(codes) & 15], axis=1).reshape(-1)[:xf.size]
+    tiny_pos = np.abs(xf) < np.float32(2.0 ** -80)
+    assert len(set(nib[tiny_pos].tolist())) == 2
+
+
 @pytest.mark.parametrize("n", [1, 2, 7, 63, 64, 65, 511, 512, 513, 1023, 2047, 2049, 100_001, 1_000_003])
 def test_ragged_sizes_and_guard_bands(n):
     say(f"case: ragged n={n}")
