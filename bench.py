@@ -682,9 +682,10 @@ def edge_us(torch, qk, workloads, iters=50):
 
 def hbm_ceilings(torch, iters=10):
     """The practical HBM ceilings next to the 8 TB/s spec: a plain 1 GiB
-    device-to-device copy (torch; read + write bytes over time) and a 4 GiB stream
+    device-to-device copy (torch; read + write bytes over time), a 4 GiB stream
     of 16-byte loads alone (libqk_probe.so, plain and nontemporal, the best of two
-    grid sizes)."""
+    grid sizes), and two mixed streams of 4 GiB + 1 GiB: 16 bytes read per 4
+    written, and 4 read per 16 written."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -713,7 +714,23 @@ def hbm_ceilings(torch, iters=10):
                     raise RuntimeError("qk_probe_read_stream failed")
             best = max(best, nbytes / _timed(torch, run, iters) / 1e12)
         out[key] = round(best, 3)
-    del src, sink
+    del sink
+    # read 16 B and write 4 (the quantization's mix), read 4 B and write 16 (the
+    # dequantization's); the rate counts read + write bytes
+    lib.qk_probe_mix_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p]
+    n16 = nbytes // 16
+    dst = torch.empty(n16 * 4, dtype=torch.int32, device="cuda")
+    for rh, key in ((1, "read4_write1_tb_per_s"), (2, "read4_write1_16b_stores_tb_per_s"),
+                    (0, "read1_write4_tb_per_s")):
+        best = 0.0
+        for grid in grids:
+            def run():
+                if lib.qk_probe_mix_stream(src.data_ptr(), dst.data_ptr(), n16, grid, rh, stream) != 0:
+                    raise RuntimeError("qk_probe_mix_stream failed")
+            best = max(best, 20 * n16 / _timed(torch, run, iters) / 1e12)
+        out[key] = round(best, 3)
+    del src, dst
     torch.cuda.empty_cache()
     return out
 

@@ -1,7 +1,9 @@
-// HBM read ceiling for the measurement script (not part of the qk C ABI): a grid of
+// HBM ceilings for the measurement script (not part of the qk C ABI): a grid of
 // 256-thread workgroups streams a buffer with 16-byte loads, 16 per lane in flight,
 // plain or with the nontemporal hint, and folds the words into one value per thread so
-// that no load is dropped.  bench.py times it with HIP events next to a device copy.
+// that no load is dropped; two mixed streams read and write in the proportions of the
+// quantization and of the dequantization.  bench.py times them with HIP events next to
+// a device copy.
 #include <hip/hip_runtime.h>
 #include <cstddef>
 #include <cstdint>
@@ -46,6 +48,79 @@ extern "C" int qk_probe_read_stream(const void* src, size_t nbytes, uint32_t* ou
         hipLaunchKernelGGL(read_stream_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p, nbytes / 16, out);
     else
         hipLaunchKernelGGL(read_stream_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p, nbytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Mixed streams: kReadHeavy reads 16 bytes (nontemporal) and writes 4 per lane and
+// step (the traffic of a 4-bit quantization of 16-bit input: 2 bytes in, about half a
+// byte out); otherwise it reads 4 bytes and writes 16 (a dequantization to 16 bits).
+namespace {
+
+constexpr int kMixUnroll = 8;
+
+// kMode 0: read-heavy, 4-byte stores; 1: write-heavy; 2: read-heavy, the words of 4
+// neighbouring lanes gathered by DPP into one 16-byte store (n16 a multiple of 4)
+template <int kMode>
+__global__ __launch_bounds__(kThreads) void mix_stream_kernel(const void* __restrict__ src, void* __restrict__ dst,
+                                                              size_t n16) {
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride * kMixUnroll) {
+        if constexpr (kMode != 1) {
+            u32x4_t v[kMixUnroll];
+#pragma unroll
+            for (int j = 0; j < kMixUnroll; ++j) {
+                const size_t k = i + (size_t)j * stride;
+                v[j] = k < n16 ? __builtin_nontemporal_load(static_cast<const u32x4_t*>(src) + k) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int j = 0; j < kMixUnroll; ++j) {
+                const size_t k = i + (size_t)j * stride;
+                const uint32_t w = v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+                if constexpr (kMode == 0) {
+                    if (k < n16) static_cast<uint32_t*>(dst)[k] = w;
+                } else {
+                    // k and the grid's lane count are multiples of 4 at lanes 4 q, so the
+                    // quad's 4 steps are k .. k + 3, all in range or all out
+                    const uint32_t w1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x39, 0xF, 0xF, false);   // lane + 1
+                    const uint32_t w2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x4E, 0xF, 0xF, false);   // lane + 2
+                    const uint32_t w3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0x93, 0xF, 0xF, false);   // lane + 3
+                    if ((threadIdx.x & 3) == 0 && k < n16) static_cast<u32x4_t*>(dst)[k / 4] = u32x4_t{w, w1, w2, w3};
+                }
+            }
+        } else {
+            uint32_t w[kMixUnroll];
+#pragma unroll
+            for (int j = 0; j < kMixUnroll; ++j) {
+                const size_t k = i + (size_t)j * stride;
+                w[j] = k < n16 ? static_cast<const uint32_t*>(src)[k] : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < kMixUnroll; ++j) {
+                const size_t k = i + (size_t)j * stride;
+                if (k < n16) static_cast<u32x4_t*>(dst)[k] = u32x4_t{w[j], w[j] ^ 1u, w[j] ^ 2u, w[j] ^ 3u};
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// n16 steps of 16 bytes: read_heavy != 0 reads 16 n16 bytes at src and writes 4 n16 at
+// dst (read_heavy = 2: by 16-byte stores, n16 a multiple of 4); otherwise reads 4 n16
+// and writes 16 n16.  Both buffers 16-byte aligned.  Returns 0,
+// or a nonzero code for bad arguments or a failed launch.
+extern "C" int qk_probe_mix_stream(const void* src, void* dst, size_t n16, int grid, int read_heavy, void* stream) {
+    if (src == nullptr || dst == nullptr || n16 == 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(dst) % 16 != 0 || grid <= 0)
+        return 1;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (read_heavy == 2 && n16 % 4 != 0) return 1;
+    if (read_heavy == 2)
+        hipLaunchKernelGGL(mix_stream_kernel<2>, dim3(grid), dim3(kThreads), 0, s, src, dst, n16);
+    else if (read_heavy)
+        hipLaunchKernelGGL(mix_stream_kernel<0>, dim3(grid), dim3(kThreads), 0, s, src, dst, n16);
+    else
+        hipLaunchKernelGGL(mix_stream_kernel<1>, dim3(grid), dim3(kThreads), 0, s, src, dst, n16);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
