@@ -238,7 +238,11 @@ def test_bf16_tiny_elements_with_a_threshold_at_zero(order):
     assert len(set(nib[tiny_pos].tolist())) == 2
 
 
-@pytest.mark.parametrize("n", [1, 2, 7, 63, 64, 65, 511, 512, 513, 1023, 2047, 2049, 100_001, 1_000_003])
+# 2048 = one 32-element-per-lane unit of the dequantization; 18_532 and 61_447 leave
+# 9 and 30 whole units (not a multiple of 8) and a tail that starts inside a
+# double-quantization block (at block 288 or 960 of 64 elements)
+@pytest.mark.parametrize("n", [1, 2, 7, 63, 64, 65, 511, 512, 513, 1023, 2047, 2048, 2049, 18_532, 61_447,
+                               100_001, 1_000_003])
 def test_ragged_sizes_and_guard_bands(n):
     say(f"case: ragged n={n}")
     g = np.random.default_rng(n)
@@ -281,8 +285,8 @@ def test_ragged_sizes_and_guard_bands(n):
 
 @pytest.mark.parametrize("offset", [0, 4, 8, 12])
 def test_dequant_codes_alignment(offset):
-    """Codes only need 4-byte alignment in a state; 16-byte aligned codes take the
-    vectorized kernel, others the per-element one.  Both must match the oracle."""
+    """Codes only need 4-byte alignment in a state: at every alignment the
+    dequantization (bf16 and fp32, a partial last unit) must match the oracle."""
     n = 3 * 2048 + 517
     say(f"case: dequant codes offset {offset}, n={n}")
     g = np.random.default_rng(77 + offset)
