@@ -27,9 +27,11 @@
 // reciprocal for every y within 2 ulp of 1/a).  Any lane holding an element
 // outside that region redoes its 8 divisions with the IEEE sequence; fp32 inputs
 // always use it.  When no decision threshold of the level table lies in
-// (-2^-60, 2^-60] (NF4 and FP4 among them), the condition on |x| is dropped: an x
-// with |x| < a*2^-64 has |x/a| < 2^-64 and a computed t below 2^-60 in magnitude,
-// and every t in that range gets the same code.
+// (-2^-60, 2^-60] (FP4, whose levels include 0, is such a table; NF4, whose two
+// middle levels are +-0.0396 with the threshold at the least positive float, is
+// not), the condition on |x| is dropped: an x with |x| < a*2^-64 has |x/a| < 2^-64
+// and a computed t below 2^-60 in magnitude, and every t in that range gets the
+// same code.
 //
 // Nearest level.  t is binned by the low 24 bits of fmaf(t, S, S + 2^23); each
 // bin of the LDS table holds at most one threshold T and the codes below and

@@ -201,7 +201,8 @@ def test_bf16_input_hard_cases(kind):
 # is the least positive float (a tie at t = 0 goes to the smaller code), so the code of an
 # element far below its block's absmax depends on its sign and on whether its quotient
 # rounds to zero.  For such a table the kernel divides exactly (IEEE) for those elements;
-# for NF4 and FP4, whose thresholds are all far from 0, it does not need to.
+# for FP4, whose thresholds are all far from 0, it does not need to.  (NF4 has the
+# same kind of threshold at 0, between its two middle levels +-0.0396.)
 _ZERO_THRESHOLD_LEVELS = np.array([-1, -0.75, -0.5, -0.375, -0.25, -0.125, -0.0625, -2.0 ** -40,
                                    2.0 ** -40, 0.0625, 0.125, 0.25, 0.375, 0.5, 0.75, 1], dtype=np.float32)
 
