@@ -150,10 +150,13 @@ def build_workload(torch, qk, workloads):
         A = (torch.randn((m["K"], R), generator=g) * 0.01).to(torch.bfloat16).to(dev)
         Bm = (torch.randn((R, m["N"]), generator=g) * 0.01).to(torch.bfloat16).to(dev)
         lora[m["name"]] = (A, Bm)
-    gemm_ws = torch.empty(max(16, qk.qk_gemm_nf4_workspace_size(M_TOK, R)), dtype=torch.uint8, device=dev)
+    gemm_ws = torch.empty(max(16, sum((qk.qk_gemm_nf4_workspace_size(M_TOK, R) + 255) // 256 * 256 for _ in mats)),
+                          dtype=torch.uint8, device=dev)
     levels_c = (ctypes.c_float * 16)(*lv.tolist())
     return {"mats": mats, "acts": acts, "lora": lora, "M": M_TOK, "r": R, "levels": lv, "levels_c": levels_c,
             "gemm_ws": gemm_ws, "dq_call": dq_group_call(torch, qk, mats),
+            "gemm_call": gemm_group_call(torch, qk, [(acts[m["K"]]["X"], m["state"]) + lora[m["name"]] + (2.0,)
+                                                     for m in mats], [m["Y"] for m in mats], gemm_ws),
             "q_call": quant_group_call(torch, qk, mats, levels_c)}
 
 
@@ -163,23 +166,18 @@ OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lo
 def step_calls(torch, qk, wl):
     """The launches of one pass of the hot path over the layer set, in order, as
     (op, matrices, callable): the quantization of the layer's weights and the
-    double quantization of their absmax arrays, one grouped call each, per weight
-    dequantize and the
-    prefill GEMM with LoRA; then the decode GEMV of the whole layer at M = 1 and at
-    M = 16, one grouped call each (the way a decoder runs a layer)."""
-    lv = wl["levels_c"]
+    double quantization of their absmax arrays, one grouped call each; per weight
+    dequantize; the prefill GEMM with LoRA of the whole layer, one grouped call
+    (the seven GEMMs' tiles in one launch after their LoRA pre-passes); then the
+    decode GEMV of the whole layer at M = 1 and at M = 16, one grouped call each
+    (the way a decoder runs a layer)."""
     mats = wl["mats"]
     calls = []
     calls.append(("quantize", list(mats), wl["q_call"]))
     calls.append(("double_quant", list(mats), wl["dq_call"]))
     for m in mats:
-        a = wl["acts"][m["K"]]
-        A, Bm = wl["lora"][m["name"]]
-        calls += [
-            ("dequantize", [m], lambda m=m: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])),
-            ("gemm_lora", [m], lambda m=m, a=a, A=A, Bm=Bm: qk.qk_gemm_nf4(a["X"], m["state"], A, Bm, 2.0, m["Y"],
-                                                                           wl["gemm_ws"])),
-        ]
+        calls.append(("dequantize", [m], lambda m=m: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])))
+    calls.append(("gemm_lora", list(mats), wl["gemm_call"]))
     for op, xk, yk in (("gemv_m1", "x1", "y1"), ("gemv_m16", "x16", "y16")):
         items = [(wl["acts"][m["K"]][xk], m["state"]) for m in mats]
         ys = [m[yk] for m in mats]
@@ -442,6 +440,27 @@ def quant_group_call(torch, qk, mats, levels_c, blocksize=64):
             raise RuntimeError(f"qk_quantize_blockwise_grouped: {qk.qk_last_error()}")
 
     call.keep = (arr, mats, levels_c)
+    return call
+
+
+def gemm_group_call(torch, qk, tasks, ys, ws):
+    """A prepared qk_gemm_nf4_grouped over (X, state, A, B, s) tasks writing ys (the
+    task array built and the workspace size checked once, so a timed loop pays no
+    Python marshalling)."""
+    arr, keep, _ = qk._gemm_tasks(tasks, ys)
+    need = qk.qk_gemm_nf4_grouped_workspace_size(tasks)
+    if ws.numel() < need:
+        raise RuntimeError(f"the GEMM workspace holds {ws.numel()} bytes, {need} needed")
+    L = qk.lib()
+    n = len(tasks)
+
+    def call():
+        rc = L.qk_gemm_nf4_grouped(arr, n, ws.data_ptr(), ws.numel(),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"qk_gemm_nf4_grouped: {qk.qk_last_error()}")
+
+    call.keep = (arr, keep, tasks, ys, ws)
     return call
 
 

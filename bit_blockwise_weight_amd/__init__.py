@@ -20,7 +20,8 @@ __all__ = [
     "qk_make_codebook", "qk_quantize_blockwise", "qk_quantize_blockwise_grouped", "qk_double_quant_workspace_size",
     "qk_double_quant",
     "qk_double_quant_grouped_workspace_size", "qk_double_quant_grouped",
-    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemv_nf4_grouped", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_gemm_nf4_noalloc", "qk_last_error", "qk_version",
+    "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemv_nf4_grouped", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_gemm_nf4_noalloc",
+    "qk_gemm_nf4_grouped_workspace_size", "qk_gemm_nf4_grouped", "GemmTask", "qk_last_error", "qk_version",
     "qk_backend_info", "quantize",
 ]
 
@@ -87,6 +88,13 @@ class GemvTask(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("st", ctypes.POINTER(QuantState)), ("y", ctypes.c_void_p)]
 
 
+class GemmTask(ctypes.Structure):
+    """Mirror of qk_gemm_task (include/qk.h)."""
+    _fields_ = [("X", ctypes.c_void_p), ("M", ctypes.c_int64), ("st", ctypes.POINTER(QuantState)),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("r", ctypes.c_int32), ("lora_scale", ctypes.c_float),
+                ("Y", ctypes.c_void_p)]
+
+
 _lib = None
 _load_error = None
 
@@ -122,6 +130,8 @@ def lib():
         "qk_gemv_nf4": [vp, i32, st_p, vp, vp],
         "qk_gemv_nf4_grouped": [ctypes.POINTER(GemvTask), i32, i32, vp],
         "qk_gemm_nf4_workspace_size": [i64, i32, ctypes.POINTER(ctypes.c_size_t)],
+        "qk_gemm_nf4_grouped_workspace_size": [ctypes.POINTER(GemmTask), i32, ctypes.POINTER(ctypes.c_size_t)],
+        "qk_gemm_nf4_grouped": [ctypes.POINTER(GemmTask), i32, vp, ctypes.c_size_t, vp],
         "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp, ctypes.c_size_t, vp],
         "qk_gemm_nf4_noalloc": [vp, i64, st_p, vp, vp, i32, f32, vp, vp],
         "qk_lora_merge": [st_p, vp, vp, i32, f32, vp, vp],
@@ -571,6 +581,71 @@ def qk_gemm_nf4(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: 
                                  _ptr(Y), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                  ctypes.c_void_p(_stream(X))))
     return Y
+
+
+def _gemm_tasks(tasks, ys):
+    """ctypes array of qk_gemm_task for a list of (X, state, A, B, lora_scale), with
+    the outputs (given in ys, or allocated)."""
+    tasks = list(tasks)
+    if not tasks:
+        raise ValueError("a grouped GEMM needs at least one (X, state, A, B, lora_scale)")
+    arr = (GemmTask * len(tasks))()
+    keep, outs = [], []
+    for i, (X, state, A, B, lora_scale) in enumerate(tasks):
+        if (A is None) != (B is None):
+            raise ValueError(f"task {i}: give both LoRA A and B, or neither")
+        for name, t in (("X", X), ("A", A), ("B", B)):
+            if t is not None and t.dtype != torch.bfloat16:
+                raise ValueError(f"task {i}: {name} must be bf16, got {t.dtype}")
+        X2 = _rows_of(X, state.cols, f"task {i}: X")
+        M = X2.shape[0]
+        r = 0 if A is None else A.shape[-1]
+        if A is not None and (tuple(A.shape) != (state.cols, r) or tuple(B.shape) != (r, state.rows)):
+            raise ValueError(f"task {i}: shapes A {tuple(A.shape)}, B {tuple(B.shape)} do not match "
+                             f"W [{state.rows}, {state.cols}]")
+        Y = None if ys is None else ys[i]
+        if Y is not None:
+            _check_out(Y, (M, state.rows), torch.bfloat16, f"task {i}: Y")
+        _require_cuda(X, A, B, Y)
+        if Y is None:
+            Y = torch.empty((M, state.rows), dtype=torch.bfloat16, device=X.device)
+        arr[i].X = X2.data_ptr()
+        arr[i].M = M
+        arr[i].st = ctypes.pointer(state)
+        arr[i].A = _ptr(A)
+        arr[i].B = _ptr(B)
+        arr[i].r = int(r)
+        arr[i].lora_scale = float(lora_scale)
+        arr[i].Y = Y.data_ptr()
+        keep.append(X2)
+        outs.append(Y)
+    return arr, keep, outs
+
+
+def qk_gemm_nf4_grouped_workspace_size(tasks) -> int:
+    """Workspace bytes of qk_gemm_nf4_grouped for a list of (X, state, A, B, lora_scale)."""
+    arr, _, _ = _gemm_tasks(tasks, None)
+    out = ctypes.c_size_t(0)
+    _check(lib().qk_gemm_nf4_grouped_workspace_size(arr, len(arr), ctypes.byref(out)))
+    return int(out.value)
+
+
+def qk_gemm_nf4_grouped(tasks, ys=None, workspace=None):
+    """Y_i = X_i deq(W_i)^T + s_i (X_i A_i) B_i for a list of (X_i, state_i, A_i, B_i, s_i),
+    in as few launches as their shapes allow; each Y_i equals what qk_gemm_nf4 of that
+    task alone writes.  Returns the list of Y_i."""
+    arr, keep, outs = _gemm_tasks(tasks, ys)
+    out = ctypes.c_size_t(0)
+    _check(lib().qk_gemm_nf4_grouped_workspace_size(arr, len(arr), ctypes.byref(out)))
+    wsb = int(out.value)
+    dev = keep[0].device
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _require_cuda(workspace)
+    with _on(dev):
+        _check(lib().qk_gemm_nf4_grouped(arr, len(arr), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                         ctypes.c_void_p(_stream(keep[0]))))
+    return outs
 
 
 def qk_gemm_nf4_noalloc(X: torch.Tensor, state: QuantState, A=None, B=None, lora_scale: float = 0.0,

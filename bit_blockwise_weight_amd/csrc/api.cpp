@@ -615,6 +615,69 @@ qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const 
                     "qk_gemm_nf4");
 }
 
+namespace {
+qk_status gemm_group_items(const char* who, const qk_gemm_task* tasks, int32_t ntasks, std::vector<qk::GemmItem>& items) {
+    if (!tasks) return fail(QK_ERR_INVALID_ARG, "%s: tasks is NULL", who);
+    if (ntasks < 1 || ntasks > 256) return fail(QK_ERR_INVALID_ARG, "%s: ntasks must be in 1..256 (got %d)", who, ntasks);
+    items.resize((size_t)ntasks);
+    for (int32_t i = 0; i < ntasks; ++i) {
+        const qk_gemm_task& t = tasks[i];
+        char fn[64];
+        std::snprintf(fn, sizeof(fn), "%s: task %d", who, i);
+        const qk_status v = check_gemm_args(fn, t.X, t.M, t.st, t.A, t.B, t.r, t.lora_scale, t.Y);
+        if (v != QK_OK) return v;
+        items[i] = qk::GemmItem{t.X, t.M, qk::MatArgs{deq_args(t.st), t.st->rows, t.st->cols}, t.A, t.B,
+                                t.A ? t.r : 0, t.lora_scale, t.Y};
+    }
+    return QK_OK;
+}
+}  // namespace
+
+qk_status qk_gemm_nf4_grouped_workspace_size(const qk_gemm_task* tasks, int32_t ntasks, size_t* bytes) {
+    if (!bytes) return fail(QK_ERR_INVALID_ARG, "qk_gemm_nf4_grouped_workspace_size: bytes is NULL");
+    std::vector<qk::GemmItem> items;
+    const qk_status v = gemm_group_items("qk_gemm_nf4_grouped_workspace_size", tasks, ntasks, items);
+    if (v != QK_OK) return v;
+    *bytes = qk::gemm_group_workspace_bytes(items.data(), ntasks);
+    return ok();
+}
+
+qk_status qk_gemm_nf4_grouped(const qk_gemm_task* tasks, int32_t ntasks, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    const char* who = "qk_gemm_nf4_grouped";
+    std::vector<qk::GemmItem> items;
+    const qk_status v = gemm_group_items(who, tasks, ntasks, items);
+    if (v != QK_OK) return v;
+    const size_t need = qk::gemm_group_workspace_bytes(items.data(), ntasks);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(QK_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 16)) return fail(QK_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", who);
+    // the GEMMs of a launch run at once: every Y must be disjoint from the other Ys, from
+    // every X and from the workspace
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + need;
+    for (int32_t i = 0; i < ntasks; ++i) {
+        const uintptr_t y0 = reinterpret_cast<uintptr_t>(tasks[i].Y);
+        const uintptr_t y1 = y0 + (uintptr_t)tasks[i].M * (uintptr_t)tasks[i].st->rows * 2;
+        if (need > 0 && w0 < y1 && y0 < w1)
+            return fail(QK_ERR_INVALID_ARG, "%s: Y of task %d overlaps the workspace", who, i);
+        for (int32_t j = 0; j < ntasks; ++j) {
+            const uintptr_t x0 = reinterpret_cast<uintptr_t>(tasks[j].X);
+            const uintptr_t x1 = x0 + (uintptr_t)tasks[j].M * (uintptr_t)tasks[j].st->cols * 2;
+            if (x0 < y1 && y0 < x1) return fail(QK_ERR_INVALID_ARG, "%s: Y of task %d overlaps X of task %d", who, i, j);
+            if (j == i) continue;
+            const uintptr_t z0 = reinterpret_cast<uintptr_t>(tasks[j].Y);
+            const uintptr_t z1 = z0 + (uintptr_t)tasks[j].M * (uintptr_t)tasks[j].st->rows * 2;
+            if (z0 < y1 && y0 < z1) return fail(QK_ERR_INVALID_ARG, "%s: Y of task %d overlaps Y of task %d", who, i, j);
+        }
+    }
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_gemm_group(items.data(), ntasks, workspace, reinterpret_cast<hipStream_t>(stream),
+                                          &g_gemm_variant),
+                    who);
+}
+
 qk_status qk_gemm_nf4_noalloc(const void* X, int64_t M, const qk_quant_state* st, const void* A, const void* B,
                               int32_t r, float lora_scale, void* Y, void* stream) {
     const qk_status v = check_gemm_args("qk_gemm_nf4_noalloc", X, M, st, A, B, r, lora_scale, Y);

@@ -26,8 +26,11 @@
 //     and (s T) * B is added after it as bf16 hi + lo.  LDS rows are padded to
 //     144 bytes so the fragment reads of 8 consecutive rows fall in distinct banks.
 // Both end with fp32 accumulators -> bf16 (RNE) -> Y.
+#include <algorithm>
+#include <cstring>
 #include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "qk_internal.h"
 #include "qk_device.h"
@@ -46,6 +49,7 @@ constexpr int BK = 64;
 constexpr int kThreads = 256;
 constexpr int kLdsStride = BK + 8;        // bf16 elements per LDS row (144 bytes)
 constexpr int kMaxRank = 64;
+constexpr int kMaxGemmGroup = 8;          // GEMMs of one grouped launch
 
 struct GemmArgs {
     const uint16_t* X;   // [M, K]
@@ -566,12 +570,21 @@ constexpr int kGroupM = 4;                // tile rows per group in the tile ord
 
 typedef __attribute__((address_space(3))) void* lptr_t;
 
+// The GEMMs of one launch (a single call is a group of one): task t owns the
+// workgroups [tile0[t], tile0[t + 1]) and reads its LoRA partials at T[t].
+struct GemmGroup {
+    GemmArgs t[kMaxGemmGroup];
+    const float* T[kMaxGemmGroup];
+    int32_t tile0[kMaxGemmGroup + 1];
+    int32_t count;
+};
+
 __device__ __forceinline__ uint32_t xoff(int row, int chunk) {   // byte offset in an X tile
     return (uint32_t)(row * 8 + (chunk ^ ((row >> 1) & 7))) * 16u;
 }
 
 template <int R16, bool kNested>
-__global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const float* __restrict__ T) {
+__global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmGroup gg) {
     constexpr int kThr = 512;                          // 8 waves, two per SIMD
     constexpr int kRp = 16 * R16;
     constexpr int kTs = 16 + 8;                        // row pitch of a staged 16-rank chunk of s X A
@@ -589,6 +602,12 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
     __shared__ __attribute__((aligned(65536))) uint2 tab[256 * kCopies];  // fp32 level pairs, 64 KB
     __shared__ __attribute__((aligned(16))) uint16_t tst[2 * TM * kTs];   // s X A chunk, bf16 hi | lo, 24 KB
 
+    // this workgroup's task (uniform: a scalar search of the launch's prefix table)
+    int task = 0;
+    while (task + 1 < gg.count && (int32_t)blockIdx.x >= gg.tile0[task + 1]) ++task;
+    const GemmArgs& a = gg.t[task];
+    const float* __restrict__ T = gg.T[task];
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -601,7 +620,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmArgs a, const flo
     {
         const uint32_t tiles_n = (uint32_t)((N + TN - 1) / TN), tiles_m = (uint32_t)((M + TM - 1) / TM);
         const uint32_t nt = tiles_n * tiles_m;
-        const uint32_t bid = blockIdx.x;
+        const uint32_t bid = blockIdx.x - (uint32_t)gg.tile0[task];
         const uint32_t lid = (nt % kXcds == 0) ? (bid % kXcds) * (nt / kXcds) + bid / kXcds : bid;
         const uint32_t per_group = kGroupM * tiles_n;
         const uint32_t first_m = (lid / per_group) * kGroupM;
@@ -1046,16 +1065,18 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
 }  // namespace v4
 
 template <bool kNested>
-void launch_fast_r(const GemmArgs& a, const float* T, hipStream_t s, dim3 grid, int r16) {
-    const dim3 block(512);
+void launch_fast_r(const v4::GemmGroup& g, hipStream_t s, int r16) {
+    const dim3 grid((unsigned)g.tile0[g.count]), block(512);
     switch (r16) {
-        case 0: hipLaunchKernelGGL((v4::gemm_fast_kernel<0, kNested>), grid, block, 0, s, a, T); break;
-        case 1: hipLaunchKernelGGL((v4::gemm_fast_kernel<1, kNested>), grid, block, 0, s, a, T); break;
-        case 2: hipLaunchKernelGGL((v4::gemm_fast_kernel<2, kNested>), grid, block, 0, s, a, T); break;
-        case 3: hipLaunchKernelGGL((v4::gemm_fast_kernel<3, kNested>), grid, block, 0, s, a, T); break;
-        default: hipLaunchKernelGGL((v4::gemm_fast_kernel<4, kNested>), grid, block, 0, s, a, T); break;
+        case 0: hipLaunchKernelGGL((v4::gemm_fast_kernel<0, kNested>), grid, block, 0, s, g); break;
+        case 1: hipLaunchKernelGGL((v4::gemm_fast_kernel<1, kNested>), grid, block, 0, s, g); break;
+        case 2: hipLaunchKernelGGL((v4::gemm_fast_kernel<2, kNested>), grid, block, 0, s, g); break;
+        case 3: hipLaunchKernelGGL((v4::gemm_fast_kernel<3, kNested>), grid, block, 0, s, g); break;
+        default: hipLaunchKernelGGL((v4::gemm_fast_kernel<4, kNested>), grid, block, 0, s, g); break;
     }
 }
+
+int64_t fast_tiles(const GemmArgs& a) { return ((a.N + v4::TN - 1) / v4::TN) * ((a.M + v4::TM - 1) / v4::TM); }
 
 void launch_lora_xa(const GemmArgs& a, float* T, hipStream_t s, int r16) {
     const dim3 grid((unsigned)((a.M + 63) / 64), v4::kSplits);
@@ -1074,18 +1095,36 @@ void launch_lora_xa(const GemmArgs& a, float* T, hipStream_t s, int r16) {
 #undef QK_LORA_XA
 }
 
-hipError_t launch_fast(const GemmArgs& a, void* workspace, hipStream_t s) {
-    const dim3 grid((unsigned)(((a.N + v4::TN - 1) / v4::TN) * ((a.M + v4::TM - 1) / v4::TM)));
-    const int r16 = a.A ? (a.r + 15) / 16 : 0;
-    float* T = reinterpret_cast<float*>(workspace);
-    if (r16 > 0) {
-        launch_lora_xa(a, T, s, r16);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+// GEMMs that share the LoRA rank class and the nesting, in one launch: each task's
+// pre-pass first (its partials at T[t]), then the tiles of all tasks, task by task in
+// the given order.
+hipError_t launch_fast_group(const GemmArgs* const* as, float* const* Ts, int32_t count, hipStream_t s) {
+    v4::GemmGroup g;
+    std::memset(&g, 0, sizeof(g));
+    const int r16 = as[0]->A ? (as[0]->r + 15) / 16 : 0;
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        g.t[i] = *as[i];
+        g.T[i] = Ts[i];
+        g.tile0[i] = (int32_t)tiles;
+        tiles += fast_tiles(*as[i]);
+        if (r16 > 0) {
+            launch_lora_xa(*as[i], Ts[i], s, r16);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
-    if (a.w.nested) launch_fast_r<true>(a, T, s, grid, r16);
-    else launch_fast_r<false>(a, T, s, grid, r16);
+    g.tile0[count] = (int32_t)tiles;
+    g.count = count;
+    if (g.t[0].w.nested) launch_fast_r<true>(g, s, r16);
+    else launch_fast_r<false>(g, s, r16);
     return hipGetLastError();
+}
+
+hipError_t launch_fast(const GemmArgs& a, void* workspace, hipStream_t s) {
+    const GemmArgs* as[1] = {&a};
+    float* Ts[1] = {reinterpret_cast<float*>(workspace)};
+    return launch_fast_group(as, Ts, 1, s);
 }
 
 // Ts[i] = T_0[i] + ... + T_{kSplits-1}[i], split order (the same order the GEMM uses).
@@ -1155,8 +1194,10 @@ size_t gemm_workspace_bytes(int64_t M, int32_t r) {
     return r > 0 ? (size_t)v4::kSplits * (size_t)M * (size_t)(((r + 15) / 16) * 16) * sizeof(float) : 0;
 }
 
-hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B, int32_t r,
-                       float lora_scale, void* Y, void* workspace, hipStream_t s, const char** variant) {
+namespace {
+
+GemmArgs gemm_args(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B, int32_t r,
+                   float lora_scale, void* Y) {
     GemmArgs a;
     a.X = reinterpret_cast<const uint16_t*>(X);
     a.A = reinterpret_cast<const uint16_t*>(A);
@@ -1168,11 +1209,24 @@ hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A
     a.K = w.K;
     a.r = A ? r : 0;
     a.lora_scale = lora_scale;
+    return a;
+}
+
+// the fast path's buffer offsets of a 256-row X tile are 32-bit: 256 * K * 2 < 2^31
+bool fast_ok(const GemmArgs& a) {
+    return (a.K % BK) == 0 && (a.K % a.w.blocksize) == 0 && (reinterpret_cast<uintptr_t>(a.X) % 16) == 0 &&
+           (reinterpret_cast<uintptr_t>(a.w.codes) % 16) == 0 && a.K < ((int64_t)1 << 22);
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B, int32_t r,
+                       float lora_scale, void* Y, void* workspace, hipStream_t s, const char** variant) {
+    const GemmArgs a = gemm_args(X, M, w, A, B, r, lora_scale, Y);
     if (a.M > 65535LL * BM || a.N > 65535LL * BN) return hipErrorInvalidValue;   // grid limits of both paths
-    // the fast path's buffer offsets of a 256-row X tile are 32-bit: 256 * K * 2 < 2^31
-    const bool fast = (w.K % BK) == 0 && (w.K % w.w.blocksize) == 0 && (reinterpret_cast<uintptr_t>(X) % 16) == 0 &&
-                      (reinterpret_cast<uintptr_t>(w.w.codes) % 16) == 0 && w.K < ((int64_t)1 << 22);
-    if (fast) {
+    if (fast_ok(a)) {
         *variant = "mfma 32x32x16 bf16, 256x256x64 tiles, W dequantized into B fragments, LoRA X*A pre-pass + epilogue";
         return launch_fast(a, workspace, s);
     }
@@ -1183,6 +1237,73 @@ hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A
     }
     *variant = "generic (element loads, flat-index dequantization), 128x128x64 tiles";
     return launch_typed<true, false>(a, s);
+}
+
+size_t gemm_group_workspace_bytes(const GemmItem* items, int32_t count) {
+    size_t b = 0;
+    for (int32_t i = 0; i < count; ++i)
+        if (items[i].A) b += align256(gemm_workspace_bytes(items[i].M, items[i].r));
+    return b;
+}
+
+hipError_t launch_gemm_group(const GemmItem* items, int32_t count, void* workspace, hipStream_t s,
+                             const char** variant) {
+    // each task with an adapter owns a slice of the workspace, in task order
+    std::vector<GemmArgs> args(count);
+    std::vector<float*> ts(count, nullptr);
+    size_t off = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const GemmItem& it = items[i];
+        args[i] = gemm_args(it.X, it.M, it.w, it.A, it.B, it.r, it.lora_scale, it.Y);
+        if (args[i].M > 65535LL * BM || args[i].N > 65535LL * BN) return hipErrorInvalidValue;
+        if (it.A) {
+            ts[i] = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + off);
+            off += align256(gemm_workspace_bytes(it.M, it.r));
+        }
+    }
+    // tasks the fast kernel cannot take go one by one; the others are launched together
+    // by rank class and nesting, the longest rows first (their tiles take longest, so
+    // they start first and the shorter ones fill in behind them), at most kMaxGemmGroup
+    // at a time
+    std::vector<int32_t> fast;
+    for (int32_t i = 0; i < count; ++i) {
+        if (fast_ok(args[i])) {
+            fast.push_back(i);
+            continue;
+        }
+        const char* v = nullptr;
+        const hipError_t e = launch_gemm(items[i].X, items[i].M, items[i].w, items[i].A, items[i].B, items[i].r,
+                                         items[i].lora_scale, items[i].Y, ts[i], s, &v);
+        if (e != hipSuccess) return e;
+        *variant = v;
+    }
+    std::stable_sort(fast.begin(), fast.end(), [&](int32_t x, int32_t y) { return args[x].K > args[y].K; });
+    std::vector<bool> used(count, false);
+    for (size_t f = 0; f < fast.size(); ++f) {
+        const int32_t i0 = fast[f];
+        if (used[i0]) continue;
+        const int r16 = args[i0].A ? (args[i0].r + 15) / 16 : 0;
+        const bool nested = args[i0].w.nested != 0;
+        const GemmArgs* as[kMaxGemmGroup];
+        float* tsg[kMaxGemmGroup];
+        int32_t n = 0;
+        int64_t tiles = 0;
+        for (size_t f2 = f; f2 < fast.size() && n < kMaxGemmGroup; ++f2) {
+            const int32_t i = fast[f2];
+            if (used[i] || (args[i].A ? (args[i].r + 15) / 16 : 0) != r16 || (args[i].w.nested != 0) != nested) continue;
+            if (tiles + fast_tiles(args[i]) > ((int64_t)1 << 31) - 1) continue;
+            as[n] = &args[i];
+            tsg[n] = ts[i];
+            tiles += fast_tiles(args[i]);
+            ++n;
+            used[i] = true;
+        }
+        const hipError_t e = launch_fast_group(as, tsg, n, s);
+        if (e != hipSuccess) return e;
+        *variant = "mfma 32x32x16 bf16, 256x256x64 tiles of the group's GEMMs in one launch, W dequantized into B "
+                   "fragments, LoRA X*A pre-pass per GEMM + epilogue";
+    }
+    return hipSuccess;
 }
 
 }  // namespace qk

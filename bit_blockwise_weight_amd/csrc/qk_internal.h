@@ -156,6 +156,20 @@ size_t gemm_workspace_bytes(int64_t M, int32_t r);
 // device, then cached).
 size_t gemm_noalloc_scratch_bytes();
 hipError_t gemm_noalloc_scratch(void** ptr);
+// One GEMM of a grouped call.
+struct GemmItem {
+    const void* X;
+    int64_t M;
+    MatArgs w;
+    const void* A;
+    const void* B;
+    int32_t r;
+    float lora_scale;
+    void* Y;
+};
+size_t gemm_group_workspace_bytes(const GemmItem* items, int32_t count);
+hipError_t launch_gemm_group(const GemmItem* items, int32_t count, void* workspace, hipStream_t s,
+                             const char** variant);
 hipError_t launch_gemm(const void* X, int64_t M, const MatArgs& w, const void* A, const void* B,
                        int32_t r, float lora_scale, void* Y, void* workspace, hipStream_t s,
                        const char** variant);

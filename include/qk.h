@@ -348,6 +348,42 @@ qk_status qk_gemm_nf4(const void* X, int64_t M, const qk_quant_state* st, const 
                       size_t workspace_bytes, void* stream);
 
 /*
+ * qk_gemm_nf4_grouped — device.  Several qk_gemm_nf4 products (the weights of
+ * a layer, each with its own X, adapter and Y) in as few launches as their
+ * shapes allow ([DEQ] sections 2-2 and 8; [NF4] §2.2).  Each Y is the one
+ * qk_gemm_nf4 of that task alone writes, bit for bit.  The tasks whose weights
+ * the 256 x 256 kernel takes (K a multiple of 64 and of the block size, 16-byte
+ * aligned X and codes) and that share the rank class ceil(r / 16) and the
+ * nesting run in one launch (up to 8 per launch), longest rows first, after
+ * their LoRA pre-passes; the others run one by one.  One launch packs the tiles
+ * of all its GEMMs, so no GEMM's partial last round leaves CUs idle.
+ *   tasks: host, ntasks (1..256) descriptors; X, M, st, A, B, r, lora_scale
+ *     and Y as for qk_gemm_nf4.  Every Y must be disjoint from the other Ys,
+ *     from every X and from the workspace.
+ *   workspace: device, >= qk_gemm_nf4_grouped_workspace_size bytes, 16-byte
+ *     aligned (may be NULL when no task has an adapter); contents ignored.
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_WORKSPACE, QK_ERR_HIP
+ *   (the argument checks run before anything is launched).
+ */
+typedef struct {
+    const void* X;               /* device, [M, K] bf16 */
+    int64_t M;
+    const qk_quant_state* st;    /* the weight, [N, K] */
+    const void* A;               /* device, [K, r] bf16, or NULL */
+    const void* B;               /* device, [r, N] bf16, or NULL */
+    int32_t r;
+    float lora_scale;
+    void* Y;                     /* device, [M, N] bf16, written */
+} qk_gemm_task;
+
+/* Bytes of workspace qk_gemm_nf4_grouped needs for these tasks (the sum of the
+ * tasks' LoRA partials, each rounded up to 256 bytes).  Host only. */
+qk_status qk_gemm_nf4_grouped_workspace_size(const qk_gemm_task* tasks, int32_t ntasks, size_t* bytes);
+
+qk_status qk_gemm_nf4_grouped(const qk_gemm_task* tasks, int32_t ntasks, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * qk_gemm_nf4_noalloc — device.  qk_gemm_nf4 for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same kernels and the same result, bit for bit, as

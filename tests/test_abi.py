@@ -361,6 +361,60 @@ def test_gemm_noalloc_argument_errors(L):
     assert call(FAKE, 8193, ctypes.byref(st), FAKE, FAKE, 17, 2.0, FAKE, None) == qk.QK_ERR_WORKSPACE
 
 
+def test_gemm_grouped_argument_errors_and_workspace(L):
+    st = _state()                        # W [4, 64]: X [M, 64], Y [M, 4]
+    T = qk.GemmTask
+
+    def arr(*entries):
+        a = (T * len(entries))()
+        for i, (x, m, s, A, B, r, y) in enumerate(entries):
+            a[i].X, a[i].M, a[i].A, a[i].B, a[i].r, a[i].lora_scale, a[i].Y = x, m, A, B, r, 2.0, y
+            a[i].st = None if s is None else ctypes.pointer(s)
+        return a
+
+    X0, Y0, Y1, A0, B0 = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    size = ctypes.c_size_t()
+    ws = L.qk_gemm_nf4_grouped_workspace_size
+    # workspace: the tasks' LoRA partials, each rounded up to 256 bytes; none without adapters
+    assert ws(arr((X0, 10, st, None, None, 0, Y0)), 1, ctypes.byref(size)) == qk.QK_OK and size.value == 0
+    assert ws(arr((X0, 10, st, A0, B0, 16, Y0), (X0, 300, st, A0, B0, 40, Y1)), 2, ctypes.byref(size)) == qk.QK_OK
+    one = lambda M, r: (qk.qk_gemm_nf4_workspace_size(M, r) + 255) // 256 * 256
+    assert size.value == one(10, 16) + one(300, 40)
+    assert ws(arr((X0, 10, st, A0, B0, 16, Y0)), 1, None) == qk.QK_ERR_INVALID_ARG
+    call = L.qk_gemm_nf4_grouped
+    ok = arr((X0, 10, st, None, None, 0, Y0))
+    assert call(None, 1, None, 0, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 0, None, 0, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 257, None, 0, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((X0, 10, None, None, None, 0, Y0)), 1, None, 0, None) == qk.QK_ERR_INVALID_ARG
+    bad = _state()
+    bad.version = 7
+    assert call(arr((X0, 10, st, None, None, 0, Y0), (X0, 10, bad, None, None, 0, Y1)), 2, None, 0, None) \
+        == qk.QK_ERR_BAD_STATE
+    assert call(arr((X0, 0, st, None, None, 0, Y0)), 1, None, 0, None) == qk.QK_ERR_INVALID_ARG      # M < 1
+    assert call(arr((X0, 10, st, A0, None, 16, Y0)), 1, None, 0, None) == qk.QK_ERR_INVALID_ARG      # A without B
+    assert call(arr((X0, 10, st, A0, B0, 65, Y0)), 1, None, 0, None) == qk.QK_ERR_INVALID_ARG        # rank > 64
+    assert "task 0" in qk.qk_last_error()
+    # workspace missing, too small, misaligned
+    lora = arr((X0, 10, st, A0, B0, 16, Y0))
+    need = one(10, 16)
+    assert call(lora, 1, None, 0, None) == qk.QK_ERR_WORKSPACE
+    assert call(lora, 1, ctypes.c_void_p(0x600000), need - 1, None) == qk.QK_ERR_WORKSPACE
+    assert call(lora, 1, ctypes.c_void_p(0x600008), need, None) == qk.QK_ERR_INVALID_ARG
+    # Y [10, 4] bf16 = 80 bytes: overlapping outputs, an output over an input or the workspace
+    assert call(arr((X0, 10, st, None, None, 0, Y0), (X0, 10, st, None, None, 0, Y0 + 78)), 2, None, 0, None) \
+        == qk.QK_ERR_INVALID_ARG
+    assert "overlaps Y" in qk.qk_last_error()
+    assert call(arr((X0, 10, st, None, None, 0, Y0), (X0, 10, st, None, None, 0, X0 + 64)), 2, None, 0, None) \
+        == qk.QK_ERR_INVALID_ARG
+    assert "overlaps X" in qk.qk_last_error()
+    assert call(lora, 1, ctypes.c_void_p(Y0 - 64), need, None) == qk.QK_ERR_INVALID_ARG
+    assert "workspace" in qk.qk_last_error()
+    # valid arguments get as far as the device check (no GPU here)
+    st_ok = call(arr((X0, 10, st, None, None, 0, Y0), (X0, 10, st, None, None, 0, Y1)), 2, None, 0, None)
+    assert st_ok not in (qk.QK_OK, qk.QK_ERR_INVALID_ARG, qk.QK_ERR_BAD_STATE, qk.QK_ERR_WORKSPACE)
+
+
 def test_gemv_grouped_argument_errors(L):
     st = _state()                        # W [4, 64]
     T = qk.GemvTask
