@@ -154,7 +154,7 @@ def build_workload(torch, qk, workloads):
                           dtype=torch.uint8, device=dev)
     levels_c = (ctypes.c_float * 16)(*lv.tolist())
     return {"mats": mats, "acts": acts, "lora": lora, "M": M_TOK, "r": R, "levels": lv, "levels_c": levels_c,
-            "gemm_ws": gemm_ws, "dq_call": dq_group_call(torch, qk, mats),
+            "gemm_ws": gemm_ws, "dq_call": dq_group_call(torch, qk, mats), "deq_call": deq_group_call(torch, qk, mats),
             "gemm_call": gemm_group_call(torch, qk, [(acts[m["K"]]["X"], m["state"]) + lora[m["name"]] + (2.0,)
                                                      for m in mats], [m["Y"] for m in mats], gemm_ws),
             "q_call": quant_group_call(torch, qk, mats, levels_c)}
@@ -165,9 +165,9 @@ OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lo
 
 def step_calls(torch, qk, wl):
     """The launches of one pass of the hot path over the layer set, in order, as
-    (op, matrices, callable): the quantization of the layer's weights and the
-    double quantization of their absmax arrays, one grouped call each; per weight
-    dequantize; the prefill GEMM with LoRA of the whole layer, one grouped call
+    (op, matrices, callable): the quantization of the layer's weights, the
+    double quantization of their absmax arrays and their dequantization, one
+    grouped call each; the prefill GEMM with LoRA of the whole layer, one grouped call
     (the seven GEMMs' tiles in one launch after their LoRA pre-passes); then the
     decode GEMV of the whole layer at M = 1 and at M = 16, one grouped call each
     (the way a decoder runs a layer)."""
@@ -175,8 +175,7 @@ def step_calls(torch, qk, wl):
     calls = []
     calls.append(("quantize", list(mats), wl["q_call"]))
     calls.append(("double_quant", list(mats), wl["dq_call"]))
-    for m in mats:
-        calls.append(("dequantize", [m], lambda m=m: qk.qk_dequantize(m["state"], torch.bfloat16, m["deq"])))
+    calls.append(("dequantize", list(mats), wl["deq_call"]))
     calls.append(("gemm_lora", list(mats), wl["gemm_call"]))
     for op, xk, yk in (("gemv_m1", "x1", "y1"), ("gemv_m16", "x16", "y16")):
         items = [(wl["acts"][m["K"]][xk], m["state"]) for m in mats]
@@ -440,6 +439,25 @@ def quant_group_call(torch, qk, mats, levels_c, blocksize=64):
             raise RuntimeError(f"qk_quantize_blockwise_grouped: {qk.qk_last_error()}")
 
     call.keep = (arr, mats, levels_c)
+    return call
+
+
+def deq_group_call(torch, qk, mats):
+    """A prepared qk_dequantize_grouped of the matrices' states into their bf16
+    buffers (the task array built once)."""
+    arr = (qk.DequantTask * len(mats))()
+    for i, m in enumerate(mats):
+        arr[i].st = ctypes.pointer(m["state"])
+        arr[i].out = m["deq"].data_ptr()
+    L = qk.lib()
+    n = len(mats)
+
+    def call():
+        rc = L.qk_dequantize_grouped(arr, n, qk.QK_BF16, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"qk_dequantize_grouped: {qk.qk_last_error()}")
+
+    call.keep = (arr, mats)
     return call
 
 

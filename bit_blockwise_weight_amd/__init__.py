@@ -21,7 +21,7 @@ __all__ = [
     "qk_double_quant",
     "qk_double_quant_grouped_workspace_size", "qk_double_quant_grouped",
     "qk_state_init", "qk_dequantize", "qk_gemv_nf4", "qk_gemv_nf4_grouped", "qk_gemm_nf4_workspace_size", "qk_gemm_nf4", "qk_gemm_nf4_noalloc",
-    "qk_gemm_nf4_grouped_workspace_size", "qk_gemm_nf4_grouped", "GemmTask", "qk_last_error", "qk_version",
+    "qk_gemm_nf4_grouped_workspace_size", "qk_gemm_nf4_grouped", "GemmTask", "qk_dequantize_grouped", "DequantTask", "qk_last_error", "qk_version",
     "qk_backend_info", "quantize",
 ]
 
@@ -88,6 +88,11 @@ class GemvTask(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("st", ctypes.POINTER(QuantState)), ("y", ctypes.c_void_p)]
 
 
+class DequantTask(ctypes.Structure):
+    """Mirror of qk_dequant_task (include/qk.h)."""
+    _fields_ = [("st", ctypes.POINTER(QuantState)), ("out", ctypes.c_void_p)]
+
+
 class GemmTask(ctypes.Structure):
     """Mirror of qk_gemm_task (include/qk.h)."""
     _fields_ = [("X", ctypes.c_void_p), ("M", ctypes.c_int64), ("st", ctypes.POINTER(QuantState)),
@@ -130,6 +135,7 @@ def lib():
         "qk_gemv_nf4": [vp, i32, st_p, vp, vp],
         "qk_gemv_nf4_grouped": [ctypes.POINTER(GemvTask), i32, i32, vp],
         "qk_gemm_nf4_workspace_size": [i64, i32, ctypes.POINTER(ctypes.c_size_t)],
+        "qk_dequantize_grouped": [ctypes.POINTER(DequantTask), i32, i32, vp],
         "qk_gemm_nf4_grouped_workspace_size": [ctypes.POINTER(GemmTask), i32, ctypes.POINTER(ctypes.c_size_t)],
         "qk_gemm_nf4_grouped": [ctypes.POINTER(GemmTask), i32, vp, ctypes.c_size_t, vp],
         "qk_gemm_nf4": [vp, i64, st_p, vp, vp, i32, f32, vp, vp, ctypes.c_size_t, vp],
@@ -483,6 +489,33 @@ def qk_dequantize(state: QuantState, out_dtype=torch.bfloat16, out=None, device=
         _check(lib().qk_dequantize(ctypes.byref(state), _ptr(out), _DTYPE_CODE[out.dtype],
                                    ctypes.c_void_p(_stream(out))))
     return out
+
+
+def qk_dequantize_grouped(states, out_dtype=torch.bfloat16, outs=None):
+    """qk_dequantize of several states in as few launches as their level tables
+    allow; returns the outputs (given in outs, or allocated)."""
+    states = list(states)
+    if not states:
+        raise ValueError("qk_dequantize_grouped needs at least one state")
+    if outs is None:
+        outs = [torch.empty(st.n, dtype=out_dtype, device=st._keep[0].device) for st in states]
+    outs = list(outs)
+    if len(outs) != len(states):
+        raise ValueError(f"{len(states)} states but {len(outs)} outputs")
+    dts = {o.dtype for o in outs}
+    if len(dts) != 1 or next(iter(dts)) not in _DTYPE_CODE:
+        raise ValueError(f"every output must have one dtype, float32 or bfloat16 (got {dts})")
+    arr = (DequantTask * len(states))()
+    for i, (st, o) in enumerate(zip(states, outs)):
+        if o.numel() != st.n:
+            raise ValueError(f"task {i}: out holds {o.numel()} elements, the state {st.n}")
+        _require_cuda(o)
+        arr[i].st = ctypes.pointer(st)
+        arr[i].out = o.data_ptr()
+    with _on(outs[0].device):
+        _check(lib().qk_dequantize_grouped(arr, len(states), _DTYPE_CODE[outs[0].dtype],
+                                           ctypes.c_void_p(_stream(outs[0]))))
+    return outs
 
 
 def _rows_of(t: torch.Tensor, cols: int, name: str) -> torch.Tensor:

@@ -465,6 +465,37 @@ qk_status qk_dequantize(const qk_quant_state* st, void* out, int32_t out_dtype, 
                     "qk_dequantize");
 }
 
+qk_status qk_dequantize_grouped(const qk_dequant_task* tasks, int32_t ntasks, int32_t out_dtype, void* stream) {
+    const char* who = "qk_dequantize_grouped";
+    if (!tasks) return fail(QK_ERR_INVALID_ARG, "%s: tasks is NULL", who);
+    if (ntasks < 1 || ntasks > 256) return fail(QK_ERR_INVALID_ARG, "%s: ntasks must be in 1..256 (got %d)", who, ntasks);
+    if (out_dtype != QK_BF16 && out_dtype != QK_F32)
+        return fail(QK_ERR_INVALID_ARG, "%s: out dtype %d (expected QK_F32 or QK_BF16)", who, out_dtype);
+    const uintptr_t esize = out_dtype == QK_BF16 ? 2 : 4;
+    std::vector<qk::DeqItem> items((size_t)ntasks);
+    for (int32_t i = 0; i < ntasks; ++i) {
+        const qk_status v = validate_state(tasks[i].st);
+        if (v != QK_OK) return v;
+        if (!tasks[i].out) return fail(QK_ERR_INVALID_ARG, "%s: task %d: out is NULL", who, i);
+        if (!aligned(tasks[i].out, 16)) return fail(QK_ERR_INVALID_ARG, "%s: task %d: out must be 16-byte aligned", who, i);
+        items[i] = qk::DeqItem{deq_args(tasks[i].st), tasks[i].out};
+    }
+    // the arrays of a launch are written at once: every out must be disjoint from the others
+    for (int32_t i = 0; i < ntasks; ++i) {
+        const uintptr_t o0 = reinterpret_cast<uintptr_t>(tasks[i].out);
+        const uintptr_t o1 = o0 + (uintptr_t)tasks[i].st->n * esize;
+        for (int32_t j = i + 1; j < ntasks; ++j) {
+            const uintptr_t p0 = reinterpret_cast<uintptr_t>(tasks[j].out);
+            const uintptr_t p1 = p0 + (uintptr_t)tasks[j].st->n * esize;
+            if (p0 < o1 && o0 < p1) return fail(QK_ERR_INVALID_ARG, "%s: out of task %d overlaps out of task %d", who, i, j);
+        }
+    }
+    const qk_status dev = ensure_device();
+    if (dev != QK_OK) return dev;
+    return launched(qk::launch_dequantize_group(items.data(), ntasks, out_dtype, reinterpret_cast<hipStream_t>(stream)),
+                    who);
+}
+
 qk_status qk_lora_merge(const qk_quant_state* st, const void* A, const void* B, int32_t r, float lora_scale,
                         void* out, void* stream) {
     const qk_status v = validate_state(st);

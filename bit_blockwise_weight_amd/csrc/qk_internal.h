@@ -132,6 +132,12 @@ struct DeqArgs {
     float levels[16];
 };
 hipError_t launch_dequantize(const DeqArgs& a, void* out, int32_t out_dtype, hipStream_t s);
+// one array of a grouped dequantization
+struct DeqItem {
+    DeqArgs a;
+    void* out;
+};
+hipError_t launch_dequantize_group(const DeqItem* items, int32_t count, int32_t out_dtype, hipStream_t s);
 
 struct MatArgs {
     DeqArgs w;       // the weight [N, K]

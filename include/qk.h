@@ -277,6 +277,25 @@ qk_status qk_state_init(qk_quant_state* st, int32_t codebook_kind, const float* 
 qk_status qk_dequantize(const qk_quant_state* st, void* out, int32_t out_dtype, void* stream);
 
 /*
+ * qk_dequantize_grouped — device.  qk_dequantize of several states (the
+ * weights of a layer) in as few launches as their level tables allow (up to 16
+ * arrays of one table per launch; [DEQ] section 5).  Each out holds what
+ * qk_dequantize of that state alone writes, bit for bit.
+ *   tasks: host, ntasks (1..256) pairs of a valid descriptor and its output
+ *     (device, [rows * cols] elements of out_dtype, 16-byte aligned, written);
+ *     the outputs must be pairwise disjoint.
+ *   out_dtype: QK_F32 or QK_BF16, for every task.
+ *   Errors: QK_ERR_BAD_STATE, QK_ERR_INVALID_ARG, QK_ERR_HIP (the argument
+ *   checks run before anything is launched).
+ */
+typedef struct {
+    const qk_quant_state* st;
+    void* out;
+} qk_dequant_task;
+
+qk_status qk_dequantize_grouped(const qk_dequant_task* tasks, int32_t ntasks, int32_t out_dtype, void* stream);
+
+/*
  * qk_gemv_nf4 — device.  Decode-time product with the dequantized weight:
  *     y[m, :] = x[m, :] · deq(W)^T,  m < M,
  *   [NF4] 【代码】 (4-bit linear forward: dequantize + matmul), [DEQ] section 5.

@@ -415,6 +415,38 @@ def test_gemm_grouped_argument_errors_and_workspace(L):
     assert st_ok not in (qk.QK_OK, qk.QK_ERR_INVALID_ARG, qk.QK_ERR_BAD_STATE, qk.QK_ERR_WORKSPACE)
 
 
+def test_dequantize_grouped_argument_errors(L):
+    st = _state()                        # W [4, 64]: 256 elements
+    T = qk.DequantTask
+
+    def arr(*entries):
+        a = (T * len(entries))()
+        for i, (s, o) in enumerate(entries):
+            a[i].st = None if s is None else ctypes.pointer(s)
+            a[i].out = o
+        return a
+
+    O0, O1 = 0x100000, 0x200000
+    call = L.qk_dequantize_grouped
+    ok = arr((st, O0), (st, O1))
+    assert call(None, 1, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 0, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 257, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
+    assert call(ok, 2, 9, None) == qk.QK_ERR_INVALID_ARG                           # out dtype
+    assert call(arr((None, O0)), 1, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
+    bad = _state()
+    bad.version = 7
+    assert call(arr((st, O0), (bad, O1)), 2, qk.QK_BF16, None) == qk.QK_ERR_BAD_STATE
+    assert call(arr((st, None)), 1, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
+    assert call(arr((st, O0 + 8)), 1, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG    # out not 16-byte aligned
+    # 256 bf16 = 512 bytes, 256 fp32 = 1024 bytes
+    assert call(arr((st, O0), (st, O0 + 496)), 2, qk.QK_BF16, None) == qk.QK_ERR_INVALID_ARG
+    assert "overlaps" in qk.qk_last_error()
+    assert call(arr((st, O0), (st, O0 + 512)), 2, qk.QK_F32, None) == qk.QK_ERR_INVALID_ARG
+    st_ok = call(arr((st, O0), (st, O0 + 512)), 2, qk.QK_BF16, None)
+    assert st_ok not in (qk.QK_OK, qk.QK_ERR_INVALID_ARG, qk.QK_ERR_BAD_STATE)
+
+
 def test_gemv_grouped_argument_errors(L):
     st = _state()                        # W [4, 64]
     T = qk.GemvTask
