@@ -134,14 +134,20 @@ def build_workload(torch, qk, workloads):
         }
         m["state"] = qk.qk_state_init(qk.NF4, lv, N, K, 64, m["codes"], None, m["q8"], m["scale"], m["mean"])
         mats.append(m)
+    # one input per group of weights that read the same activations in a decoder layer:
+    # q, k, v the normed hidden state; o the attention output; gate, up the normed
+    # post-attention state; down the gated product
+    for m in mats:
+        m["in"] = INPUT_OF[m["name"]]
     acts = {}
-    for K in sorted(set(m["K"] for m in mats)):
-        acts[K] = {
-            "x1": torch.from_numpy(workloads.activations("llama7b_layer", 1, K, tag=100 + K).view("int16"))
+    for gi, name in enumerate(INPUT_GROUPS):
+        K = next(m["K"] for m in mats if m["in"] == name)
+        acts[name] = {
+            "x1": torch.from_numpy(workloads.activations("llama7b_layer", 1, K, tag=100 + K + 10000 * gi).view("int16"))
             .view(torch.bfloat16).to(dev),
-            "x16": torch.from_numpy(workloads.activations("llama7b_layer", 16, K, tag=200 + K).view("int16"))
-            .view(torch.bfloat16).to(dev),
-            "X": torch.from_numpy(workloads.activations("qlora_prefill", M_TOK, K, tag=K).view("int16"))
+            "x16": torch.from_numpy(workloads.activations("llama7b_layer", 16, K, tag=200 + K + 10000 * gi)
+                                    .view("int16")).view(torch.bfloat16).to(dev),
+            "X": torch.from_numpy(workloads.activations("qlora_prefill", M_TOK, K, tag=K + 10000 * gi).view("int16"))
             .view(torch.bfloat16).to(dev),
         }
     lora = {}
@@ -155,12 +161,16 @@ def build_workload(torch, qk, workloads):
     levels_c = (ctypes.c_float * 16)(*lv.tolist())
     return {"mats": mats, "acts": acts, "lora": lora, "M": M_TOK, "r": R, "levels": lv, "levels_c": levels_c,
             "gemm_ws": gemm_ws, "dq_call": dq_group_call(torch, qk, mats), "deq_call": deq_group_call(torch, qk, mats),
-            "gemm_call": gemm_group_call(torch, qk, [(acts[m["K"]]["X"], m["state"]) + lora[m["name"]] + (2.0,)
+            "gemm_call": gemm_group_call(torch, qk, [(acts[m["in"]]["X"], m["state"]) + lora[m["name"]] + (2.0,)
                                                      for m in mats], [m["Y"] for m in mats], gemm_ws),
             "q_call": quant_group_call(torch, qk, mats, levels_c)}
 
 
 OPS = ["quantize", "double_quant", "dequantize", "gemv_m1", "gemv_m16", "gemm_lora"]
+# the activations each weight of the layer reads
+INPUT_GROUPS = ["attn_in", "attn_out", "mlp_in", "mlp_act"]
+INPUT_OF = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "attn_out", "gate": "mlp_in", "up": "mlp_in",
+            "down": "mlp_act"}
 
 
 def step_calls(torch, qk, wl):
@@ -178,7 +188,7 @@ def step_calls(torch, qk, wl):
     calls.append(("dequantize", list(mats), wl["deq_call"]))
     calls.append(("gemm_lora", list(mats), wl["gemm_call"]))
     for op, xk, yk in (("gemv_m1", "x1", "y1"), ("gemv_m16", "x16", "y16")):
-        items = [(wl["acts"][m["K"]][xk], m["state"]) for m in mats]
+        items = [(wl["acts"][m["in"]][xk], m["state"]) for m in mats]
         ys = [m[yk] for m in mats]
         calls.append((op, list(mats), lambda items=items, ys=ys: qk.qk_gemv_nf4_grouped(items, ys)))
     return calls
@@ -291,7 +301,7 @@ def backward_rate(torch, qk, wl, iters=5):
 
     def run(lora):
         for m, dA, dB in zip(mats, das, dbs):
-            X = wl["acts"][m["K"]]["X"]
+            X = wl["acts"][m["in"]]["X"]
             if lora:
                 A, Bm = wl["lora"][m["name"]]
                 qk.qk_qlora_backward(dys[m["N"]], m["state"], X, A, Bm, 2.0, dxs[m["K"]], dA, dB, ws)

@@ -36,8 +36,8 @@ def _task(g, M, N, K, B=64, kind=ocb.NF4, nested=True, r=16):
 
 
 def _check(tasks, oracle_idx=()):
-    ys = qk.qk_gemm_nf4_grouped([(t["Xd"], t["qw"].state, t["Ad"], t["Bd"], 2.0) for t in tasks])
-    singles = [t["qw"].gemm(t["Xd"], t["Ad"], t["Bd"], 2.0) for t in tasks]
+    ys = qk.qk_gemm_nf4_grouped([(t["Xd"], t["qw"].state, t["Ad"], t["Bd"], t.get("s", 2.0)) for t in tasks])
+    singles = [t["qw"].gemm(t["Xd"], t["Ad"], t["Bd"], t.get("s", 2.0)) for t in tasks]
     torch.cuda.synchronize()
     for i, (t, y, y1) in enumerate(zip(tasks, ys, singles)):
         assert_bits_equal(host(y), host(y1), f"task {i} [{t['M']}x{t['N']}x{t['K']}] r={t['r']} grouped vs alone")
@@ -48,7 +48,7 @@ def _check(tasks, oracle_idx=()):
         Xf = bf16_bits_to_f32(t["X"]).reshape(M, K)
         if r:
             ref = omm.qlora_forward_f64(Xf, wd, bf16_bits_to_f32(t["A"]).reshape(K, r),
-                                        bf16_bits_to_f32(t["Bm"]).reshape(r, N), 2.0)
+                                        bf16_bits_to_f32(t["Bm"]).reshape(r, N), t.get("s", 2.0))
         else:
             ref = omm.qlora_forward_f64(Xf, wd)
         check_close(bf16_bits_to_f32(host(ys[i])).reshape(M, N), ref, f"task {i} vs oracle")
@@ -73,6 +73,25 @@ def test_grouped_mixed_ranks_shapes_and_paths():
              _task(g, 200, 96, 4099, r=16), _task(g, 64, 512, 768, B=128, r=16), _task(g, 1, 33, 512, r=16),
              _task(g, 96, 64, 11008, r=16)]
     _check(tasks, oracle_idx=(0, 3, 5, 7))
+
+
+def test_grouped_shared_input_and_scales():
+    """Seven GEMMs reading one X, with adapters of 16, 16, 32, 16, 48, 16 and 24 ranks
+    and scales of their own, and one more on another X: every Y must equal its
+    single call bit for bit."""
+    say("case: grouped gemm shared X, own scales")
+    g = np.random.default_rng(13)
+    M, K = 512, 1024
+    X = ofl.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    Xd = dev_bf16(X).reshape(M, K)
+    tasks = []
+    for j, (N, r, sc) in enumerate([(256, 16, 2.0), (384, 16, 0.5), (300, 32, 1.0), (256, 16, 3.0), (512, 48, 0.25),
+                                    (128, 16, 2.0), (256, 24, 1.5)]):
+        t = _task(g, M, N, K, r=r)
+        t.update(X=X, Xd=Xd, s=sc)
+        tasks.append(t)
+    tasks.append(_task(g, M, 256, 2048, r=16))
+    _check(tasks, oracle_idx=(2, 4, 6))
 
 
 def test_grouped_more_than_one_launch_of_tasks():
