@@ -1063,7 +1063,7 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path
                              "fetch_scale": fetch_scale, "write_scale": write_scale},
         "fetch_bytes_per_dispatch": f_gemm * fetch_scale, "write_bytes_per_dispatch": w_gemm * write_scale,
         "bytes_per_dispatch": f_gemm * fetch_scale + w_gemm * write_scale,
-        "note": "average over the dispatches of the bench step (7 weight shapes)",
+        "note": "average over the dispatches of the bench step (one grouped launch over the 7 weights per step)",
     }
     with open(out_path, "w") as fh:
         json.dump(out, fh, indent=1)
