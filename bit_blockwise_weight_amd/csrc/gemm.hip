@@ -918,8 +918,26 @@ __global__ __launch_bounds__(512, 1) void gemm_fast_kernel(GemmGroup gg) {
 // are clamped to the split's last step.  (An 8-deep ring measured slower.)  The GEMM
 // kernel adds the kSplits partials of its rows in split order (deterministic)
 // when it stages s X A.
+// The pre-passes of one launch (a single call is a group of one): GEMM t owns the
+// workgroups [blk0[t], blk0[t + 1]), one per 64-row block and K split (row block
+// fastest), and writes its partials at T[t].
+struct XaGroup {
+    GemmArgs t[kMaxGemmGroup];
+    float* T[kMaxGemmGroup];
+    int32_t blk0[kMaxGemmGroup + 1];
+    int32_t count;
+};
+
 template <int R16, bool kVec>
-__global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restrict__ T) {
+__global__ __launch_bounds__(256) void lora_xa_kernel(XaGroup gx) {
+    // this workgroup's GEMM (uniform: a scalar search of the launch's prefix table)
+    int task = 0;
+    while (task + 1 < gx.count && (int32_t)blockIdx.x >= gx.blk0[task + 1]) ++task;
+    const GemmArgs& a = gx.t[task];
+    float* __restrict__ T = gx.T[task];
+    const int32_t nrb = (int32_t)((a.M + 63) / 64);
+    const int32_t local = (int32_t)blockIdx.x - gx.blk0[task];
+    const int32_t rb = local % nrb;
     constexpr int kRp = 16 * R16;
     constexpr int kChunk = R16 == 1 ? 16 : (R16 == 2 ? 8 : 4);   // steps per A^T chunk (about 33 KB of LDS)
     constexpr int kS = kChunk * TK + 8;                           // A^T row pitch (elements)
@@ -929,9 +947,9 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
     const int64_t M = a.M, K = a.K;
     const int r = a.r;
     const int64_t nk = K / TK;
-    const int split = blockIdx.y;
+    const int split = local / nrb;
     const int64_t s0 = nk * split / kSplits, s1 = nk * (split + 1) / kSplits;
-    const int64_t mrow = (int64_t)blockIdx.x * 64 + 16 * wave + l16;
+    const int64_t mrow = (int64_t)rb * 64 + 16 * wave + l16;
     const int64_t mrow_c = mrow < M ? mrow : M - 1;
     const uint16_t* xrow = a.X + mrow_c * K + 8 * q4;
     // kVec: r % 8 == 0 and A 16-byte aligned (A rows load as 16-byte pieces)
@@ -1056,7 +1074,7 @@ __global__ __launch_bounds__(256) void lora_xa_kernel(GemmArgs a, float* __restr
     for (int jt = 0; jt < R16; ++jt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int64_t m = (int64_t)blockIdx.x * 64 + 16 * wave + 4 * q4 + e;
+            const int64_t m = (int64_t)rb * 64 + 16 * wave + 4 * q4 + e;
             if (m < M) Tp[m * kRp + 16 * jt + l16] = acc[jt][e] * a.lora_scale;
         }
     }
@@ -1076,15 +1094,31 @@ void launch_fast_r(const v4::GemmGroup& g, hipStream_t s, int r16) {
     }
 }
 
+// an adapter whose rows load as 16-byte pieces
+bool lora_vec(const GemmArgs& a) { return (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.A) % 16) == 0; }
+
 int64_t fast_tiles(const GemmArgs& a) { return ((a.N + v4::TN - 1) / v4::TN) * ((a.M + v4::TM - 1) / v4::TM); }
 
-void launch_lora_xa(const GemmArgs& a, float* T, hipStream_t s, int r16) {
-    const dim3 grid((unsigned)((a.M + 63) / 64), v4::kSplits);
-    const bool vec = (a.r % 8) == 0 && (reinterpret_cast<uintptr_t>(a.A) % 16) == 0;
+// pre-passes that share the rank class and the 16-byte adapter loads, in one launch
+void launch_lora_xa_group(const GemmArgs* const* as, float* const* Ts, int32_t count, hipStream_t s) {
+    v4::XaGroup g;
+    std::memset(&g, 0, sizeof(g));
+    int64_t blocks = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        g.t[i] = *as[i];
+        g.T[i] = Ts[i];
+        g.blk0[i] = (int32_t)blocks;
+        blocks += ((as[i]->M + 63) / 64) * v4::kSplits;
+    }
+    g.blk0[count] = (int32_t)blocks;
+    g.count = count;
+    const dim3 grid((unsigned)blocks);
+    const bool vec = lora_vec(*as[0]);
+    const int r16 = (as[0]->r + 15) / 16;
 #define QK_LORA_XA(R)                                                                  \
     do {                                                                               \
-        if (vec) hipLaunchKernelGGL((v4::lora_xa_kernel<R, true>), grid, dim3(256), 0, s, a, T); \
-        else hipLaunchKernelGGL((v4::lora_xa_kernel<R, false>), grid, dim3(256), 0, s, a, T);    \
+        if (vec) hipLaunchKernelGGL((v4::lora_xa_kernel<R, true>), grid, dim3(256), 0, s, g); \
+        else hipLaunchKernelGGL((v4::lora_xa_kernel<R, false>), grid, dim3(256), 0, s, g);    \
     } while (0)
     switch (r16) {
         case 1: QK_LORA_XA(1); break;
@@ -1095,8 +1129,15 @@ void launch_lora_xa(const GemmArgs& a, float* T, hipStream_t s, int r16) {
 #undef QK_LORA_XA
 }
 
-// GEMMs that share the LoRA rank class and the nesting, in one launch: each task's
-// pre-pass first (its partials at T[t]), then the tiles of all tasks, task by task in
+void launch_lora_xa(const GemmArgs& a, float* T, hipStream_t s, int r16) {
+    (void)r16;
+    const GemmArgs* as[1] = {&a};
+    float* Ts[1] = {T};
+    launch_lora_xa_group(as, Ts, 1, s);
+}
+
+// GEMMs that share the LoRA rank class and the nesting, in one launch (their LoRA
+// partials already formed, task t's at Ts[t]): the tiles of all tasks, task by task in
 // the given order.
 hipError_t launch_fast_group(const GemmArgs* const* as, float* const* Ts, int32_t count, hipStream_t s) {
     v4::GemmGroup g;
@@ -1108,11 +1149,6 @@ hipError_t launch_fast_group(const GemmArgs* const* as, float* const* Ts, int32_
         g.T[i] = Ts[i];
         g.tile0[i] = (int32_t)tiles;
         tiles += fast_tiles(*as[i]);
-        if (r16 > 0) {
-            launch_lora_xa(*as[i], Ts[i], s, r16);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
     }
     g.tile0[count] = (int32_t)tiles;
     g.count = count;
@@ -1122,8 +1158,14 @@ hipError_t launch_fast_group(const GemmArgs* const* as, float* const* Ts, int32_
 }
 
 hipError_t launch_fast(const GemmArgs& a, void* workspace, hipStream_t s) {
+    float* T = reinterpret_cast<float*>(workspace);
+    if (a.A) {
+        launch_lora_xa(a, T, s, (a.r + 15) / 16);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const GemmArgs* as[1] = {&a};
-    float* Ts[1] = {reinterpret_cast<float*>(workspace)};
+    float* Ts[1] = {T};
     return launch_fast_group(as, Ts, 1, s);
 }
 
@@ -1276,6 +1318,35 @@ hipError_t launch_gemm_group(const GemmItem* items, int32_t count, void* workspa
                                          items[i].lora_scale, items[i].Y, ts[i], s, &v);
         if (e != hipSuccess) return e;
         *variant = v;
+    }
+    // the LoRA pre-passes of the fast GEMMs, together by rank class and adapter loads
+    // (their latency chains overlap: one launch instead of one per GEMM)
+    {
+        std::vector<bool> done(count, false);
+        for (size_t f = 0; f < fast.size(); ++f) {
+            const int32_t i0 = fast[f];
+            if (done[i0] || !args[i0].A) continue;
+            const int r16 = (args[i0].r + 15) / 16;
+            const bool vec = lora_vec(args[i0]);
+            const GemmArgs* as[kMaxGemmGroup];
+            float* tsg[kMaxGemmGroup];
+            int32_t n = 0;
+            int64_t blocks = 0;
+            for (size_t f2 = f; f2 < fast.size() && n < kMaxGemmGroup; ++f2) {
+                const int32_t i = fast[f2];
+                if (done[i] || !args[i].A || (args[i].r + 15) / 16 != r16 || lora_vec(args[i]) != vec) continue;
+                const int64_t b = ((args[i].M + 63) / 64) * v4::kSplits;
+                if (blocks + b > ((int64_t)1 << 31) - 1) continue;
+                as[n] = &args[i];
+                tsg[n] = ts[i];
+                blocks += b;
+                ++n;
+                done[i] = true;
+            }
+            launch_lora_xa_group(as, tsg, n, s);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     std::stable_sort(fast.begin(), fast.end(), [&](int32_t x, int32_t y) { return args[x].K > args[y].K; });
     std::vector<bool> used(count, false);
