@@ -18,6 +18,9 @@
 //     from a K-split pre-pass (lora_xa_kernel) whose partials the epilogue sums in
 //     split order and applies as bf16 hi + lo with two more MFMAs per tile.  The
 //     pipeline and its measured limits are described next to the kernel below.
+//     A grouped call (a layer's GEMMs) runs the pre-passes of its GEMMs in one
+//     launch and their tiles in another, longest rows first; both kernels find
+//     their GEMM in the launch's prefix table and run the single call's code.
 //   * gemm_tile128_kernel (any other shape or alignment): 128 x 128 tiles, 4
 //     waves as 2 x 2, each 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16; the
 //     W tile is dequantized by the workgroup into LDS (flat indexing when blocks
