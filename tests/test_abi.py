@@ -555,3 +555,28 @@ def test_quantize_grouped_argument_errors(L):
     bad = (ctypes.c_float * 16)(*([2.0] * 16))
     assert call(one, 1, qk.QK_BF16, 64, bad, None) == qk.QK_ERR_INVALID_ARG
     assert L.qk_quantize_blockwise(FAKE, qk.QK_BF16, (1 << 40) + 1, 64, lv, FAKE, FAKE, None) == qk.QK_ERR_INVALID_ARG
+
+
+def test_probe_library_exports_and_argument_checks():
+    """libqk_probe.so (the HBM ceiling probes bench.py times) exports its three calls
+    and refuses bad arguments before launching anything."""
+    import os
+    path = os.path.join(os.path.dirname(qk.LIB_PATH), "libqk_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("libqk_probe.so is not built; run python -m bit_blockwise_weight_amd.build")
+    P = ctypes.CDLL(path)
+    for name in ("qk_probe_read_stream", "qk_probe_mix_stream", "qk_probe_buffer_range"):
+        assert hasattr(P, name), name
+    P.qk_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    P.qk_probe_mix_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    F = 0x100000
+    assert P.qk_probe_read_stream(None, 1024, F, 64, 0, None) == 1
+    assert P.qk_probe_read_stream(F, 1000, F, 64, 0, None) == 1            # not a multiple of 16
+    assert P.qk_probe_read_stream(F + 8, 1024, F, 64, 0, None) == 1        # misaligned
+    assert P.qk_probe_read_stream(F, 1024, F, 0, 0, None) == 1             # no grid
+    assert P.qk_probe_mix_stream(None, F, 64, 64, 1, None) == 1
+    assert P.qk_probe_mix_stream(F, F + 8, 64, 64, 1, None) == 1           # misaligned dst
+    assert P.qk_probe_mix_stream(F, F, 0, 64, 1, None) == 1
+    assert P.qk_probe_mix_stream(F, F, 6, 64, 2, None) == 1                # 16-byte stores need n16 % 4 == 0
