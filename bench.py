@@ -1285,7 +1285,7 @@ def main():
         return summarize_pmc(*args.summarize_pmc, command=args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the hot path here runs on a single "
-              "device and this build has no multi-GPU path", file=sys.stderr)
+              "device and the library has no multi-GPU path", file=sys.stderr)
         return 2
     if args.copy_calibration:
         return copy_calibration()

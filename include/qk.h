@@ -78,7 +78,7 @@ typedef int32_t qk_status;
 enum {
     QK_OK = 0,
     QK_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad enum, misaligned buffer */
-    QK_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement */
+    QK_ERR_UNSUPPORTED = -2,   /* valid request the library does not implement */
     QK_ERR_BAD_STATE = -3,     /* qk_quant_state with a wrong magic, version, size or
                                   inconsistent fields (unknown or corrupted metadata) */
     QK_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed */
