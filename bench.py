@@ -985,6 +985,35 @@ def bench(args):
     return 0
 
 
+def rowblock_probe():
+    """Read bandwidth of the LoRA pre-pass's X access pattern (16 rows per wave, a
+    64-element step at a time, K in splits) with each load instruction taking half of
+    16 cache lines, as the pre-pass does, or 8 whole lines (libqk_probe.so); one JSON
+    line per case."""
+    import torch
+    probe = os.path.join(ROOT, "bit_blockwise_weight_amd", "libqk_probe.so")
+    L = ctypes.CDLL(probe)
+    L.qk_probe_rowblock_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    for M, K, copies in ((4096, 4096, 12), (4096, 11008, 6)):
+        xs = [torch.ones((M, K), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+        for nsplit in (8, 16):
+            out = torch.empty(((M + 63) // 64) * nsplit * 256, dtype=torch.int32, device="cuda")
+            for full in (0, 1):
+                def run():
+                    for x in xs:
+                        if L.qk_probe_rowblock_stream(x.data_ptr(), M, K, nsplit, full, out.data_ptr(), stream) != 0:
+                            raise RuntimeError("qk_probe_rowblock_stream failed")
+                s = _timed(torch, run, 5) / copies
+                print(json.dumps({"M": M, "K": K, "splits": nsplit, "whole_lines_per_load": bool(full),
+                                  "us_per_matrix": round(s * 1e6, 2), "tb_per_s": round(M * K * 2 / s / 1e12, 3)}),
+                      flush=True)
+        del xs
+        torch.cuda.empty_cache()
+    return 0
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -1262,6 +1291,8 @@ def main():
     ap.add_argument("--skip-rows", action="store_true",
                     help="skip the timings of the merge, backward, 8-bit state and LLM.int8 calls")
     ap.add_argument("--copy-calibration", action="store_true", help="run a plain 1 GiB device copy")
+    ap.add_argument("--rowblock-probe", action="store_true",
+                    help="read bandwidth of the LoRA pre-pass's access pattern against whole-line loads")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"),
                     help="summarize a rocprofv3 --kernel-trace --stats directory into OUT")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT"),
@@ -1289,6 +1320,8 @@ def main():
         return 2
     if args.copy_calibration:
         return copy_calibration()
+    if args.rowblock_probe:
+        return rowblock_probe()
     return bench(args)
 
 

@@ -124,6 +124,77 @@ extern "C" int qk_probe_mix_stream(const void* src, void* dst, size_t n16, int g
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
+// Row-block streams of a row-major [M, K] bf16 matrix, the access pattern of a pass
+// that takes 16 rows per wave, 4 waves per workgroup and K in nsplit splits, one
+// 64-element step at a time, 4 steps in flight per lane.  kFullLines 0: lane
+// (row l % 16, quarter l / 16) loads 16 bytes at 16 q and 64 + 16 q of its row (each
+// load instruction takes half of 16 lines); 1: a load instruction takes 8 whole 128-byte
+// lines (lane l: row 8 i + l / 8, bytes 16 (l % 8)).  Reads are folded into one word
+// per thread.
+namespace {
+
+template <int kFullLines>
+__global__ __launch_bounds__(256) void rowblock_stream_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                              int nsplit, uint32_t* __restrict__ out) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t nrb = (M + 63) / 64;
+    const int64_t rb = blockIdx.x % nrb, split = blockIdx.x / nrb;
+    const int64_t nk = K / 64, s0 = nk * split / nsplit, s1 = nk * (split + 1) / nsplit;
+    int64_t r0, r1, c0, c1;
+    if constexpr (kFullLines) {
+        r0 = rb * 64 + 16 * wave + lane / 8;
+        r1 = r0 + 8;
+        c0 = c1 = 8 * (lane % 8);
+    } else {
+        r0 = r1 = rb * 64 + 16 * wave + (lane & 15);
+        c0 = 8 * (lane >> 4);
+        c1 = c0 + 32;
+    }
+    r0 = r0 < M ? r0 : M - 1;
+    r1 = r1 < M ? r1 : M - 1;
+    uint32_t acc = 0;
+    u32x4_t v[4][2];
+    auto ld = [&](int64_t s, u32x4_t (&d)[2]) {
+        const int64_t sc = s < s1 ? s : s1 - 1;
+        d[0] = *reinterpret_cast<const u32x4_t*>(x + r0 * K + sc * 64 + c0);
+        d[1] = *reinterpret_cast<const u32x4_t*>(x + r1 * K + sc * 64 + c1);
+    };
+    if (s0 < s1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ld(s0 + i, v[i]);
+        for (int64_t s = s0; s < s1; s += 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc ^= v[i][0].x ^ v[i][0].y ^ v[i][0].z ^ v[i][0].w ^ v[i][1].x ^ v[i][1].y ^ v[i][1].z ^ v[i][1].w;
+                __builtin_amdgcn_sched_barrier(0);
+                ld(s + 4 + i, v[i]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    out[(int64_t)blockIdx.x * 256 + tid] = acc;
+}
+
+}  // namespace
+
+// Streams x [M, K] bf16 (K a multiple of 64, x 16-byte aligned) in the row-block
+// pattern above; out holds ceil(M / 64) * nsplit * 256 words.  Returns 0, or a nonzero
+// code for bad arguments or a failed launch.
+extern "C" int qk_probe_rowblock_stream(const void* x, int64_t M, int64_t K, int nsplit, int full_lines,
+                                        uint32_t* out, void* stream) {
+    if (x == nullptr || out == nullptr || M < 1 || K < 64 || K % 64 != 0 || nsplit < 1 || nsplit > K / 64 ||
+        reinterpret_cast<uintptr_t>(x) % 16 != 0)
+        return 1;
+    const dim3 grid((unsigned)(((M + 63) / 64) * nsplit));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* p = static_cast<const uint16_t*>(x);
+    if (full_lines)
+        hipLaunchKernelGGL(rowblock_stream_kernel<1>, grid, dim3(256), 0, s, p, M, K, nsplit, out);
+    else
+        hipLaunchKernelGGL(rowblock_stream_kernel<0>, grid, dim3(256), 0, s, p, M, K, nsplit, out);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 // The range check of a raw buffer load that writes into LDS: one wave, 64 lanes,
 // lane l loads 16 bytes at vector offset 16 l and the given scalar offset from a
 // resource of num_records = 512 bytes at src (which must hold at least 512 +

@@ -565,7 +565,7 @@ def test_probe_library_exports_and_argument_checks():
     if not os.path.exists(path):
         pytest.fail("libqk_probe.so is not built; run python -m bit_blockwise_weight_amd.build")
     P = ctypes.CDLL(path)
-    for name in ("qk_probe_read_stream", "qk_probe_mix_stream", "qk_probe_buffer_range"):
+    for name in ("qk_probe_read_stream", "qk_probe_mix_stream", "qk_probe_buffer_range", "qk_probe_rowblock_stream"):
         assert hasattr(P, name), name
     P.qk_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_void_p]
@@ -580,3 +580,8 @@ def test_probe_library_exports_and_argument_checks():
     assert P.qk_probe_mix_stream(F, F + 8, 64, 64, 1, None) == 1           # misaligned dst
     assert P.qk_probe_mix_stream(F, F, 0, 64, 1, None) == 1
     assert P.qk_probe_mix_stream(F, F, 6, 64, 2, None) == 1                # 16-byte stores need n16 % 4 == 0
+    P.qk_probe_rowblock_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    assert P.qk_probe_rowblock_stream(F, 64, 100, 1, 0, F, None) == 1     # K not a multiple of 64
+    assert P.qk_probe_rowblock_stream(F, 64, 128, 3, 0, F, None) == 1     # more splits than steps
+    assert P.qk_probe_rowblock_stream(F + 8, 64, 128, 1, 0, F, None) == 1  # misaligned x
