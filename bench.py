@@ -38,6 +38,7 @@ Other modes:
   --summarize-counters D.. O  per-kernel counter averages of rocprofv3 --pmc csv output
                               (--workload W, --trace-dir D for durations)
   --summarize-trace D O       summarize rocprofv3 --kernel-trace --stats csv output
+                              (--bench-log L: the profiled run's stdout, for its live figure)
   --summarize-pmc F W CF CW O HBM traffic of the GEMM from FETCH_SIZE / WRITE_SIZE runs
 """
 
@@ -1037,9 +1038,12 @@ def _csv_rows(directory, suffix):
     return rows
 
 
-def summarize_trace(directory, out_path, command):
+def summarize_trace(directory, out_path, command, bench_log=None):
     """Writes a short markdown summary of a `rocprofv3 --kernel-trace --stats`
-    output directory (its *_kernel_stats.csv) with the command that made it."""
+    output directory (its *_kernel_stats.csv) with the command that made it.
+    With bench_log (the stdout of the same profiled bench.py run), it adds the run's
+    own live per-launch time of the dominant call beside the trace's averages of
+    the kernels that call launches."""
     rows = _csv_rows(directory, "kernel_stats.csv")
     if not rows:
         print(f"no kernel_stats.csv under {directory}", file=sys.stderr)
@@ -1052,6 +1056,25 @@ def summarize_trace(directory, out_path, command):
             name = name[:107] + "..."
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    if bench_log:
+        line = None
+        with open(bench_log) as fh:
+            for text in fh:
+                text = text.strip()
+                if text.startswith("{") and '"roofline"' in text:
+                    line = json.loads(text)
+        if line is None:
+            print(f"no bench JSON line in {bench_log}", file=sys.stderr)
+            return 1
+        rl = line["roofline"]
+        avg = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in rows}
+        parts = [(k, v) for k, v in avg.items() if "gemm_fast_kernel" in k or "lora_xa_kernel" in k]
+        traced = sum(v for _, v in parts)
+        lines += ["", f"The same run's bench line (HIP events on the call's stream): {rl['us_per_launch']:.2f} us "
+                  f"per grouped GEMM call ({rl['kernel']}), {rl['achieved']:.1f} {rl['unit']}.",
+                  f"The trace's averages of the kernels that call launches "
+                  f"({' + '.join(f'{v:.2f}' for _, v in parts)}): {traced:.2f} us "
+                  f"({100.0 * (rl['us_per_launch'] / traced - 1.0):+.1f}% for the events)."]
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out_path}")
@@ -1295,6 +1318,9 @@ def main():
                     help="read bandwidth of the LoRA pre-pass's access pattern against whole-line loads")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "OUT"),
                     help="summarize a rocprofv3 --kernel-trace --stats directory into OUT")
+    ap.add_argument("--bench-log", default=None,
+                    help="with --summarize-trace: the stdout of the profiled bench.py run, whose "
+                         "live per-launch time is set beside the trace's averages")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT"),
                     help="GEMM HBM traffic per dispatch from rocprofv3 --pmc runs")
     ap.add_argument("--command", default="", help="the command recorded in a summary")
@@ -1311,7 +1337,7 @@ def main():
         return summarize_counters(args.summarize_counters[:-1], args.summarize_counters[-1], args.command,
                                   args.workload, args.trace_dir)
     if args.summarize_trace:
-        return summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command)
+        return summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.command, args.bench_log)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, command=args.command)
     if args.gpus != 1:
