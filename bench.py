@@ -989,8 +989,8 @@ def bench(args):
 def rowblock_probe():
     """Read bandwidth of the LoRA pre-pass's X access pattern (16 rows per wave, a
     64-element step at a time, K in splits) with each load instruction taking half of
-    16 cache lines, as the pre-pass does, or 8 whole lines (libqk_probe.so); one JSON
-    line per case."""
+    16 cache lines, as the pre-pass does, or 8 whole lines, with consecutive lanes in
+    one row or in different rows (libqk_probe.so); one JSON line per case."""
     import torch
     probe = os.path.join(ROOT, "bit_blockwise_weight_amd", "libqk_probe.so")
     L = ctypes.CDLL(probe)
@@ -1001,13 +1001,14 @@ def rowblock_probe():
         xs = [torch.ones((M, K), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
         for nsplit in (8, 16):
             out = torch.empty(((M + 63) // 64) * nsplit * 256, dtype=torch.int32, device="cuda")
-            for full in (0, 1):
+            for full in (0, 1, 2):
                 def run():
                     for x in xs:
                         if L.qk_probe_rowblock_stream(x.data_ptr(), M, K, nsplit, full, out.data_ptr(), stream) != 0:
                             raise RuntimeError("qk_probe_rowblock_stream failed")
                 s = _timed(torch, run, 5) / copies
                 print(json.dumps({"M": M, "K": K, "splits": nsplit, "whole_lines_per_load": bool(full),
+                                  "consecutive_lanes": ("same row", "same row", "other rows")[full],
                                   "us_per_matrix": round(s * 1e6, 2), "tb_per_s": round(M * K * 2 / s / 1e12, 3)}),
                       flush=True)
         del xs

@@ -129,8 +129,9 @@ extern "C" int qk_probe_mix_stream(const void* src, void* dst, size_t n16, int g
 // 64-element step at a time, 4 steps in flight per lane.  kFullLines 0: lane
 // (row l % 16, quarter l / 16) loads 16 bytes at 16 q and 64 + 16 q of its row (each
 // load instruction takes half of 16 lines); 1: a load instruction takes 8 whole 128-byte
-// lines (lane l: row 8 i + l / 8, bytes 16 (l % 8)).  Reads are folded into one word
-// per thread.
+// lines (lane l: row 8 i + l / 8, bytes 16 (l % 8)); 2: the same 8 whole lines with the
+// lanes in the other order (lane l: row 8 i + l % 8, bytes 16 (l / 8)), so consecutive
+// lanes read different rows.  Reads are folded into one word per thread.
 namespace {
 
 template <int kFullLines>
@@ -141,10 +142,14 @@ __global__ __launch_bounds__(256) void rowblock_stream_kernel(const uint16_t* __
     const int64_t rb = blockIdx.x % nrb, split = blockIdx.x / nrb;
     const int64_t nk = K / 64, s0 = nk * split / nsplit, s1 = nk * (split + 1) / nsplit;
     int64_t r0, r1, c0, c1;
-    if constexpr (kFullLines) {
+    if constexpr (kFullLines == 1) {
         r0 = rb * 64 + 16 * wave + lane / 8;
         r1 = r0 + 8;
         c0 = c1 = 8 * (lane % 8);
+    } else if constexpr (kFullLines == 2) {
+        r0 = rb * 64 + 16 * wave + lane % 8;
+        r1 = r0 + 8;
+        c0 = c1 = 8 * (lane / 8);
     } else {
         r0 = r1 = rb * 64 + 16 * wave + (lane & 15);
         c0 = 8 * (lane >> 4);
@@ -183,12 +188,15 @@ __global__ __launch_bounds__(256) void rowblock_stream_kernel(const uint16_t* __
 extern "C" int qk_probe_rowblock_stream(const void* x, int64_t M, int64_t K, int nsplit, int full_lines,
                                         uint32_t* out, void* stream) {
     if (x == nullptr || out == nullptr || M < 1 || K < 64 || K % 64 != 0 || nsplit < 1 || nsplit > K / 64 ||
+        full_lines < 0 || full_lines > 2 ||
         reinterpret_cast<uintptr_t>(x) % 16 != 0)
         return 1;
     const dim3 grid((unsigned)(((M + 63) / 64) * nsplit));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const uint16_t* p = static_cast<const uint16_t*>(x);
-    if (full_lines)
+    if (full_lines == 2)
+        hipLaunchKernelGGL(rowblock_stream_kernel<2>, grid, dim3(256), 0, s, p, M, K, nsplit, out);
+    else if (full_lines == 1)
         hipLaunchKernelGGL(rowblock_stream_kernel<1>, grid, dim3(256), 0, s, p, M, K, nsplit, out);
     else
         hipLaunchKernelGGL(rowblock_stream_kernel<0>, grid, dim3(256), 0, s, p, M, K, nsplit, out);

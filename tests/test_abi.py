@@ -585,3 +585,4 @@ def test_probe_library_exports_and_argument_checks():
     assert P.qk_probe_rowblock_stream(F, 64, 100, 1, 0, F, None) == 1     # K not a multiple of 64
     assert P.qk_probe_rowblock_stream(F, 64, 128, 3, 0, F, None) == 1     # more splits than steps
     assert P.qk_probe_rowblock_stream(F + 8, 64, 128, 1, 0, F, None) == 1  # misaligned x
+    assert P.qk_probe_rowblock_stream(F, 64, 128, 1, 3, F, None) == 1     # no such pattern
